@@ -1,0 +1,200 @@
+"""CPU oracle for decode attention read directly from a low-rank-compressed KV cache.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the library imports this module; only the
+test suite, the smoke check and the CPU-baseline leg of the benchmark call it.
+It shares no code, tables or helpers with the HIP path.
+
+Everything is float64 NumPy, written for a reader to check against the pages by
+eye; there is no blocking, fusion or reordering beyond what the definition needs.
+
+What it follows:
+
+* "Half the Memory, None of the Answers Lost" (altslate blog), section 04 "what
+  worked": one projection per (layer, head) maps each 128-dim key (taken after
+  RoPE) and value to an r-dim code, r < 128; the codes are what is stored.
+* The same blog, section 08 "at serving time": attention can be computed against
+  the codes themselves, which is algebraically the same as reconstructing the
+  cache; the projection matrices are shared per head.
+* "OjaKV: Online Low-Rank Compression for LLM Key-Value Caches" (astrobobo
+  article), FAQ on which tokens are compressed: the first token and the most
+  recent tokens are kept at full rank as anchors; every token in between is
+  stored low-rank.
+
+Readings where the pages are silent (each also listed in the design doc):
+
+* the score scale is 1/sqrt(d) with d = 128, the model's own scale;
+* ``n`` counts the cached tokens including the decode token itself; the anchor
+  set is {0} plus the last ``window`` tokens, the codes are everything between;
+* query head i of a GQA group reads KV head i // g;
+* codes are ``x @ U`` with U a (128, r) matrix with orthonormal columns.
+
+Pins (tests/test_oracle.py): full attention at r = d with an orthogonal basis
+(the blog's section 04 plumbing check), brute-force reconstruction on tiny
+inputs, torch's float64 scaled_dot_product_attention, softmax weights summing to
+one, closed forms (n = 1, q = 0, constant values), invariances (basis sign, token
+order), compress closed forms and the OjaKV FAQ's ~16 GB KV-cache size.  Values
+on random inputs beyond those pins are "parity unpinned": the pages print no
+worked example.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+HEAD_DIM = 128
+
+
+# ---------------------------------------------------------------------------
+# number format
+# ---------------------------------------------------------------------------
+
+def bf16_round(x) -> np.ndarray:
+    """Round to the nearest bfloat16 value, ties to even, straight from float64.
+
+    bfloat16 keeps 8 significant bits (7 stored) and float32's exponent range;
+    below the smallest normal (2**-126) the spacing stays 2**-133.  Written from
+    that definition: quantum = 2**(e - 8) for a frexp exponent e (mantissa in
+    [0.5, 1)), and np.rint rounds half to even.  Overflow is not handled (the
+    workloads never come near it)."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    e = np.maximum(e, -125)
+    quantum = np.ldexp(1.0, e - 8)
+    return np.rint(x / quantum) * quantum
+
+
+# ---------------------------------------------------------------------------
+# which tokens are anchors (OjaKV FAQ), which are codes (blog section 04)
+# ---------------------------------------------------------------------------
+
+def anchor_positions(n: int, window: int) -> np.ndarray:
+    """Token 0 plus the most recent ``window`` tokens, kept at full rank."""
+    if n < 1:
+        raise ValueError("n must be >= 1")
+    recent = range(max(1, n - window), n)
+    return np.array([0, *recent], dtype=np.int64)
+
+
+def code_positions(n: int, window: int) -> np.ndarray:
+    """Tokens strictly between the first token and the recent window."""
+    return np.arange(1, max(1, n - window), dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# prefill compression (blog section 04)
+# ---------------------------------------------------------------------------
+
+def oracle_compress(x, u) -> np.ndarray:
+    """Codes of the rows of ``x`` (t, 128) under the basis ``u`` (128, r): x @ u."""
+    x = np.asarray(x, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    return x @ u
+
+
+# ---------------------------------------------------------------------------
+# decode attention against codes and anchors (blog section 08), one step at a time
+# ---------------------------------------------------------------------------
+
+def project_query(q, u_k) -> np.ndarray:
+    """q~ = U_K^T q for each query row: (g, 128) -> (g, r_k)."""
+    return np.asarray(q, np.float64) @ np.asarray(u_k, np.float64)
+
+
+def code_scores(q_tilde, c_k, scale: float) -> np.ndarray:
+    """Scores of the compressed tokens, taken in code space: (g, c)."""
+    return (q_tilde @ np.asarray(c_k, np.float64).T) * scale
+
+
+def anchor_scores(q, k_a, scale: float) -> np.ndarray:
+    """Scores of the full-rank anchor tokens: (g, a)."""
+    return (np.asarray(q, np.float64) @ np.asarray(k_a, np.float64).T) * scale
+
+
+def softmax_weights(s) -> tuple:
+    """One softmax over all scores of a query row.  Returns the unnormalised
+    weights e = exp(s - max s) and their sum L (so p = e / L)."""
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return e, e.sum(axis=1, keepdims=True)
+
+
+def rank_space_values(e_codes, c_v) -> np.ndarray:
+    """o~ = sum_j e_j c^V_j, accumulated in the r_v-dim code space: (g, r_v)."""
+    return e_codes @ np.asarray(c_v, np.float64)
+
+
+def anchor_values(e_anchors, v_a) -> np.ndarray:
+    """sum_j e_j v_j over the anchors, in full 128-dim space: (g, 128)."""
+    return e_anchors @ np.asarray(v_a, np.float64)
+
+
+def up_project(o_tilde, u_v) -> np.ndarray:
+    """The single up-projection U_V o~ per query row: (g, r_v) -> (g, 128)."""
+    return o_tilde @ np.asarray(u_v, np.float64).T
+
+
+def oracle_decode_unit(q, u_k, u_v, c_k, c_v, k_a, v_a, scale: float, return_p: bool = False):
+    """Decode attention of the g query heads that share one KV head.
+
+    q (g, 128); u_k (128, r_k); u_v (128, r_v); c_k (c, r_k); c_v (c, r_v);
+    k_a, v_a (a, 128).  Returns out (g, 128) and, if asked, the normalised
+    weights p (g, c + a) with the code tokens first, then the anchors."""
+    c = np.asarray(c_k).shape[0]
+    q_tilde = project_query(q, u_k)
+    s = np.concatenate([code_scores(q_tilde, c_k, scale), anchor_scores(q, k_a, scale)], axis=1)
+    e, total = softmax_weights(s)
+    o_tilde = rank_space_values(e[:, :c], c_v)
+    out = (up_project(o_tilde, u_v) + anchor_values(e[:, c:], v_a)) / total
+    if return_p:
+        return out, e / total
+    return out
+
+
+def default_scale(d: int = HEAD_DIM) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def oracle_decode_layer(q, bases_k, bases_v, codes_k, codes_v, anchors_k, anchors_v,
+                        scale: float | None = None) -> np.ndarray:
+    """One decode step of a whole layer.
+
+    q (batch, Hq, 128); bases_k[h] (128, r_k[h]); bases_v[h] (128, r_v[h]);
+    codes_k[b][h] (c_b, r_k[h]); codes_v[b][h] (c_b, r_v[h]);
+    anchors_k[b][h], anchors_v[b][h] (a_b, 128).  Query head i reads KV head
+    i // g.  Returns out (batch, Hq, 128) in float64."""
+    q = np.asarray(q, np.float64)
+    batch, n_q, _ = q.shape
+    n_kv = len(bases_k)
+    g = n_q // n_kv
+    scale = default_scale() if scale is None else scale
+    out = np.empty((batch, n_q, HEAD_DIM))
+    for b in range(batch):
+        for h in range(n_kv):
+            rows = slice(h * g, (h + 1) * g)
+            out[b, rows] = oracle_decode_unit(
+                q[b, rows], bases_k[h], bases_v[h], codes_k[b][h], codes_v[b][h],
+                anchors_k[b][h], anchors_v[b][h], scale)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# byte accounting (OjaKV FAQ: ~16 GB of KV for Llama-3.1-8B, 32K tokens, batch 4;
+# blog section 08: the per-request cache shrinks with the code width, plus the
+# shared projection matrices)
+# ---------------------------------------------------------------------------
+
+def full_kv_bytes(n_layers: int, n_kv_heads: int, n_tokens: int, batch: int,
+                  head_dim: int = HEAD_DIM, elem_bytes: int = 2) -> int:
+    """Bytes of an uncompressed cache: keys and values of every layer and KV head."""
+    return 2 * n_layers * n_kv_heads * head_dim * n_tokens * batch * elem_bytes
+
+
+def compressed_unit_bytes(n: int, window: int, r_k: int, r_v: int, elem_bytes: int = 2,
+                          head_dim: int = HEAD_DIM) -> int:
+    """Bytes one decode step must read for one (batch row, KV head): the codes of
+    the compressed tokens plus the full-rank anchors."""
+    c = len(code_positions(n, window))
+    a = len(anchor_positions(n, window))
+    return c * (r_k + r_v) * elem_bytes + a * 2 * head_dim * elem_bytes

@@ -1,0 +1,354 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+what the pages or the mathematics fix.  test_oracle.py runs them all;
+test_oracle_mutants.py plants plausible mistakes in the oracle and checks that
+at least one pin catches each.
+
+References used here (none shares code with the oracle):
+* torch.nn.functional.scaled_dot_product_attention in float64 on the CPU;
+* brute force: the cache reconstructed token by token, then softmax attention
+  written as explicit Python loops with math.exp;
+* torch's float32 -> bfloat16 conversion for the rounding helper;
+* closed forms and invariances of softmax attention.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+
+D = 128
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------------------
+# independent references
+# ---------------------------------------------------------------------------
+
+def sdpa(q, keys, values, scale):
+    """Library softmax attention, float64 CPU: q (g, d), keys/values (n, d) shared by all g rows."""
+    qt = torch.from_numpy(np.asarray(q, np.float64))[None, :, None, :]
+    g = qt.shape[1]
+    kt = torch.from_numpy(np.asarray(keys, np.float64))[None, None].expand(1, g, -1, -1)
+    vt = torch.from_numpy(np.asarray(values, np.float64))[None, None].expand(1, g, -1, -1)
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+    return out[0, :, 0, :].numpy()
+
+
+def brute_attention(q_row, keys, values, scale):
+    """Softmax attention for one query row with explicit loops."""
+    n = len(keys)
+    scores = [scale * sum(float(q_row[i]) * float(keys[j][i]) for i in range(len(q_row))) for j in range(n)]
+    top = max(scores)
+    w = [math.exp(s - top) for s in scores]
+    tot = sum(w)
+    d = len(values[0])
+    out = [sum(w[j] * float(values[j][i]) for j in range(n)) / tot for i in range(d)]
+    return np.array(out), np.array(w) / tot
+
+
+def reconstruct(codes, u):
+    """Full-dim rows back from codes, one token at a time: x_hat_j = U c_j."""
+    return np.stack([np.asarray(u, np.float64) @ np.asarray(c, np.float64) for c in codes]) \
+        if len(codes) else np.zeros((0, D))
+
+
+# ---------------------------------------------------------------------------
+# random inputs for the pins
+# ---------------------------------------------------------------------------
+
+def orthonormal(rng, r):
+    a = rng.standard_normal((D, D))
+    qm, _ = np.linalg.qr(a)
+    return qm[:, :r]
+
+
+def random_unit(rng, n, window, r_k, r_v, g=2, q_scale=1.0, u_k=None, u_v=None):
+    """A random cache for one KV head at n tokens, split into codes and anchors
+    by the oracle's own partition.  Returns dict of arrays (float64)."""
+    k = rng.standard_normal((n, D))
+    v = rng.standard_normal((n, D))
+    q = rng.standard_normal((g, D)) * q_scale
+    u_k = orthonormal(rng, r_k) if u_k is None else u_k
+    u_v = orthonormal(rng, r_v) if u_v is None else u_v
+    cpos = oracle.code_positions(n, window)
+    apos = oracle.anchor_positions(n, window)
+    return dict(q=q, k=k, v=v, u_k=u_k, u_v=u_v, cpos=cpos, apos=apos,
+                c_k=k[cpos] @ u_k, c_v=v[cpos] @ u_v, k_a=k[apos], v_a=v[apos])
+
+
+def run_unit(u, scale=None, return_p=False):
+    scale = oracle.default_scale() if scale is None else scale
+    return oracle.oracle_decode_unit(u["q"], u["u_k"], u["u_v"], u["c_k"], u["c_v"],
+                                     u["k_a"], u["v_a"], scale, return_p=return_p)
+
+
+def rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ---------------------------------------------------------------------------
+# pins
+# ---------------------------------------------------------------------------
+
+def pin_bf16_round_matches_torch():
+    rng = np.random.default_rng(11)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-38).astype(np.float32),   # subnormal range
+        (rng.standard_normal(2000) * 1e30).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, -1.0], np.float32),
+    ])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.bf16_round(x.astype(np.float64))
+    assert np.array_equal(got, ref), "bf16 rounding disagrees with torch's conversion"
+
+
+def pin_bf16_round_ties():
+    # spacing of bf16 in [1, 2) is 2**-7; halfway cases go to the even neighbour
+    cases = {1 + 2**-8: 1.0, 1 + 3 * 2**-8: 1 + 2**-6, -(1 + 2**-8): -1.0,
+             1 + 2**-8 + 2**-20: 1 + 2**-7, 2**-133 * 1.5: 2**-132, 3.0: 3.0}
+    for x, want in cases.items():
+        got = float(oracle.bf16_round(np.array([x]))[0])
+        assert got == want, (x, got, want)
+
+
+def pin_partition():
+    for n in [1, 2, 3, 16, 17, 18, 19, 100, 257]:
+        for w in [0, 1, 16, 64]:
+            a = oracle.anchor_positions(n, w)
+            c = oracle.code_positions(n, w)
+            allp = np.sort(np.concatenate([a, c]))
+            assert np.array_equal(allp, np.arange(n)), (n, w)
+            assert len(a) == min(n, 1 + w), (n, w, len(a))
+            assert a[0] == 0
+            if n > 1 and w > 0:
+                assert a[-1] == n - 1, "the decode token itself must be a full-rank anchor"
+            assert len(c) == max(0, n - 1 - w)
+
+
+def pin_plumbing_identity_basis():
+    """Blog section 04 plumbing check: an uncompressed cache routed through the
+    path (r = d, U = I) reproduces full attention."""
+    rng = np.random.default_rng(1)
+    eye = np.eye(D)
+    u = random_unit(rng, 200, 16, D, D, g=3, u_k=eye, u_v=eye)
+    got = run_unit(u)
+    want = sdpa(u["q"], u["k"], u["v"], oracle.default_scale())
+    assert rel(got, want) < 1e-12, rel(got, want)
+
+
+def pin_plumbing_orthogonal_basis():
+    """Same check with a full-rank non-symmetric orthogonal basis (r = d)."""
+    rng = np.random.default_rng(2)
+    u_k = orthonormal(rng, D)
+    u_v = orthonormal(rng, D)
+    u = random_unit(rng, 150, 8, D, D, g=2, u_k=u_k, u_v=u_v)
+    got = run_unit(u)
+    want = sdpa(u["q"], u["k"], u["v"], oracle.default_scale())
+    assert rel(got, want) < 1e-12, rel(got, want)
+
+
+def pin_brute_force_tiny():
+    """Low rank: the oracle equals attention over the reconstructed cache,
+    computed with explicit loops, including the weights."""
+    rng = np.random.default_rng(3)
+    for (n, w, rk, rv, g) in [(12, 3, 16, 32, 2), (7, 0, 48, 16, 1), (9, 20, 32, 16, 3), (30, 5, 96, 64, 2)]:
+        u = random_unit(rng, n, w, rk, rv, g=g, q_scale=3.0)
+        out, p = run_unit(u, return_p=True)
+        keys = np.concatenate([reconstruct(u["c_k"], u["u_k"]), u["k_a"]])
+        vals = np.concatenate([reconstruct(u["c_v"], u["u_v"]), u["v_a"]])
+        for i in range(g):
+            bo, bp = brute_attention(u["q"][i], keys, vals, oracle.default_scale())
+            assert rel(out[i], bo) < 1e-12, (n, w, rk, rv, rel(out[i], bo))
+            assert np.max(np.abs(p[i] - bp)) < 1e-14
+
+
+def pin_sdpa_low_rank():
+    """Low rank at larger n against the library routine over the reconstructed cache."""
+    rng = np.random.default_rng(4)
+    for (n, w, rk, rv, g, qs) in [(300, 16, 64, 32, 4, 1.0), (513, 64, 32, 16, 2, 8.0),
+                                 (64, 100, 64, 32, 1, 1.0), (1000, 0, 128, 16, 8, 4.0)]:
+        u = random_unit(rng, n, w, rk, rv, g=g, q_scale=qs)
+        got = run_unit(u)
+        keys = np.concatenate([u["c_k"] @ u["u_k"].T, u["k_a"]])
+        vals = np.concatenate([u["c_v"] @ u["u_v"].T, u["v_a"]])
+        want = sdpa(u["q"], keys, vals, oracle.default_scale())
+        assert rel(got, want) < 1e-12, (n, w, rk, rv, rel(got, want))
+
+
+def pin_code_space_identity():
+    """(U^T q).(U^T k) = q.(U U^T k) for any basis: ties scoring and orientation."""
+    rng = np.random.default_rng(5)
+    for r in [16, 48, 128]:
+        u = orthonormal(rng, r)
+        q = rng.standard_normal((3, D))
+        k = rng.standard_normal((10, D))
+        s_code = oracle.code_scores(oracle.project_query(q, u), oracle.oracle_compress(k, u), 1.0)
+        s_full = q @ (u @ u.T @ k.T)
+        assert np.max(np.abs(s_code - s_full)) < 1e-11
+
+
+def pin_weights_sum_to_one():
+    rng = np.random.default_rng(6)
+    for qs in [1.0, 30.0]:
+        u = random_unit(rng, 400, 32, 64, 32, g=4, q_scale=qs)
+        _, p = run_unit(u, return_p=True)
+        assert np.all(p >= 0)
+        assert np.max(np.abs(p.sum(axis=1) - 1)) < 1e-14
+
+
+def pin_constant_values():
+    """Every value (reconstructed or anchor) equal to v0 -> out = v0."""
+    rng = np.random.default_rng(7)
+    u = random_unit(rng, 120, 10, 64, 32, g=2, q_scale=5.0)
+    z = rng.standard_normal(32)
+    v0 = u["u_v"] @ z
+    u["c_v"] = np.tile(z, (len(u["cpos"]), 1))
+    u["v_a"] = np.tile(v0, (len(u["apos"]), 1))
+    got = run_unit(u)
+    assert np.max(np.abs(got - v0[None, :])) < 1e-13
+
+
+def pin_anchors_only():
+    """n <= 1 + W: nothing is compressed; full attention over the n tokens."""
+    rng = np.random.default_rng(8)
+    u = random_unit(rng, 40, 64, 32, 16, g=2)
+    assert len(u["cpos"]) == 0
+    got = run_unit(u)
+    want = sdpa(u["q"], u["k"], u["v"], oracle.default_scale())
+    assert rel(got, want) < 1e-12
+
+
+def pin_single_token():
+    rng = np.random.default_rng(9)
+    u = random_unit(rng, 1, 16, 64, 32, g=3)
+    got = run_unit(u)
+    assert np.max(np.abs(got - u["v"][0][None, :])) < 1e-15
+
+
+def pin_zero_query():
+    """q = 0: all scores equal, out is the mean of all (reconstructed) values."""
+    rng = np.random.default_rng(10)
+    u = random_unit(rng, 90, 7, 48, 32, g=2)
+    u["q"] = np.zeros_like(u["q"])
+    got = run_unit(u)
+    mean = (u["c_v"].sum(axis=0) @ u["u_v"].T + u["v_a"].sum(axis=0)) / 90
+    assert np.max(np.abs(got - mean[None, :])) < 1e-14
+
+
+def pin_basis_sign_and_token_order():
+    rng = np.random.default_rng(12)
+    u = random_unit(rng, 200, 12, 64, 32, g=2)
+    base = run_unit(u)
+    flipped = dict(u)
+    sk = np.where(rng.random(64) < 0.5, -1.0, 1.0)
+    sv = np.where(rng.random(32) < 0.5, -1.0, 1.0)
+    flipped["u_k"] = u["u_k"] * sk
+    flipped["c_k"] = u["c_k"] * sk
+    flipped["u_v"] = u["u_v"] * sv
+    flipped["c_v"] = u["c_v"] * sv
+    assert rel(run_unit(flipped), base) < 1e-13
+    perm = dict(u)
+    pc = rng.permutation(len(u["cpos"]))
+    pa = rng.permutation(len(u["apos"]))
+    perm["c_k"], perm["c_v"] = u["c_k"][pc], u["c_v"][pc]
+    perm["k_a"], perm["v_a"] = u["k_a"][pa], u["v_a"][pa]
+    assert rel(run_unit(perm), base) < 1e-13
+
+
+def pin_scale_is_head_dim():
+    """The score scale is 1/sqrt(128) whatever the rank: at r = d with U = I the
+    oracle must agree with the library's default-scaled attention."""
+    assert oracle.default_scale() == 1.0 / math.sqrt(128)
+    rng = np.random.default_rng(13)
+    eye = np.eye(D)
+    u = random_unit(rng, 64, 4, D, D, g=1, q_scale=4.0, u_k=eye, u_v=eye)
+    qt = torch.from_numpy(u["q"])[None, :, None, :]
+    kt = torch.from_numpy(u["k"])[None, None]
+    vt = torch.from_numpy(u["v"])[None, None]
+    want = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[0, :, 0].numpy()
+    assert rel(run_unit(u), want) < 1e-12
+
+
+def pin_compress_closed_forms():
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((50, D))
+    assert np.array_equal(oracle.oracle_compress(x, np.eye(D)), x)
+    for r in [16, 64]:
+        u = orthonormal(rng, r)
+        z = rng.standard_normal((40, r))
+        assert np.max(np.abs(oracle.oracle_compress(z @ u.T, u) - z)) < 1e-13
+    # calibration: the columns of X U have norms equal to the top singular values
+    xc = rng.standard_normal((256, D)) * np.exp(-np.arange(D) / 16.0)
+    _, s, vt = np.linalg.svd(xc, full_matrices=False)
+    c = oracle.oracle_compress(xc, vt[:32].T)
+    assert np.max(np.abs(np.linalg.norm(c, axis=0) - s[:32]) / s[:32]) < 1e-12
+    # rows of different shapes of the same data give the same codes
+    assert np.array_equal(oracle.oracle_compress(x[:7], np.eye(D)[:, :16]), x[:7, :16])
+
+
+def pin_kv_bytes_ojakv():
+    g = json.load(open(os.path.join(GOLDEN, "ojakv_kv_bytes.json")))
+    nbytes = oracle.full_kv_bytes(g["n_layers"], g["n_kv_heads"], g["n_tokens"], g["batch"],
+                                  g["head_dim"], g["elem_bytes"])
+    assert nbytes == 16 * 2**30
+    assert abs(nbytes / 1e9 - g["stated_gb"]) / g["stated_gb"] < 0.1
+
+
+def pin_payload_ratios_blog():
+    g = json.load(open(os.path.join(GOLDEN, "blog_payload_ratios.json")))
+    full = 2 * D * 2
+    for case in g["cases"]:
+        if "ratio" in case:
+            n = 100000
+            per_tok = oracle.compressed_unit_bytes(n, 0, case["r_k"], case["r_v"]) / n
+            ratio = full / per_tok
+            assert abs(ratio - case["ratio"]) <= case["tolerance"] * case["ratio"] + 0.04, (case, ratio)
+        else:
+            assert case["r_v"] / D == case["value_fraction"]
+    # anchors are read at full width: at n <= 1 + W nothing is saved
+    assert oracle.compressed_unit_bytes(50, 64, 32, 16) == 50 * full
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+def pin_layer_gqa_sdpa():
+    """Whole-layer decode with distinct KV heads against the library's GQA
+    attention (query head i reads KV head i // g)."""
+    rng = np.random.default_rng(15)
+    batch, n_kv, g, n, w = 2, 3, 2, 70, 5
+    cpos, apos = oracle.code_positions(n, w), oracle.anchor_positions(n, w)
+    q = rng.standard_normal((batch, n_kv * g, D)) * 2
+    bk = [orthonormal(rng, rk) for rk in (16, 32, 64)]
+    bv = [orthonormal(rng, rv) for rv in (32, 16, 48)]
+    K = rng.standard_normal((batch, n_kv, n, D))
+    V = rng.standard_normal((batch, n_kv, n, D))
+    ck = [[K[b, h][cpos] @ bk[h] for h in range(n_kv)] for b in range(batch)]
+    cv = [[V[b, h][cpos] @ bv[h] for h in range(n_kv)] for b in range(batch)]
+    ka = [[K[b, h][apos] for h in range(n_kv)] for b in range(batch)]
+    va = [[V[b, h][apos] for h in range(n_kv)] for b in range(batch)]
+    got = oracle.oracle_decode_layer(q, bk, bv, ck, cv, ka, va)
+    Kh = np.empty((batch, n_kv, n, D))
+    Vh = np.empty((batch, n_kv, n, D))
+    for b in range(batch):
+        for h in range(n_kv):
+            Kh[b, h][cpos] = ck[b][h] @ bk[h].T
+            Kh[b, h][apos] = ka[b][h]
+            Vh[b, h][cpos] = cv[b][h] @ bv[h].T
+            Vh[b, h][apos] = va[b][h]
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, :, None, :], torch.from_numpy(Kh), torch.from_numpy(Vh),
+        enable_gqa=True)[:, :, 0, :].numpy()
+    assert rel(got, want) < 1e-12, rel(got, want)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

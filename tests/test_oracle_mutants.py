@@ -1,0 +1,94 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch every one of them.  A mutant survives only if every pin still passes."""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.lrkv_oracle as lo
+import oracle_pins
+
+
+def _any_pin_fails():
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except Exception:  # AssertionError or a shape error both count as caught
+            return True
+    return False
+
+
+def _two_softmaxes(q, u_k, u_v, c_k, c_v, k_a, v_a, scale, return_p=False):
+    c = np.asarray(c_k).shape[0]
+    qt = lo.project_query(q, u_k)
+    out = 0
+    for s, vals in [(lo.code_scores(qt, c_k, scale), None), (lo.anchor_scores(q, k_a, scale), v_a)]:
+        if s.shape[1] == 0:
+            continue
+        e, tot = lo.softmax_weights(s)
+        part = lo.up_project(lo.rank_space_values(e, c_v), u_v) if vals is None else lo.anchor_values(e, vals)
+        out = out + part / tot
+    return (out, None) if return_p else out
+
+
+MUTANTS = {
+    "scale_by_rank": ("code_scores", lambda qt, ck, scale: (qt @ np.asarray(ck, float).T) / np.sqrt(np.asarray(ck).shape[1])),
+    "anchor_values_dropped": ("anchor_values", lambda e, v: np.zeros((e.shape[0], 128))),
+    "up_projection_transposed": ("up_project", lambda o, u: o @ np.asarray(u, float)),
+    "query_not_projected": ("project_query", lambda q, u: np.asarray(q, float)[:, : np.asarray(u).shape[1]]),
+    "anchor_window_off_by_one": ("anchor_positions", lambda n, w: np.array([0, *range(max(1, n - w - 1), n)])),
+    "codes_include_window_edge": ("code_positions", lambda n, w: np.arange(1, max(1, n - w + 1))),
+    "bf16_truncates": ("bf16_round", lambda x: np.asarray(np.asarray(x, np.float32).view(np.uint32) & 0xFFFF0000, np.uint32).view(np.float32).astype(np.float64)),
+    "no_normalisation": ("softmax_weights", lambda s: (np.exp(s - s.max(axis=1, keepdims=True)), np.ones((s.shape[0], 1)))),
+    "values_through_key_basis": ("up_project", None),
+    "two_separate_softmaxes": ("oracle_decode_unit", _two_softmaxes),
+    "gqa_modulo_mapping": ("oracle_decode_layer", None),
+    "missing_scale": ("anchor_scores", lambda q, ka, scale: np.asarray(q, float) @ np.asarray(ka, float).T),
+}
+
+
+def _gqa_modulo(q, bases_k, bases_v, codes_k, codes_v, anchors_k, anchors_v, scale=None):
+    q = np.asarray(q, np.float64)
+    batch, n_q, _ = q.shape
+    n_kv = len(bases_k)
+    scale = lo.default_scale() if scale is None else scale
+    out = np.empty((batch, n_q, 128))
+    for b in range(batch):
+        for i in range(n_q):
+            h = i % n_kv
+            out[b, i] = lo.oracle_decode_unit(q[b, i:i + 1], bases_k[h], bases_v[h], codes_k[b][h],
+                                              codes_v[b][h], anchors_k[b][h], anchors_v[b][h], scale)[0]
+    return out
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    if name == "values_through_key_basis":
+        # value accumulation reads the key codes instead of the value codes
+        orig = lo.rank_space_values
+        monkeypatch.setattr(lo, "oracle_decode_unit", _values_from_keys(orig))
+        monkeypatch.setattr(oracle, "oracle_decode_unit", lo.oracle_decode_unit)
+    elif name == "gqa_modulo_mapping":
+        monkeypatch.setattr(lo, attr, _gqa_modulo)
+        monkeypatch.setattr(oracle, attr, _gqa_modulo)
+    else:
+        monkeypatch.setattr(lo, attr, fn)
+        if hasattr(oracle, attr):
+            monkeypatch.setattr(oracle, attr, fn)
+    assert _any_pin_fails(), f"mutant {name} survived every pin"
+
+
+def _values_from_keys(_orig):
+    def decode(q, u_k, u_v, c_k, c_v, k_a, v_a, scale, return_p=False):
+        c = np.asarray(c_k).shape[0]
+        qt = lo.project_query(q, u_k)
+        s = np.concatenate([lo.code_scores(qt, c_k, scale), lo.anchor_scores(q, k_a, scale)], axis=1)
+        e, tot = lo.softmax_weights(s)
+        out = (lo.up_project(lo.rank_space_values(e[:, :c], c_k), u_k) + lo.anchor_values(e[:, c:], v_a)) / tot
+        return (out, e / tot) if return_p else out
+    return decode
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert not _any_pin_fails()
