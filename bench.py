@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Decode attention over a low-rank-compressed KV cache on one MI355X.
+
+One step = one decode call (``lrkv_decode_attn``: projected-query scoring of the
+codes, full-rank anchors, one softmax, rank-space value sums, one up-projection)
+for a whole layer of the Llama-3.1-8B-shaped 32K-context workload (batch 4,
+32 query / 8 KV heads, d = 128, r_k = 64, r_v = 32, first token + last 128 as
+anchors, 32 context splits).  The cache is built on the GPU by the library's own
+prefill compression from seeded synthetic keys and values, and is replicated so
+that successive calls rotate over >= 1 GiB of cache (as the layers of a model
+would) and read from HBM rather than the 256 MB last-level cache.
+
+Prints one JSON line: tokens*heads/s of whole calls, the roofline of the
+dominant kernel (its algorithmic bytes over its event-timed duration) and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+DOMINANT_KERNEL = "lrkv decode partials (code splits + anchors)"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("decode.hip", "lrkv_internal.h"):
+        with open(os.path.join(ROOT, "rank_kv_cache_lrkv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, n):
+    """Bytes the method must move for one decode call of one layer, and the part
+    the partials kernel moves (codes, anchors, U_K, q)."""
+    import oracle
+    s = 4 if w.dtype == "f32" else 2
+    c = len(oracle.code_positions(n, w.window))
+    a = len(oracle.anchor_positions(n, w.window))
+    units = w.batch * w.n_kv_heads
+    codes = units * c * (w.rank_k + w.rank_v) * s
+    anchors = units * a * 2 * 128 * s
+    u_k = w.n_kv_heads * 128 * w.rank_k * s
+    u_v = w.n_kv_heads * 128 * w.rank_v * s
+    q = w.batch * w.n_q_heads * 128 * s
+    out = w.batch * w.n_q_heads * 128 * 4
+    return {"call": codes + anchors + u_k + u_v + q + out, "partials": codes + anchors + u_k + q,
+            "codes": codes, "anchors": anchors}
+
+
+def build_cache(w, B, dev):
+    """Prefill on the GPU: compress tokens 1..n-W-1, store token 0 and the window."""
+    import numpy as np
+    import torch
+
+    import synth
+    from rank_kv_cache_lrkv_amd import layout
+
+    rk, rv = synth.ranks(w, 0)
+    bases = np.concatenate([np.concatenate([synth.basis(w, 0, h, "k", int(rk[h])).ravel(),
+                                            synth.basis(w, 0, h, "v", int(rv[h])).ravel()])
+                            for h in range(w.n_kv_heads)])
+    n = w.n_ctx
+    c = max(0, n - 1 - w.window)
+    L = B.Layer.allocate(dtype=B.LRKV_BF16 if w.dtype == "bf16" else B.LRKV_F32, batch=w.batch,
+                         n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, window=w.window,
+                         cap=layout.round_cap(c), rank_k=rk, rank_v=rv, bases=dev(bases))
+    td = L.torch_dtype
+    K = torch.empty((w.batch, w.n_kv_heads, n, 128), dtype=td, device="cuda")
+    V = torch.empty_like(K)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            K[b, h] = dev(synth.unit_kv(w, 0, h, b, "k")[:n])
+            V[b, h] = dev(synth.unit_kv(w, 0, h, b, "v")[:n])
+    # prefill compression, timed once warm
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for rep in range(2):
+        ev[0].record()
+        B.lrkv_compress(L, 0, K[:, :, 1:], c, 0)
+        B.lrkv_compress(L, 1, V[:, :, 1:], c, 0)
+        ev[1].record()
+    B.lrkv_store_anchors(L, K[:, :, 0:1], V[:, :, 0:1], 0, 1)
+    lo = max(1, n - w.window)
+    B.lrkv_store_anchors(L, K[:, :, lo:n], V[:, :, lo:n], lo, n - lo)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1])
+    s = 2 if w.dtype == "bf16" else 4
+    moved = w.batch * w.n_kv_heads * c * (2 * 128 + w.rank_k + w.rank_v) * s
+    compress = {"ms": round(ms, 4), "tokens": c, "alg_bytes": moved,
+                "gbps": round(moved / (ms * 1e-3) / 1e9, 1)}
+    del K, V
+    return L, compress
+
+
+def replicate(L, B):
+    return B.Layer(L.dtype, L.batch, L.n_q_heads, L.n_kv_heads, L.window, L.cap, L.rank_k, L.rank_v,
+                   L.bases.clone(), L.codes_k.clone(), L.codes_v.clone(), L.anchor_k.clone(),
+                   L.anchor_v.clone())
+
+
+def cpu_baseline(w, seconds):
+    """The oracle as it stands, timed on this host's cores over a bounded sample
+    of (batch row, KV head) units of the same workload at full context."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    n = w.n_ctx
+    rk, rv = synth.ranks(w, 0)
+    cpos, apos = oracle.code_positions(n, w.window), oracle.anchor_positions(n, w.window)
+    g = w.group
+    scale = oracle.default_scale()
+    spent, done, units = 0.0, 0, []
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            units.append((b, h))
+    prepared = []
+    for b, h in units:
+        k = synth.unit_kv(w, 0, h, b, "k")[:n].astype(np.float64)
+        v = synth.unit_kv(w, 0, h, b, "v")[:n].astype(np.float64)
+        uk = synth.basis(w, 0, h, "k", int(rk[h])).astype(np.float64)
+        uv = synth.basis(w, 0, h, "v", int(rv[h])).astype(np.float64)
+        rnd = oracle.bf16_round if w.dtype == "bf16" else (lambda x: x.astype(np.float32).astype(np.float64))
+        ck = rnd(oracle.oracle_compress(k[cpos], uk))
+        cv = rnd(oracle.oracle_compress(v[cpos], uv))
+        q = synth.queries(w, 0, 0, b)[h * g:(h + 1) * g].astype(np.float64)
+        prepared.append((q, uk, uv, ck, cv, k[apos], v[apos]))
+        if len(prepared) == 8:
+            break
+    # cycle over the prepared units until the time budget is spent
+    while spent < seconds:
+        for args in prepared:
+            t0 = time.perf_counter()
+            oracle.oracle_decode_unit(*args, scale)
+            spent += time.perf_counter() - t0
+            done += 1
+    value = done * g * n / spent
+    return {"value": value, "unit": "tokens*heads/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} unit decodes cycling over {len(prepared)} of the {len(units)} "
+                      f"(batch row, KV head) units at full context n={n}, {g} query heads each; "
+                      f"float64 NumPy oracle_decode_unit, {spent:.1f} s of decode time "
+                      f"(code preparation untimed)"}
+
+
+def traffic_from_profile(source_hash):
+    """HBM traffic per launch of the dominant kernel, from the committed counter
+    summary, if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "decode_partials_llama31_8b_32k_traffic.json")
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("source_hash") != source_hash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama31_8b_32k")
+    ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated (0: >= 1 GiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode path has no cross-GPU step in this build; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from rank_kv_cache_lrkv_amd import binding as B
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    if w.n_layers != 1:
+        w = w.scaled(n_layers=1, n_steps=0, mixed_ranks=False)
+    td = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(td).cuda()
+
+    log(f"workload {w.name}: batch {w.batch}, heads {w.n_q_heads}/{w.n_kv_heads}, n {w.n_ctx}, "
+        f"ranks {w.rank_k}/{w.rank_v}, window {w.window}")
+    t0 = time.time()
+    L0, compress = build_cache(w, B, dev)
+    log(f"cache built and compressed on the GPU in {time.time() - t0:.1f} s "
+        f"(compress {compress['ms']:.3f} ms, {compress['gbps']} GB/s)")
+    nb = algorithmic_bytes(w, w.n_ctx)
+    R = args.replicas or max(1, math.ceil((1 << 30) / nb["call"]))
+    layers = [L0] + [replicate(L0, B) for _ in range(R - 1)]
+    n = w.n_ctx
+    S = w.n_splits or B.lrkv_decode_auto_splits(L0, n)
+    q = dev(np.stack([synth.queries(w, 0, 0, b) for b in range(w.batch)]))
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device="cuda")
+    ws = B.workspace(L0, S)
+    scale = 1.0 / math.sqrt(128)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        B.lrkv_decode_attn(layers[i % R], n, q, out, scale, S, ws, stream=stream)
+
+    log(f"{R} cache replicas ({R * nb['call'] / 2**30:.2f} GiB), {S} splits; warmup {args.warmup}")
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all(), "non-finite decode output"
+
+    # timed region: whole calls, events on the stream the kernels run on
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        call(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"timed {args.steps} calls: {ms_per_step * 1e3:.2f} us per call")
+
+    # the dominant kernel alone: events around each partials launch
+    e_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    e_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for i in range(args.steps):
+        L = layers[i % R]
+        e_start[i].record(stream)
+        B.lrkv_decode_partials(L, n, q, scale, S, ws, stream=stream)
+        e_end[i].record(stream)
+        B.lrkv_decode_combine(L, S, ws, out, stream=stream)
+    torch.cuda.synchronize()
+    k2_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(e_start, e_end)]))
+    log(f"partials kernel: {k2_ms * 1e3:.2f} us per launch")
+
+    t_call = ms_per_step * 1e-3
+    value = w.batch * w.n_q_heads * n / t_call
+    achieved = nb["partials"] / (k2_ms * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profile(src_hash)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log(f"oracle: {cpu['value']:.3e} tokens*heads/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": "compressed-KV decode attention tokens*heads/s (+ achieved HBM GB/s vs peak)",
+        "value": value,
+        "unit": "tokens*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded decaying-spectrum keys/values, calibration-SVD bases)",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": 128, "n_ctx": n, "rank_k": w.rank_k,
+                   "rank_v": w.rank_v, "window": w.window, "n_splits": S, "cache_replicas": R},
+        "roofline": {"bound": "hbm", "kernel": DOMINANT_KERNEL, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "alg_bytes_per_launch": nb["partials"],
+                     "us_per_launch": round(k2_ms * 1e3, 3), "source_hash": src_hash},
+        "call_hbm_gbps": round(nb["call"] / t_call / 1e9, 1),
+        "call_alg_bytes": nb["call"],
+        "compress": compress,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

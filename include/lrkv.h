@@ -1,0 +1,194 @@
+/*
+ * lrkv.h - decode attention read directly from a low-rank-compressed KV cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method.  Per (layer, KV head) the keys (taken after RoPE) and the values
+ * are stored as r-dim codes under fixed bases with orthonormal columns,
+ * C_K = K U_K and C_V = V U_V (blog "Half the Memory, None of the Answers Lost",
+ * section 04).  The first token and the most recent `window` tokens stay at full
+ * rank as anchors (OjaKV article, FAQ on which tokens are compressed).  A decode
+ * step scores the codes in code space with the projected query q~ = U_K^T q, the
+ * anchors with q itself, runs one softmax over both, sums the values of the codes
+ * in the r_v-dim code space and up-projects that sum once (blog section 08: the
+ * compressed form is algebraically the attention over the reconstructed cache,
+ * so the full tensors are never rebuilt).
+ *
+ * Conventions for every entry point:
+ *  - head_dim is fixed at 128.  Query head i reads KV head i / g, g = n_q_heads / n_kv_heads.
+ *  - All tensors are caller-owned.  The library allocates no device memory and keeps
+ *    no per-call state; device pointers are plain HIP device addresses.
+ *  - Every argument is checked on the host before any HIP call; on an error
+ *    nothing is launched and no buffer is touched.  Launch failures return
+ *    LRKV_ERR_HIP; faults inside a kernel surface at the caller's next stream sync.
+ *  - Work is enqueued on `stream` (0 = the null stream) and returns at once.
+ *    Calls on different streams that write the same buffers race.
+ *  - Device pointers must be 16-byte aligned.
+ */
+#ifndef LRKV_H
+#define LRKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *lrkv_stream_t; /* same object as hipStream_t */
+
+typedef enum lrkv_status {
+  LRKV_OK = 0,
+  LRKV_ERR_NULL = 1,      /* a required pointer is NULL */
+  LRKV_ERR_SHAPE = 2,     /* a size, count, position or stride is out of range */
+  LRKV_ERR_RANK = 3,      /* a rank is not a multiple of 16 in [16, 128] */
+  LRKV_ERR_DTYPE = 4,     /* unknown storage type */
+  LRKV_ERR_ALIGN = 5,     /* a device pointer or row stride is not 16-byte aligned */
+  LRKV_ERR_CAPACITY = 6,  /* the code slots needed exceed `cap` */
+  LRKV_ERR_WORKSPACE = 7, /* workspace missing or smaller than lrkv_decode_workspace_size */
+  LRKV_ERR_HIP = 8        /* a kernel launch failed */
+} lrkv_status;
+
+typedef enum lrkv_dtype {
+  LRKV_F32 = 0,  /* float32 storage and float32 arithmetic */
+  LRKV_BF16 = 1  /* bfloat16 storage, float32 accumulation */
+} lrkv_dtype;
+
+#define LRKV_HEAD_DIM 128
+#define LRKV_BLOCK 32         /* code slots per layout block */
+#define LRKV_MAX_KV_HEADS 64  /* per layer */
+#define LRKV_MAX_GROUP 16     /* query heads per KV head */
+#define LRKV_MAX_SPLITS 1024
+
+/*
+ * One layer of compressed cache.  Storage type `dtype` applies to the bases, the
+ * codes, the anchors, the queries and the compress/append inputs; the decode
+ * output is always float32.
+ *
+ * rank_k[h], rank_v[h] (host arrays of n_kv_heads): multiples of 16 in [16, 128].
+ *
+ * bases (device): the heads in order; head h holds U_K(h) as [128][rank_k[h]] and
+ *   right after it U_V(h) as [128][rank_v[h]], row-major, so U_K(h) starts at
+ *   element 128 * sum_{h' < h} (rank_k[h'] + rank_v[h']).  Codes are x U (x a
+ *   128-row vector), so the columns of U are the basis directions.
+ *
+ * codes_k, codes_v (device): the heads in order; head h owns `batch * cap * r`
+ *   elements (r = rank_k[h] resp. rank_v[h]), starting at element
+ *   batch * cap * sum_{h' < h} r(h').  Inside, batch row b owns cap * r elements
+ *   (cap a multiple of 32), grouped in blocks of 32 slots (32 * r elements each).
+ *   Code slot j holds token j + 1 (the tokens between the first one and the
+ *   window).  Slot j lives in block j / 32 at in-block position t = j % 32, and
+ *   column c of its code sits at in-block element
+ *     keys:   ((t / 16) * (r / 8) + c / 8) * 128 + (t % 16) * 8 + c % 8
+ *     values: ((t % 16) / 4 * r + c) * 8 + 4 * (t / 16) + t % 4
+ *   i.e. 8 consecutive columns of 16 tokens (keys), or 8 tokens of one column
+ *   (values), are 8 consecutive elements: the order the matrix cores consume.
+ *
+ * anchor_k, anchor_v (device): [batch][n_kv_heads][1 + window][128].  Slot 0 is
+ *   token 0; a token p >= 1 inside the window sits in slot 1 + (p - 1) % window.
+ *   At context n the valid slots are the prefix [0, min(n, 1 + window)).
+ */
+typedef struct lrkv_layer {
+  int32_t dtype;          /* lrkv_dtype */
+  int32_t batch;          /* >= 1 */
+  int32_t n_q_heads;      /* multiple of n_kv_heads, group <= LRKV_MAX_GROUP */
+  int32_t n_kv_heads;     /* 1 .. LRKV_MAX_KV_HEADS */
+  int32_t window;         /* W >= 0 recent tokens kept at full rank */
+  int32_t cap;            /* code slots per (batch row, KV head); multiple of 32, >= 0 */
+  const int32_t *rank_k;  /* host [n_kv_heads] */
+  const int32_t *rank_v;  /* host [n_kv_heads] */
+  const void *bases;      /* device, see above */
+  void *codes_k;          /* device */
+  void *codes_v;          /* device */
+  void *anchor_k;         /* device [batch][n_kv_heads][1 + window][128] */
+  void *anchor_v;         /* device */
+} lrkv_layer;
+
+/*
+ * Prefill compression (blog section 04: one projection per (layer, head), keys
+ * after RoPE).  For every (batch row b, KV head h) and t in [0, n_tok): code slot
+ * slot0 + t of `which` (0 = keys with U_K, 1 = values with U_V) receives
+ * x[b, h, t, :] U, rounded to the storage type (bf16: round to nearest even of
+ * the float32 accumulation).
+ *   x: device, element (b, h, t, i) at x + b*stride_b + h*stride_h + t*stride_t + i
+ *      (strides in elements of the storage type; the 128 features contiguous).
+ * Errors: LRKV_ERR_SHAPE if n_tok < 0, slot0 < 0 or a stride is negative;
+ * LRKV_ERR_CAPACITY if slot0 + n_tok > cap; LRKV_ERR_ALIGN if x or a stride is
+ * not 16-byte aligned.  n_tok == 0 is a no-op.
+ */
+lrkv_status lrkv_compress(const lrkv_layer *L, int32_t which, const void *x,
+                          int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                          int32_t n_tok, int32_t slot0, lrkv_stream_t stream);
+
+/*
+ * Full-rank anchors (OjaKV FAQ: the first token and the most recent tokens are
+ * kept uncompressed).  Copies tokens [pos0, pos0 + n_tok) of k and v into their
+ * anchor slots (slot 0 for token 0, 1 + (p - 1) % window otherwise).
+ *   k, v: device, element (b, h, t, i) at base + b*stride_b + h*stride_h + t*stride_t + i,
+ *         where t = p - pos0.
+ * Errors: LRKV_ERR_SHAPE unless n_tok >= 0, pos0 >= 0 and the range maps to
+ * distinct slots (pos0 == 0: n_tok <= 1 + window; pos0 >= 1: n_tok <= window).
+ */
+lrkv_status lrkv_store_anchors(const lrkv_layer *L, const void *k, const void *v,
+                               int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                               int32_t pos0, int32_t n_tok, lrkv_stream_t stream);
+
+/*
+ * Cache maintenance of one decode step, the same for every batch row: the new
+ * token at position `pos` (k_new, v_new: device [batch][n_kv_heads][128]).
+ *  - window >= 1 and pos > window: token pos - window leaves the window; its anchor
+ *    slot is compressed into code slot pos - window - 1 (keys and values), then the
+ *    new token takes over that slot.
+ *  - window == 0 and pos >= 1: the new token is compressed into code slot pos - 1.
+ *  - otherwise the new token is stored into its anchor slot.
+ * Errors: LRKV_ERR_SHAPE if pos < 0; LRKV_ERR_CAPACITY if the code slot >= cap.
+ */
+lrkv_status lrkv_append(const lrkv_layer *L, const void *k_new, const void *v_new,
+                        int32_t pos, lrkv_stream_t stream);
+
+/*
+ * Decode attention (blog section 08) in two stages that lrkv_decode_attn runs
+ * back to back.
+ *
+ * n_ctx: cached tokens including the decode token (>= 1); codes cover tokens
+ *   1 .. n_ctx - window - 1 and need cap >= max(0, n_ctx - 1 - window).
+ * ctx_lens: optional device int32 [batch] of per-row lengths (ragged batches);
+ *   each is clamped into [1, n_ctx].  NULL: every row has n_ctx tokens.
+ * q: device [batch][n_q_heads][128] in the storage type.
+ * sm_scale: score scale, normally 1/sqrt(128).
+ * n_splits: the compressed tokens of each (row, KV head) are cut into this many
+ *   contiguous ranges of 32-slot blocks, each scored by its own workgroup
+ *   (1 .. LRKV_MAX_SPLITS; 0 = lrkv_decode_auto_splits).  Results agree across
+ *   n_splits to rounding; a fixed n_splits is bitwise reproducible.
+ * workspace: device, >= lrkv_decode_workspace_size(L, n_splits) bytes, float32
+ *   partial results; fully rewritten by each call.
+ * out: device float32 [batch][n_q_heads][128].
+ */
+size_t lrkv_decode_workspace_size(const lrkv_layer *L, int32_t n_splits);
+int32_t lrkv_decode_auto_splits(const lrkv_layer *L, int32_t n_ctx);
+
+/* Stage 1: per (row, query head, split) the running max (log2 units), the
+ * softmax denominator and the rank-space value sum; per (row, query head) the
+ * same over the anchors with a 128-dim value sum. */
+lrkv_status lrkv_decode_partials(const lrkv_layer *L, int32_t n_ctx, const int32_t *ctx_lens,
+                                 const void *q, float sm_scale, int32_t n_splits,
+                                 void *workspace, size_t workspace_bytes, lrkv_stream_t stream);
+
+/* Stage 2: merge the partials of each (row, query head), up-project the
+ * rank-space sum once with U_V, add the anchor part and normalise. */
+lrkv_status lrkv_decode_combine(const lrkv_layer *L, int32_t n_splits, const void *workspace,
+                                size_t workspace_bytes, float *out, lrkv_stream_t stream);
+
+lrkv_status lrkv_decode_attn(const lrkv_layer *L, int32_t n_ctx, const int32_t *ctx_lens,
+                             const void *q, float *out, float sm_scale, int32_t n_splits,
+                             void *workspace, size_t workspace_bytes, lrkv_stream_t stream);
+
+const char *lrkv_status_string(lrkv_status s);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int32_t lrkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRKV_H */

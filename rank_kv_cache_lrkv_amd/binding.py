@@ -1,0 +1,248 @@
+"""Thin ctypes binding of liblrkv.so (include/lrkv.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's kernels.  The
+functions keep the C names.  There is no fallback: if the library is missing
+and cannot be built, loading raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_void_p
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+from . import layout
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblrkv.so")
+
+LRKV_F32, LRKV_BF16 = 0, 1
+HEAD_DIM = 128
+BLOCK = 32
+
+STATUS = {
+    0: "LRKV_OK", 1: "LRKV_ERR_NULL", 2: "LRKV_ERR_SHAPE", 3: "LRKV_ERR_RANK",
+    4: "LRKV_ERR_DTYPE", 5: "LRKV_ERR_ALIGN", 6: "LRKV_ERR_CAPACITY",
+    7: "LRKV_ERR_WORKSPACE", 8: "LRKV_ERR_HIP",
+}
+
+
+class LrkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({_status_string(status)})")
+
+
+class lrkv_layer(ctypes.Structure):
+    _fields_ = [
+        ("dtype", c_int32), ("batch", c_int32), ("n_q_heads", c_int32),
+        ("n_kv_heads", c_int32), ("window", c_int32), ("cap", c_int32),
+        ("rank_k", POINTER(c_int32)), ("rank_v", POINTER(c_int32)),
+        ("bases", c_void_p), ("codes_k", c_void_p), ("codes_v", c_void_p),
+        ("anchor_k", c_void_p), ("anchor_v", c_void_p),
+    ]
+
+
+_lib = None
+_lock = threading.Lock()
+
+# (name, restype, argtypes) for every entry point of include/lrkv.h
+_P = POINTER(lrkv_layer)
+SIGNATURES = [
+    ("lrkv_compress", c_int32, [_P, c_int32, c_void_p, c_int64, c_int64, c_int64, c_int32, c_int32, c_void_p]),
+    ("lrkv_store_anchors", c_int32, [_P, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int32, c_int32, c_void_p]),
+    ("lrkv_append", c_int32, [_P, c_void_p, c_void_p, c_int32, c_void_p]),
+    ("lrkv_decode_workspace_size", c_size_t, [_P, c_int32]),
+    ("lrkv_decode_auto_splits", c_int32, [_P, c_int32]),
+    ("lrkv_decode_partials", c_int32, [_P, c_int32, c_void_p, c_void_p, c_float, c_int32, c_void_p, c_size_t, c_void_p]),
+    ("lrkv_decode_combine", c_int32, [_P, c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
+    ("lrkv_decode_attn", c_int32, [_P, c_int32, c_void_p, c_void_p, c_void_p, c_float, c_int32, c_void_p, c_size_t, c_void_p]),
+    ("lrkv_status_string", ctypes.c_char_p, [c_int32]),
+    ("lrkv_version", c_int32, []),
+]
+
+
+def lib():
+    """Load liblrkv.so (building it first only if it does not exist)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                from .build import build
+                build()
+            h = ctypes.CDLL(LIB_PATH)
+            for name, res, args in SIGNATURES:
+                f = getattr(h, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = h
+    return _lib
+
+
+def _status_string(status: int) -> str:
+    try:
+        return lib().lrkv_status_string(status).decode()
+    except Exception:  # pragma: no cover - only while reporting another error
+        return "?"
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise LrkvError(status, where)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+# ---------------------------------------------------------------------------
+# a layer of compressed cache in torch-owned device memory
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Layer:
+    """One layer of compressed cache.  The tensors follow the layouts of lrkv.h;
+    ``struct`` is the C description handed to every call."""
+
+    dtype: int
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    window: int
+    cap: int
+    rank_k: np.ndarray
+    rank_v: np.ndarray
+    bases: "object"
+    codes_k: "object"
+    codes_v: "object"
+    anchor_k: "object"
+    anchor_v: "object"
+    _rk: object = field(default=None, repr=False)
+    _rv: object = field(default=None, repr=False)
+    struct: lrkv_layer = field(default=None, repr=False)
+
+    def __post_init__(self):
+        self._rk = (c_int32 * self.n_kv_heads)(*[int(x) for x in self.rank_k])
+        self._rv = (c_int32 * self.n_kv_heads)(*[int(x) for x in self.rank_v])
+        self.struct = lrkv_layer(
+            self.dtype, self.batch, self.n_q_heads, self.n_kv_heads, self.window, self.cap,
+            ctypes.cast(self._rk, POINTER(c_int32)), ctypes.cast(self._rv, POINTER(c_int32)),
+            _ptr(self.bases), _ptr(self.codes_k), _ptr(self.codes_v),
+            _ptr(self.anchor_k), _ptr(self.anchor_v))
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def torch_dtype(self):
+        import torch
+        return torch.float32 if self.dtype == LRKV_F32 else torch.bfloat16
+
+    @classmethod
+    def allocate(cls, *, dtype: int, batch: int, n_q_heads: int, n_kv_heads: int, window: int,
+                 cap: int, rank_k: Sequence[int], rank_v: Sequence[int], device="cuda",
+                 bases=None) -> "Layer":
+        """Allocate zeroed codes and anchors (torch) for the given geometry.
+        ``bases`` (optional) is the flat bases tensor; otherwise zeros."""
+        import torch
+        td = torch.float32 if dtype == LRKV_F32 else torch.bfloat16
+        rk = np.asarray(rank_k, np.int32)
+        rv = np.asarray(rank_v, np.int32)
+        cap = layout.round_cap(cap)
+        nb = layout.bases_elems(rk, rv)
+        if bases is None:
+            bases = torch.zeros(nb, dtype=td, device=device)
+        assert bases.numel() == nb and bases.dtype == td
+        ck = torch.zeros(max(1, layout.codes_elems(rk, batch, cap)), dtype=td, device=device)
+        cv = torch.zeros(max(1, layout.codes_elems(rv, batch, cap)), dtype=td, device=device)
+        ak = torch.zeros((batch, n_kv_heads, 1 + window, HEAD_DIM), dtype=td, device=device)
+        av = torch.zeros_like(ak)
+        return cls(dtype, batch, n_q_heads, n_kv_heads, window, cap, rk, rv, bases, ck, cv, ak, av)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def lrkv_compress(layer: Layer, which: int, x, n_tok: int, slot0: int, stream=None):
+    """x: device tensor viewed as [batch][n_kv_heads][>= n_tok][128] (any strides,
+    last dimension contiguous)."""
+    sb, sh, st, si = x.stride()
+    assert si == 1
+    _check(lib().lrkv_compress(ctypes.byref(layer.struct), which, _ptr(x), sb, sh, st, n_tok, slot0,
+                               _stream(stream)), "lrkv_compress")
+
+
+def lrkv_store_anchors(layer: Layer, k, v, pos0: int, n_tok: int, stream=None):
+    assert k.stride() == v.stride() and k.stride()[3] == 1
+    sb, sh, st, _ = k.stride()
+    _check(lib().lrkv_store_anchors(ctypes.byref(layer.struct), _ptr(k), _ptr(v), sb, sh, st, pos0,
+                                    n_tok, _stream(stream)), "lrkv_store_anchors")
+
+
+def lrkv_append(layer: Layer, k_new, v_new, pos: int, stream=None):
+    assert k_new.is_contiguous() and v_new.is_contiguous()
+    _check(lib().lrkv_append(ctypes.byref(layer.struct), _ptr(k_new), _ptr(v_new), pos,
+                             _stream(stream)), "lrkv_append")
+
+
+def lrkv_decode_workspace_size(layer: Layer, n_splits: int) -> int:
+    return int(lib().lrkv_decode_workspace_size(ctypes.byref(layer.struct), n_splits))
+
+
+def lrkv_decode_auto_splits(layer: Layer, n_ctx: int) -> int:
+    return int(lib().lrkv_decode_auto_splits(ctypes.byref(layer.struct), n_ctx))
+
+
+def workspace(layer: Layer, n_splits: int, device="cuda"):
+    """A workspace tensor of the required size (uint8)."""
+    import torch
+    n = lrkv_decode_workspace_size(layer, n_splits)
+    if n == 0:
+        raise LrkvError(2, "lrkv_decode_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def lrkv_decode_partials(layer: Layer, n_ctx: int, q, sm_scale: float, n_splits: int, ws,
+                         ctx_lens=None, stream=None):
+    _check(lib().lrkv_decode_partials(ctypes.byref(layer.struct), n_ctx, _ptr(ctx_lens), _ptr(q),
+                                      sm_scale, n_splits, _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream(stream)), "lrkv_decode_partials")
+
+
+def lrkv_decode_combine(layer: Layer, n_splits: int, ws, out, stream=None):
+    _check(lib().lrkv_decode_combine(ctypes.byref(layer.struct), n_splits, _ptr(ws),
+                                     ws.numel() * ws.element_size(), _ptr(out), _stream(stream)),
+           "lrkv_decode_combine")
+
+
+def lrkv_decode_attn(layer: Layer, n_ctx: int, q, out, sm_scale: float, n_splits: int, ws,
+                     ctx_lens=None, stream=None):
+    _check(lib().lrkv_decode_attn(ctypes.byref(layer.struct), n_ctx, _ptr(ctx_lens), _ptr(q),
+                                  _ptr(out), sm_scale, n_splits, _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)),
+           "lrkv_decode_attn")
+
+
+def lrkv_version() -> int:
+    return int(lib().lrkv_version())
+
+
+def exported_names() -> List[str]:
+    return [s[0] for s in SIGNATURES]

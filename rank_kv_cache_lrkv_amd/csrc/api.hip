@@ -1,0 +1,250 @@
+// C entry points: argument checks on the host (before any HIP call), layout
+// offsets, then the launches.  No device memory is allocated here.
+
+#include <cstring>
+
+#include "lrkv_internal.h"
+
+using namespace lrkv;
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_rank(int32_t r) { return r >= 16 && r <= 128 && r % 16 == 0; }
+int elem_bytes(int32_t dtype) { return dtype == LRKV_F32 ? 4 : 2; }
+
+// Checks the layer description and fills the kernel-side copy.
+lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
+  if (!L) return LRKV_ERR_NULL;
+  if (L->dtype != LRKV_F32 && L->dtype != LRKV_BF16) return LRKV_ERR_DTYPE;
+  if (L->batch < 1 || L->n_kv_heads < 1 || L->n_kv_heads > LRKV_MAX_KV_HEADS) return LRKV_ERR_SHAPE;
+  if (L->n_q_heads < L->n_kv_heads || L->n_q_heads % L->n_kv_heads) return LRKV_ERR_SHAPE;
+  if (L->n_q_heads / L->n_kv_heads > LRKV_MAX_GROUP) return LRKV_ERR_SHAPE;
+  if (L->window < 0 || L->cap < 0 || L->cap % LRKV_BLOCK) return LRKV_ERR_SHAPE;
+  if (!L->rank_k || !L->rank_v || !L->bases || !L->codes_k || !L->codes_v || !L->anchor_k ||
+      !L->anchor_v)
+    return LRKV_ERR_NULL;
+  if (!aligned16(L->bases) || !aligned16(L->codes_k) || !aligned16(L->codes_v) ||
+      !aligned16(L->anchor_k) || !aligned16(L->anchor_v))
+    return LRKV_ERR_ALIGN;
+  std::memset(A, 0, sizeof(*A));
+  A->dtype = L->dtype;
+  A->batch = L->batch;
+  A->n_q = L->n_q_heads;
+  A->n_kv = L->n_kv_heads;
+  A->group = L->n_q_heads / L->n_kv_heads;
+  A->window = L->window;
+  A->cap = L->cap;
+  A->bases = L->bases;
+  A->codes_k = L->codes_k;
+  A->codes_v = L->codes_v;
+  A->anchor_k = L->anchor_k;
+  A->anchor_v = L->anchor_v;
+  int64_t ub = 0, ck = 0, cv = 0;
+  int rv_max = 0;
+  for (int h = 0; h < L->n_kv_heads; ++h) {
+    const int32_t rk = L->rank_k[h], rv = L->rank_v[h];
+    if (!valid_rank(rk) || !valid_rank(rv)) return LRKV_ERR_RANK;
+    HeadInfo &hd = A->heads[h];
+    hd.rk = rk;
+    hd.rv = rv;
+    hd.u_k = int32_t(ub);
+    hd.u_v = int32_t(ub + int64_t(kD) * rk);
+    hd.ck = ck;
+    hd.cv = cv;
+    ub += int64_t(kD) * (rk + rv);
+    ck += int64_t(L->batch) * L->cap * rk;
+    cv += int64_t(L->batch) * L->cap * rv;
+    rv_max = rv > rv_max ? rv : rv_max;
+  }
+  A->rv_max = rv_max;
+  return LRKV_OK;
+}
+
+int32_t rec_floats(const LayerArgs &A) { return 4 + ((A.rv_max + 3) / 4) * 4; }
+
+int32_t auto_splits(const LayerArgs &A, int32_t n_ctx) {
+  const int64_t c = n_ctx - 1 - A.window;
+  const int64_t nblk = c > 0 ? (c + LRKV_BLOCK - 1) / LRKV_BLOCK : 0;
+  const int64_t units = int64_t(A.batch) * A.n_kv;
+  // about four workgroups of codes per compute unit (256 CUs), at least four
+  // 32-slot blocks per split
+  int64_t s = (1024 + units - 1) / units;
+  const int64_t most = nblk / 4 > 1 ? nblk / 4 : 1;
+  if (s > most) s = most;
+  if (s < 1) s = 1;
+  if (s > LRKV_MAX_SPLITS) s = LRKV_MAX_SPLITS;
+  return int32_t(s);
+}
+
+size_t ws_bytes(const LayerArgs &A, int32_t S) {
+  const size_t rows = size_t(A.batch) * A.n_q;
+  return (rows * S * rec_floats(A) + rows * kAnchorRec) * sizeof(float);
+}
+
+lrkv_status check_strides(const lrkv_layer *L, const void *x, int64_t sb, int64_t sh, int64_t st) {
+  if (sb < 0 || sh < 0 || st < 0) return LRKV_ERR_SHAPE;
+  const int64_t eb = elem_bytes(L->dtype);
+  if (!aligned16(x) || (sb * eb) % 16 || (sh * eb) % 16 || (st * eb) % 16) return LRKV_ERR_ALIGN;
+  return LRKV_OK;
+}
+
+// Builds the decode arguments; shared by the three decode entry points.
+lrkv_status make_decode(const lrkv_layer *L, const LayerArgs &A, int32_t n_ctx,
+                        const int32_t *ctx_lens, const void *q, float sm_scale, int32_t n_splits,
+                        void *ws, size_t ws_len, DecodeArgs *D) {
+  if (n_ctx < 1) return LRKV_ERR_SHAPE;
+  const int64_t c = int64_t(n_ctx) - 1 - A.window;
+  if (c > A.cap) return LRKV_ERR_CAPACITY;
+  if (n_splits < 0 || n_splits > LRKV_MAX_SPLITS) return LRKV_ERR_SHAPE;
+  if (!(sm_scale > 0.f) || sm_scale != sm_scale) return LRKV_ERR_SHAPE;
+  const int32_t S = n_splits ? n_splits : auto_splits(A, n_ctx);
+  if (!ws) return LRKV_ERR_WORKSPACE;
+  if (ws_len < ws_bytes(A, S)) return LRKV_ERR_WORKSPACE;
+  if (!aligned16(ws) || (ctx_lens && (reinterpret_cast<uintptr_t>(ctx_lens) & 3u)))
+    return LRKV_ERR_ALIGN;
+  if (q && !aligned16(q)) return LRKV_ERR_ALIGN;
+  (void)L;
+  std::memset(D, 0, sizeof(*D));
+  D->n_ctx = n_ctx;
+  D->n_splits = S;
+  D->rec = rec_floats(A);
+  D->scale_log2 = sm_scale * kLog2e;
+  D->ctx_lens = ctx_lens;
+  D->q = q;
+  D->ws_codes = static_cast<float *>(ws);
+  D->ws_anchor = static_cast<float *>(ws) + size_t(A.batch) * A.n_q * S * D->rec;
+  return LRKV_OK;
+}
+
+lrkv_status hip_status(hipError_t e) { return e == hipSuccess ? LRKV_OK : LRKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+lrkv_status lrkv_compress(const lrkv_layer *L, int32_t which, const void *x, int64_t stride_b,
+                          int64_t stride_h, int64_t stride_t, int32_t n_tok, int32_t slot0,
+                          lrkv_stream_t stream) {
+  LayerArgs A;
+  lrkv_status st = make_layer(L, &A);
+  if (st != LRKV_OK) return st;
+  if (which != 0 && which != 1) return LRKV_ERR_SHAPE;
+  if (n_tok < 0 || slot0 < 0) return LRKV_ERR_SHAPE;
+  if (int64_t(slot0) + n_tok > L->cap) return LRKV_ERR_CAPACITY;
+  if (n_tok == 0) return LRKV_OK;
+  if (!x) return LRKV_ERR_NULL;
+  st = check_strides(L, x, stride_b, stride_h, stride_t);
+  if (st != LRKV_OK) return st;
+  return hip_status(launch_compress(A, which, x, stride_b, stride_h, stride_t, n_tok, slot0,
+                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
+lrkv_status lrkv_store_anchors(const lrkv_layer *L, const void *k, const void *v, int64_t stride_b,
+                               int64_t stride_h, int64_t stride_t, int32_t pos0, int32_t n_tok,
+                               lrkv_stream_t stream) {
+  LayerArgs A;
+  lrkv_status st = make_layer(L, &A);
+  if (st != LRKV_OK) return st;
+  if (n_tok < 0 || pos0 < 0) return LRKV_ERR_SHAPE;
+  const int64_t most = pos0 == 0 ? int64_t(1) + L->window : L->window;
+  if (n_tok > most) return LRKV_ERR_SHAPE;
+  if (n_tok == 0) return LRKV_OK;
+  if (!k || !v) return LRKV_ERR_NULL;
+  st = check_strides(L, k, stride_b, stride_h, stride_t);
+  if (st == LRKV_OK) st = check_strides(L, v, stride_b, stride_h, stride_t);
+  if (st != LRKV_OK) return st;
+  return hip_status(launch_store_anchors(A, k, v, stride_b, stride_h, stride_t, pos0, n_tok,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
+lrkv_status lrkv_append(const lrkv_layer *L, const void *k_new, const void *v_new, int32_t pos,
+                        lrkv_stream_t stream) {
+  LayerArgs A;
+  lrkv_status st = make_layer(L, &A);
+  if (st != LRKV_OK) return st;
+  if (pos < 0) return LRKV_ERR_SHAPE;
+  if (!k_new || !v_new) return LRKV_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return LRKV_ERR_ALIGN;
+  const int64_t code_slot = L->window >= 1 ? int64_t(pos) - L->window - 1 : int64_t(pos) - 1;
+  if (code_slot >= L->cap) return LRKV_ERR_CAPACITY;
+  return hip_status(launch_append(A, k_new, v_new, pos, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t lrkv_decode_workspace_size(const lrkv_layer *L, int32_t n_splits) {
+  LayerArgs A;
+  if (make_layer(L, &A) != LRKV_OK) return 0;
+  if (n_splits < 1 || n_splits > LRKV_MAX_SPLITS) return 0;
+  return ws_bytes(A, n_splits);
+}
+
+int32_t lrkv_decode_auto_splits(const lrkv_layer *L, int32_t n_ctx) {
+  LayerArgs A;
+  if (make_layer(L, &A) != LRKV_OK || n_ctx < 1) return 0;
+  return auto_splits(A, n_ctx);
+}
+
+lrkv_status lrkv_decode_partials(const lrkv_layer *L, int32_t n_ctx, const int32_t *ctx_lens,
+                                 const void *q, float sm_scale, int32_t n_splits, void *workspace,
+                                 size_t workspace_bytes, lrkv_stream_t stream) {
+  LayerArgs A;
+  lrkv_status st = make_layer(L, &A);
+  if (st != LRKV_OK) return st;
+  if (!q) return LRKV_ERR_NULL;
+  DecodeArgs D;
+  st = make_decode(L, A, n_ctx, ctx_lens, q, sm_scale, n_splits, workspace, workspace_bytes, &D);
+  if (st != LRKV_OK) return st;
+  return hip_status(launch_decode_partials(A, D, reinterpret_cast<hipStream_t>(stream)));
+}
+
+lrkv_status lrkv_decode_combine(const lrkv_layer *L, int32_t n_splits, const void *workspace,
+                                size_t workspace_bytes, float *out, lrkv_stream_t stream) {
+  LayerArgs A;
+  lrkv_status st = make_layer(L, &A);
+  if (st != LRKV_OK) return st;
+  if (!out) return LRKV_ERR_NULL;
+  if (!aligned16(out)) return LRKV_ERR_ALIGN;
+  if (n_splits < 1 || n_splits > LRKV_MAX_SPLITS) return LRKV_ERR_SHAPE;
+  DecodeArgs D;
+  // the context length does not enter the combine; 1 passes every check
+  st = make_decode(L, A, 1, nullptr, nullptr, 1.f, n_splits, const_cast<void *>(workspace),
+                   workspace_bytes, &D);
+  if (st != LRKV_OK) return st;
+  return hip_status(launch_decode_combine(A, D, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+lrkv_status lrkv_decode_attn(const lrkv_layer *L, int32_t n_ctx, const int32_t *ctx_lens,
+                             const void *q, float *out, float sm_scale, int32_t n_splits,
+                             void *workspace, size_t workspace_bytes, lrkv_stream_t stream) {
+  LayerArgs A;
+  lrkv_status st = make_layer(L, &A);
+  if (st != LRKV_OK) return st;
+  if (!q || !out) return LRKV_ERR_NULL;
+  if (!aligned16(out)) return LRKV_ERR_ALIGN;
+  DecodeArgs D;
+  st = make_decode(L, A, n_ctx, ctx_lens, q, sm_scale, n_splits, workspace, workspace_bytes, &D);
+  if (st != LRKV_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = hip_status(launch_decode_partials(A, D, s));
+  if (st != LRKV_OK) return st;
+  return hip_status(launch_decode_combine(A, D, out, s));
+}
+
+const char *lrkv_status_string(lrkv_status s) {
+  switch (s) {
+    case LRKV_OK: return "ok";
+    case LRKV_ERR_NULL: return "a required pointer is NULL";
+    case LRKV_ERR_SHAPE: return "a size, count, position or stride is out of range";
+    case LRKV_ERR_RANK: return "a rank is not a multiple of 16 in [16, 128]";
+    case LRKV_ERR_DTYPE: return "unknown storage type";
+    case LRKV_ERR_ALIGN: return "a device pointer or stride is not 16-byte aligned";
+    case LRKV_ERR_CAPACITY: return "the code slots needed exceed the capacity";
+    case LRKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case LRKV_ERR_HIP: return "a HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t lrkv_version(void) { return 100; }
+
+}  // extern "C"

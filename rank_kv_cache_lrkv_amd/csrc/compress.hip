@@ -1,0 +1,159 @@
+// Cache writers: prefill projection into codes, full-rank anchor stores and the
+// per-step maintenance that moves the token leaving the recent window into the
+// code region.
+//
+// Prefill projection follows the blog "Half the Memory, None of the Answers
+// Lost", section 04 (one projection per (layer, head), keys after RoPE); the
+// anchor policy follows the OjaKV article's FAQ (first token and the most recent
+// tokens stay at full rank).
+
+#include "lrkv_internal.h"
+
+namespace lrkv {
+
+// ---------------------------------------------------------------------------
+// Generic projection: float32 storage (and any storage type as a plain path).
+// One workgroup per (64-token tile, batch row, KV head).  The 64x128 input tile
+// is staged in LDS as float32; each thread produces code columns with a float32
+// dot product over the 128 features; the basis is read through the cache.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_compress_generic(LayerArgs L, int which, const T *x,
+                                                          int64_t sb, int64_t sh, int64_t st,
+                                                          int n_tok, int slot0) {
+  constexpr int TT = 64;
+  __shared__ float sx[TT][kD + 1];
+  const int unit = blockIdx.y;
+  const int b = unit / L.n_kv, h = unit % L.n_kv;
+  const HeadInfo hd = L.heads[h];
+  const int r = which ? hd.rv : hd.rk;
+  const T *U = static_cast<const T *>(L.bases) + (which ? hd.u_v : hd.u_k);
+  T *codes = static_cast<T *>(which ? L.codes_v : L.codes_k) + (which ? hd.cv : hd.ck) +
+             int64_t(b) * L.cap * r;
+  const int t0 = blockIdx.x * TT;
+  const int nt = min(TT, n_tok - t0);
+  const T *xb = x + b * sb + h * sh + int64_t(t0) * st;
+  for (int i = threadIdx.x; i < nt * kD; i += blockDim.x) {
+    const int t = i / kD, k = i % kD;
+    sx[t][k] = to_f32(xb[int64_t(t) * st + k]);
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < nt * r; o += blockDim.x) {
+    const int t = o / r, c = o % r;
+    float acc = 0.f;
+    for (int k = 0; k < kD; ++k) acc = fmaf(sx[t][k], to_f32(U[k * r + c]), acc);
+    const int j = slot0 + t0 + t;
+    codes[which ? vslot(j, c, r) : kslot(j, c, r)] = from_f32<T>(acc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Anchor store: one workgroup (128 threads, one per feature) per (token, row, head).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(128) void k_store_anchors(LayerArgs L, const T *k, const T *v,
+                                                       int64_t sb, int64_t sh, int64_t st,
+                                                       int pos0) {
+  const int t = blockIdx.x;
+  const int unit = blockIdx.y;
+  const int b = unit / L.n_kv, h = unit % L.n_kv;
+  const int slot = anchor_slot(pos0 + t, L.window);
+  const int64_t src = b * sb + h * sh + int64_t(t) * st + threadIdx.x;
+  const int64_t dst = (int64_t(unit) * (1 + L.window) + slot) * kD + threadIdx.x;
+  static_cast<T *>(L.anchor_k)[dst] = k[src];
+  static_cast<T *>(L.anchor_v)[dst] = v[src];
+}
+
+// ---------------------------------------------------------------------------
+// Decode-step maintenance: one workgroup (128 threads) per (row, head).  The row
+// to compress is staged in LDS before the anchor slot is overwritten, so the
+// read of the leaving token and the write of the new one cannot overlap.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, const T *vnew, int pos) {
+  __shared__ float rk_row[kD], rv_row[kD];
+  const int unit = blockIdx.x;
+  const int b = unit / L.n_kv, h = unit % L.n_kv;
+  const int W = L.window;
+  const int tid = threadIdx.x;
+  const HeadInfo hd = L.heads[h];
+  T *ak = static_cast<T *>(L.anchor_k) + int64_t(unit) * (1 + W) * kD;
+  T *av = static_cast<T *>(L.anchor_v) + int64_t(unit) * (1 + W) * kD;
+  const T *kn = knew + int64_t(unit) * kD;
+  const T *vn = vnew + int64_t(unit) * kD;
+
+  int slot = -1, code_slot = -1;
+  if (W >= 1 && pos > W) {
+    slot = 1 + (pos - 1) % W;  // holds token pos - W, which now leaves the window
+    code_slot = pos - W - 1;
+    rk_row[tid] = to_f32(ak[slot * kD + tid]);
+    rv_row[tid] = to_f32(av[slot * kD + tid]);
+  } else if (W == 0 && pos >= 1) {
+    code_slot = pos - 1;
+    rk_row[tid] = to_f32(kn[tid]);
+    rv_row[tid] = to_f32(vn[tid]);
+  } else {
+    slot = anchor_slot(pos, W);
+  }
+  __syncthreads();
+  if (code_slot >= 0) {
+    const T *Uk = static_cast<const T *>(L.bases) + hd.u_k;
+    const T *Uv = static_cast<const T *>(L.bases) + hd.u_v;
+    T *ck = static_cast<T *>(L.codes_k) + hd.ck + int64_t(b) * L.cap * hd.rk;
+    T *cv = static_cast<T *>(L.codes_v) + hd.cv + int64_t(b) * L.cap * hd.rv;
+    if (tid < hd.rk) {
+      float acc = 0.f;
+      for (int k = 0; k < kD; ++k) acc = fmaf(rk_row[k], to_f32(Uk[k * hd.rk + tid]), acc);
+      ck[kslot(code_slot, tid, hd.rk)] = from_f32<T>(acc);
+    }
+    if (tid < hd.rv) {
+      float acc = 0.f;
+      for (int k = 0; k < kD; ++k) acc = fmaf(rv_row[k], to_f32(Uv[k * hd.rv + tid]), acc);
+      cv[vslot(code_slot, tid, hd.rv)] = from_f32<T>(acc);
+    }
+  }
+  if (slot >= 0) {
+    ak[slot * kD + tid] = kn[tid];
+    av[slot * kD + tid] = vn[tid];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_compress(const LayerArgs &L, int which, const void *x, int64_t sb, int64_t sh,
+                           int64_t st, int n_tok, int slot0, hipStream_t s) {
+  dim3 grid((n_tok + 63) / 64, L.batch * L.n_kv);
+  if (L.dtype == LRKV_F32)
+    hipLaunchKernelGGL(k_compress_generic<float>, grid, dim3(256), 0, s, L, which,
+                       static_cast<const float *>(x), sb, sh, st, n_tok, slot0);
+  else
+    hipLaunchKernelGGL(k_compress_generic<bf16_t>, grid, dim3(256), 0, s, L, which,
+                       static_cast<const bf16_t *>(x), sb, sh, st, n_tok, slot0);
+  return hipGetLastError();
+}
+
+hipError_t launch_store_anchors(const LayerArgs &L, const void *k, const void *v, int64_t sb,
+                                int64_t sh, int64_t st, int pos0, int n_tok, hipStream_t s) {
+  dim3 grid(n_tok, L.batch * L.n_kv);
+  if (L.dtype == LRKV_F32)
+    hipLaunchKernelGGL(k_store_anchors<float>, grid, dim3(kD), 0, s, L,
+                       static_cast<const float *>(k), static_cast<const float *>(v), sb, sh, st, pos0);
+  else
+    hipLaunchKernelGGL(k_store_anchors<bf16_t>, grid, dim3(kD), 0, s, L,
+                       static_cast<const bf16_t *>(k), static_cast<const bf16_t *>(v), sb, sh, st, pos0);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const LayerArgs &L, const void *k, const void *v, int pos, hipStream_t s) {
+  dim3 grid(L.batch * L.n_kv);
+  if (L.dtype == LRKV_F32)
+    hipLaunchKernelGGL(k_append<float>, grid, dim3(kD), 0, s, L, static_cast<const float *>(k),
+                       static_cast<const float *>(v), pos);
+  else
+    hipLaunchKernelGGL(k_append<bf16_t>, grid, dim3(kD), 0, s, L, static_cast<const bf16_t *>(k),
+                       static_cast<const bf16_t *>(v), pos);
+  return hipGetLastError();
+}
+
+}  // namespace lrkv

@@ -1,0 +1,97 @@
+// Internal definitions shared by the kernels and the host entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lrkv.h"
+
+namespace lrkv {
+
+constexpr int kD = LRKV_HEAD_DIM;
+constexpr int kBlock = LRKV_BLOCK;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Per-KV-head geometry, element offsets precomputed on the host.
+struct HeadInfo {
+  int32_t rk, rv;
+  int32_t u_k, u_v;  // offsets of U_K(h), U_V(h) in the bases buffer
+  int64_t ck, cv;    // offsets of head h's [batch][cap][r] code region
+};
+
+struct LayerArgs {
+  int32_t dtype, batch, n_q, n_kv, group, window, cap, rv_max;
+  const void *bases;
+  void *codes_k, *codes_v, *anchor_k, *anchor_v;
+  HeadInfo heads[LRKV_MAX_KV_HEADS];
+};
+
+struct DecodeArgs {
+  int32_t n_ctx;
+  int32_t n_splits;
+  int32_t rec;           // floats per code-split record: 4 + rv_max (rounded to 4)
+  float scale_log2;      // sm_scale * log2(e): scores are kept in log2 units
+  const int32_t *ctx_lens;
+  const void *q;
+  float *ws_codes;       // [batch][n_q][n_splits][rec]
+  float *ws_anchor;      // [batch][n_q][4 + 128]
+};
+
+constexpr int kAnchorRec = 4 + kD;
+
+// ---------------------------------------------------------------------------
+// storage types
+// ---------------------------------------------------------------------------
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+  // gfx950 converts with round-to-nearest-even in hardware (v_cvt_pk_bf16_f32)
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(bf16_t, b);
+}
+
+// ---------------------------------------------------------------------------
+// code layout: in-block element positions (see lrkv.h)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int kpos(int t, int c, int r) {
+  return ((t >> 4) * (r >> 3) + (c >> 3)) * 128 + (t & 15) * 8 + (c & 7);
+}
+__device__ __forceinline__ int vpos(int t, int c, int r) {
+  return (((t & 15) >> 2) * r + c) * 8 + ((t >> 4) << 2) + (t & 3);
+}
+// element offset of code slot j, column c, inside one (row, head) region
+__device__ __forceinline__ int64_t kslot(int j, int c, int r) {
+  return int64_t(j >> 5) * (kBlock * r) + kpos(j & 31, c, r);
+}
+__device__ __forceinline__ int64_t vslot(int j, int c, int r) {
+  return int64_t(j >> 5) * (kBlock * r) + vpos(j & 31, c, r);
+}
+
+__device__ __forceinline__ int anchor_slot(int p, int window) {
+  return p == 0 ? 0 : 1 + (p - 1) % window;
+}
+
+// context length of batch row b
+__device__ __forceinline__ int row_ctx(const DecodeArgs &d, int b) {
+  if (!d.ctx_lens) return d.n_ctx;
+  int n = d.ctx_lens[b];
+  return n < 1 ? 1 : (n > d.n_ctx ? d.n_ctx : n);
+}
+
+// ---------------------------------------------------------------------------
+// host-side launchers (defined in the .hip files)
+// ---------------------------------------------------------------------------
+hipError_t launch_compress(const LayerArgs &L, int which, const void *x, int64_t sb, int64_t sh,
+                           int64_t st, int n_tok, int slot0, hipStream_t s);
+hipError_t launch_store_anchors(const LayerArgs &L, const void *k, const void *v, int64_t sb,
+                                int64_t sh, int64_t st, int pos0, int n_tok, hipStream_t s);
+hipError_t launch_append(const LayerArgs &L, const void *k, const void *v, int pos, hipStream_t s);
+hipError_t launch_decode_partials(const LayerArgs &L, const DecodeArgs &d, hipStream_t s);
+hipError_t launch_decode_combine(const LayerArgs &L, const DecodeArgs &d, float *out, hipStream_t s);
+
+}  // namespace lrkv

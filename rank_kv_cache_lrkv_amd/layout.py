@@ -1,0 +1,79 @@
+"""Host-side helpers for the buffer layouts of include/lrkv.h (NumPy, no GPU).
+
+Used to size buffers and to move codes between the logical (tokens, rank)
+view and the blocked order the kernels read.
+"""
+
+from __future__ import annotations
+
+from typing import Sequence
+
+import numpy as np
+
+HEAD_DIM = 128
+BLOCK = 32
+
+
+def round_cap(n: int) -> int:
+    """Smallest valid capacity (a multiple of 32 slots) holding n codes."""
+    n = max(0, int(n))
+    return (n + BLOCK - 1) // BLOCK * BLOCK
+
+
+def bases_elems(rank_k: Sequence[int], rank_v: Sequence[int]) -> int:
+    return HEAD_DIM * int(np.sum(rank_k) + np.sum(rank_v))
+
+
+def bases_offsets(rank_k: Sequence[int], rank_v: Sequence[int]):
+    """Element offsets of U_K(h) and U_V(h) in the bases buffer."""
+    uk, uv, off = [], [], 0
+    for rk, rv in zip(rank_k, rank_v):
+        uk.append(off)
+        uv.append(off + HEAD_DIM * int(rk))
+        off += HEAD_DIM * (int(rk) + int(rv))
+    return np.array(uk), np.array(uv)
+
+
+def codes_elems(ranks: Sequence[int], batch: int, cap: int) -> int:
+    return int(batch) * int(cap) * int(np.sum(ranks))
+
+
+def code_offsets(ranks: Sequence[int], batch: int, cap: int) -> np.ndarray:
+    """Element offset of head h's [batch][cap][r] region in a codes buffer."""
+    r = np.asarray(ranks, np.int64)
+    return np.concatenate([[0], np.cumsum(int(batch) * int(cap) * r)[:-1]]).astype(np.int64)
+
+
+def block_positions(r: int, which: str) -> np.ndarray:
+    """In-block element position of (slot t in 0..31, column c in 0..r-1)."""
+    t = np.arange(BLOCK)[:, None]
+    c = np.arange(r)[None, :]
+    if which == "k":
+        return ((t // 16) * (r // 8) + c // 8) * 128 + (t % 16) * 8 + c % 8
+    if which == "v":
+        return ((t % 16) // 4 * r + c) * 8 + 4 * (t // 16) + t % 4
+    raise ValueError(which)
+
+
+def slot_positions(n: int, r: int, which: str) -> np.ndarray:
+    """Element position of (slot j in 0..n-1, column c) inside one (row, head) region."""
+    j = np.arange(n)
+    return (j // BLOCK)[:, None] * (BLOCK * r) + block_positions(r, which)[j % BLOCK]
+
+
+def pack_codes(codes: np.ndarray, cap: int, which: str) -> np.ndarray:
+    """(n, r) logical codes of slots 0..n-1 -> flat (cap * r) blocked region."""
+    n, r = codes.shape
+    assert n <= cap and cap % BLOCK == 0
+    out = np.zeros(cap * r, dtype=codes.dtype)
+    out[slot_positions(n, r, which)] = codes
+    return out
+
+
+def unpack_codes(region: np.ndarray, n: int, r: int, which: str) -> np.ndarray:
+    """Flat blocked region -> (n, r) logical codes of slots 0..n-1."""
+    return np.asarray(region)[slot_positions(n, r, which)]
+
+
+def anchor_slot(p: int, window: int) -> int:
+    return 0 if p == 0 else 1 + (p - 1) % window

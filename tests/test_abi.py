@@ -1,0 +1,152 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/lrkv.h declares, and rejects bad arguments on the host before any HIP
+call (no compute is launched here)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from rank_kv_cache_lrkv_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lrkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lrkv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_entry_points():
+    assert declared_functions() == sorted(B.exported_names())
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {B.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_status_strings_and_version():
+    lib = B.lib()
+    assert lib.lrkv_status_string(0) == b"ok"
+    for s in range(1, 9):
+        assert lib.lrkv_status_string(s) not in (b"ok", b"unknown status")
+    assert lib.lrkv_version() >= 100
+
+
+FAKE = 1 << 20   # a 16-byte-aligned non-null address; validation fails before any use
+
+
+def layer(**kw):
+    d = dict(dtype=1, batch=2, n_q_heads=8, n_kv_heads=2, window=4, cap=64,
+             rank_k=[64, 32], rank_v=[32, 16])
+    d.update(kw)
+    rk = (ctypes.c_int32 * len(d["rank_k"]))(*d["rank_k"])
+    rv = (ctypes.c_int32 * len(d["rank_v"]))(*d["rank_v"])
+    s = B.lrkv_layer(d["dtype"], d["batch"], d["n_q_heads"], d["n_kv_heads"], d["window"], d["cap"],
+                     ctypes.cast(rk, ctypes.POINTER(ctypes.c_int32)),
+                     ctypes.cast(rv, ctypes.POINTER(ctypes.c_int32)),
+                     d.get("bases", FAKE), d.get("codes_k", FAKE), d.get("codes_v", FAKE),
+                     d.get("anchor_k", FAKE), d.get("anchor_v", FAKE))
+    s._keep = (rk, rv)
+    return s
+
+
+def decode(L, n_ctx=50, q=FAKE, out=FAKE, scale=0.088, S=2, ws=FAKE, ws_bytes=1 << 30):
+    return B.lib().lrkv_decode_attn(ctypes.byref(L), n_ctx, None, q, out, scale, S, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), 4),
+    (dict(batch=0), 2),
+    (dict(n_q_heads=7), 2),
+    (dict(n_q_heads=2 * 17, n_kv_heads=2), 2),
+    (dict(window=-1), 2),
+    (dict(cap=40), 2),
+    (dict(rank_k=[64, 24]), 3),
+    (dict(rank_v=[32, 0]), 3),
+    (dict(rank_k=[144, 32]), 3),
+    (dict(bases=None), 1),
+    (dict(codes_v=None), 1),
+    (dict(anchor_k=FAKE + 8), 5),
+])
+def test_layer_validation(kw, status):
+    assert decode(layer(**kw)) == status
+
+
+def test_decode_argument_validation():
+    L = layer()
+    assert decode(L, n_ctx=0) == 2
+    assert decode(L, n_ctx=4 + 64 + 2) == 6           # needs 65 code slots, cap is 64
+    assert decode(L, q=None) == 1
+    assert decode(L, out=None) == 1
+    assert decode(L, out=FAKE + 4) == 5
+    assert decode(L, S=-1) == 2
+    assert decode(L, S=B.lib().lrkv_decode_workspace_size(ctypes.byref(L), 1) and 1025) == 2
+    assert decode(L, scale=0.0) == 2
+    assert decode(L, scale=float("nan")) == 2
+    assert decode(L, ws=None) == 7
+    need = B.lib().lrkv_decode_workspace_size(ctypes.byref(L), 2)
+    assert decode(L, ws_bytes=need - 1) == 7
+
+
+def test_workspace_size_formula():
+    L = layer()
+    lib = B.lib()
+    # records: 4 + max r_v (32) floats per (row, query head, split) plus 132 per (row, query head)
+    assert lib.lrkv_decode_workspace_size(ctypes.byref(L), 3) == (2 * 8 * 3 * 36 + 2 * 8 * 132) * 4
+    assert lib.lrkv_decode_workspace_size(ctypes.byref(L), 0) == 0
+    assert lib.lrkv_decode_workspace_size(ctypes.byref(layer(batch=0)), 3) == 0
+
+
+def test_auto_splits():
+    lib = B.lib()
+    # Llama-3.1-8B-shaped layer at 32K: 32 (row, KV head) units -> 32 splits
+    L = layer(batch=4, n_q_heads=32, n_kv_heads=8, window=128, cap=32768,
+              rank_k=[64] * 8, rank_v=[32] * 8)
+    assert lib.lrkv_decode_auto_splits(ctypes.byref(L), 32768) == 32
+    assert lib.lrkv_decode_auto_splits(ctypes.byref(L), 100) == 1
+    assert lib.lrkv_decode_auto_splits(ctypes.byref(L), 0) == 0
+
+
+def test_compress_validation():
+    lib = B.lib()
+    L = layer()
+    f = lambda **k: lib.lrkv_compress(ctypes.byref(L), k.get("which", 0), k.get("x", FAKE),
+                                      k.get("sb", 1024), k.get("sh", 512), k.get("st", 128),
+                                      k.get("n", 10), k.get("slot0", 0), None)
+    assert f(which=2) == 2
+    assert f(n=-1) == 2
+    assert f(slot0=-1) == 2
+    assert f(n=60, slot0=5) == 6
+    assert f(n=0, x=None) == 0           # empty range is a no-op
+    assert f(x=None) == 1
+    assert f(st=100) == 5                 # 200-byte row stride is not 16-byte aligned
+    assert f(sh=-512) == 2
+    assert f(x=FAKE + 2) == 5
+
+
+def test_store_and_append_validation():
+    lib = B.lib()
+    L = layer()
+    sa = lambda pos0, n, k=FAKE: lib.lrkv_store_anchors(ctypes.byref(L), k, FAKE, 1024, 512, 128, pos0, n, None)
+    assert sa(0, 6) == 2          # 1 + window = 5 slots
+    assert sa(3, 5) == 2          # 4 ring slots
+    assert sa(-1, 1) == 2
+    assert sa(0, 0) == 0
+    assert sa(0, 2, k=None) == 1
+    ap = lambda pos, k=FAKE: lib.lrkv_append(ctypes.byref(L), k, FAKE, pos, None)
+    assert ap(-1) == 2
+    assert ap(4 + 64 + 1) == 6    # would compress into slot 64 of a 64-slot region
+    assert ap(5, k=None) == 1
+    assert ap(5, k=FAKE + 2) == 5
+    L0 = layer(window=0)
+    assert lib.lrkv_store_anchors(ctypes.byref(L0), FAKE, FAKE, 1024, 512, 128, 1, 1, None) == 2
+    assert lib.lrkv_append(ctypes.byref(L0), FAKE, FAKE, 65, None) == 6

@@ -1,0 +1,184 @@
+"""End to end on the GPU: prefill compression, anchor stores, decode steps with
+cache maintenance, against the oracle (which makes its own codes from the same
+keys and values).  Includes the five workloads at their full sizes, checked on
+sampled (batch row, KV head) units the oracle computes one by one."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from cases import D, announce, check_decode, dev, host_case, gpu_layer, to_storage
+from rank_kv_cache_lrkv_amd import binding as B, layout
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def full_rows(w, layer, which):
+    """[batch][Hkv][n_total][128] float32 storage values, generated unit by unit."""
+    a = np.empty((w.batch, w.n_kv_heads, w.n_total, D), np.float32)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            a[b, h] = synth.unit_kv(w, layer, h, b, which)
+    return a
+
+
+def bases_flat(w, layer):
+    rk, rv = synth.ranks(w, layer)
+    parts = []
+    for h in range(w.n_kv_heads):
+        parts += [synth.basis(w, layer, h, "k", int(rk[h])).ravel(),
+                  synth.basis(w, layer, h, "v", int(rv[h])).ravel()]
+    return rk, rv, np.concatenate(parts)
+
+
+def prefill(w, layer, n, cap=None):
+    """Allocate a layer, compress tokens 1..n-W-1 and store the anchors of a
+    context of n tokens, all on the GPU.  Returns (Layer, K, V) (K, V on GPU)."""
+    rk, rv, bases = bases_flat(w, layer)
+    cmax = max(0, n - 1 - w.window)
+    cap = layout.round_cap(cmax + w.n_steps) if cap is None else cap
+    L = B.Layer.allocate(dtype=B.LRKV_F32 if w.dtype == "f32" else B.LRKV_BF16, batch=w.batch,
+                         n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, window=w.window, cap=cap,
+                         rank_k=rk, rank_v=rv, bases=dev(bases, w.dtype))
+    K = dev(full_rows(w, layer, "k"), w.dtype)
+    V = dev(full_rows(w, layer, "v"), w.dtype)
+    B.lrkv_compress(L, 0, K[:, :, 1:], cmax, 0)
+    B.lrkv_compress(L, 1, V[:, :, 1:], cmax, 0)
+    B.lrkv_store_anchors(L, K[:, :, 0:1], V[:, :, 0:1], 0, 1)
+    lo = max(1, n - w.window)
+    B.lrkv_store_anchors(L, K[:, :, lo:n], V[:, :, lo:n], lo, n - lo)
+    return L, K, V
+
+
+def oracle_units(w, layer, n, step, units, q):
+    """Oracle output for the listed (b, h) units at context n (float64)."""
+    rk, rv = synth.ranks(w, layer)
+    g = w.group
+    out = np.full((w.batch, w.n_q_heads, D), np.nan)
+    cpos, apos = oracle.code_positions(n, w.window), oracle.anchor_positions(n, w.window)
+    for b, h in units:
+        k = synth.unit_kv(w, layer, h, b, "k").astype(np.float64)
+        v = synth.unit_kv(w, layer, h, b, "v").astype(np.float64)
+        uk = synth.basis(w, layer, h, "k", int(rk[h])).astype(np.float64)
+        uv = synth.basis(w, layer, h, "v", int(rv[h])).astype(np.float64)
+        ck = to_storage(oracle.oracle_compress(k[cpos], uk), w.dtype)
+        cv = to_storage(oracle.oracle_compress(v[cpos], uv), w.dtype)
+        rows = slice(h * g, (h + 1) * g)
+        out[b, rows] = oracle.oracle_decode_unit(q[b, rows], uk, uv, ck, cv, k[apos], v[apos],
+                                                 oracle.default_scale())
+    return out
+
+
+def decode(L, w, n, q_np, S):
+    q = dev(q_np, w.dtype)
+    out = torch.empty((w.batch, w.n_q_heads, D), dtype=torch.float32, device="cuda")
+    ws = B.workspace(L, S)
+    B.lrkv_decode_attn(L, n, q, out, oracle.default_scale(), S, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def queries(w, layer, step):
+    return np.stack([synth.queries(w, layer, step, b) for b in range(w.batch)]).astype(np.float64)
+
+
+def sample_units(w, k=3):
+    us = {(0, 0), (w.batch - 1, w.n_kv_heads - 1), (w.batch // 2, w.n_kv_heads // 2)}
+    return sorted(us)[:k]
+
+
+REDUCED = [
+    ("tiny_f32", W["tiny_f32"]),
+    ("qwen3_n1500", W["qwen3_1p7b_4k"].scaled(batch=2, n_ctx=1500)),
+    ("hc_n600", W["llama31_8b_hc_8k"].scaled(batch=2, n_ctx=600)),
+]
+
+
+@pytest.mark.parametrize("label,w", REDUCED, ids=[r[0] for r in REDUCED])
+def test_prefill_then_decode(label, w):
+    announce(f"e2e prefill+decode {label}")
+    L, _, _ = prefill(w, 0, w.n_ctx)
+    q = queries(w, 0, 0)
+    S = B.lrkv_decode_auto_splits(L, w.n_ctx)
+    got = decode(L, w, w.n_ctx, q, S)
+    units = [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
+    check_decode(got, oracle_units(w, 0, w.n_ctx, 0, units, q), w.dtype, f"e2e_{label}")
+
+
+@pytest.mark.parametrize("window", [0, 1, 16])
+def test_decode_steps_with_append(window):
+    """The decode loop: append the new token (compressing the one that leaves the
+    window), then decode; every step against the oracle from scratch."""
+    w = W["llama31_8b_32layer"].scaled(batch=2, n_ctx=60, n_steps=40, window=window)
+    announce(f"e2e append steps W={window}")
+    L, K, V = prefill(w, 3, w.n_ctx)
+    units = [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
+    for t in range(1, w.n_steps + 1):
+        pos = w.n_ctx + t - 1
+        B.lrkv_append(L, K[:, :, pos].contiguous(), V[:, :, pos].contiguous(), pos)
+        n = pos + 1
+        q = queries(w, 3, t)
+        got = decode(L, w, n, q, B.lrkv_decode_auto_splits(L, n))
+        if t in (1, 2, w.window + 1, w.window + 2, w.n_steps) or t % 9 == 0:
+            check_decode(got, oracle_units(w, 3, n, t, units, q), "bf16", f"append_W{window}_t{t}")
+
+
+def test_append_from_empty_cache():
+    """Build the cache token by token from position 0 with append only."""
+    w = W["qwen3_1p7b_4k"].scaled(batch=1, n_q_heads=4, n_kv_heads=2, window=4, n_ctx=0, n_steps=40)
+    rk, rv, bases = bases_flat(w, 0)
+    L = B.Layer.allocate(dtype=B.LRKV_BF16, batch=1, n_q_heads=4, n_kv_heads=2, window=4, cap=64,
+                         rank_k=rk, rank_v=rv, bases=dev(bases, "bf16"))
+    K = dev(full_rows(w, 0, "k"), "bf16")
+    V = dev(full_rows(w, 0, "v"), "bf16")
+    announce("e2e append from empty")
+    units = [(0, 0), (0, 1)]
+    for pos in range(40):
+        B.lrkv_append(L, K[:, :, pos].contiguous(), V[:, :, pos].contiguous(), pos)
+        n = pos + 1
+        if n in (1, 2, 5, 6, 7, 40):
+            q = queries(w, 0, n)
+            check_decode(decode(L, w, n, q, 2), oracle_units(w, 0, n, n, units, q), "bf16", f"from_empty_n{n}")
+
+
+# ---------------------------------------------------------------------------
+# full sizes, sampled units
+# ---------------------------------------------------------------------------
+
+FULL = [("qwen3_1p7b_4k", 0), ("llama31_8b_32k", 32), ("llama31_8b_hc_8k", 0), ("tiny_f32", 0)]
+
+
+@pytest.mark.parametrize("name,S", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled(name, S):
+    w = W[name]
+    announce(f"full size {name}: batch {w.batch} n {w.n_ctx}")
+    L, _, _ = prefill(w, 0, w.n_ctx)
+    S = S or B.lrkv_decode_auto_splits(L, w.n_ctx)
+    q = queries(w, 0, 0)
+    got = decode(L, w, w.n_ctx, q, S)
+    assert np.all(np.isfinite(got))
+    check_decode(got, oracle_units(w, 0, w.n_ctx, 0, sample_units(w), q), w.dtype, f"full_{name}")
+
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_full_size_32layer_decode_steps(layer):
+    """32-layer workload at full context: prefill 32768 tokens with the layer's
+    mixed ranks, then 16 decode steps with cache maintenance (sampled units)."""
+    w = W["llama31_8b_32layer"]
+    rk, rv = synth.ranks(w, layer)
+    announce(f"full 32-layer workload, layer {layer}, ranks {rk.tolist()} / {rv.tolist()}")
+    L, K, V = prefill(w, layer, w.n_ctx)
+    units = sample_units(w, 2)
+    for t in range(1, w.n_steps + 1):
+        pos = w.n_ctx + t - 1
+        B.lrkv_append(L, K[:, :, pos].contiguous(), V[:, :, pos].contiguous(), pos)
+        n = pos + 1
+        q = queries(w, layer, t)
+        got = decode(L, w, n, q, B.lrkv_decode_auto_splits(L, n))
+        assert np.all(np.isfinite(got))
+        if t in (1, 8, 16):
+            check_decode(got, oracle_units(w, layer, n, t, units, q), "bf16", f"l{layer}_step{t}")
