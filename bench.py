@@ -71,9 +71,8 @@ def build_cache(w, B, dev):
     from rank_kv_cache_lrkv_amd import layout
 
     rk, rv = synth.ranks(w, 0)
-    bases = np.concatenate([np.concatenate([synth.basis(w, 0, h, "k", int(rk[h])).ravel(),
-                                            synth.basis(w, 0, h, "v", int(rv[h])).ravel()])
-                            for h in range(w.n_kv_heads)])
+    bases = layout.pack_bases([synth.basis(w, 0, h, "k", int(rk[h])) for h in range(w.n_kv_heads)],
+                              [synth.basis(w, 0, h, "v", int(rv[h])) for h in range(w.n_kv_heads)])
     n = w.n_ctx
     c = max(0, n - 1 - w.window)
     L = B.Layer.allocate(dtype=B.LRKV_BF16 if w.dtype == "bf16" else B.LRKV_F32, batch=w.batch,

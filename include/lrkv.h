@@ -66,10 +66,11 @@ typedef enum lrkv_dtype {
  *
  * rank_k[h], rank_v[h] (host arrays of n_kv_heads): multiples of 16 in [16, 128].
  *
- * bases (device): the heads in order; head h holds U_K(h) as [128][rank_k[h]] and
- *   right after it U_V(h) as [128][rank_v[h]], row-major, so U_K(h) starts at
- *   element 128 * sum_{h' < h} (rank_k[h'] + rank_v[h']).  Codes are x U (x a
- *   128-row vector), so the columns of U are the basis directions.
+ * bases (device): the heads in order; head h holds the rank_k[h] key basis
+ *   directions (the columns of U_K(h)) as rows of 128 contiguous elements, i.e.
+ *   U_K(h)^T as [rank_k[h]][128], and right after it U_V(h)^T as [rank_v[h]][128];
+ *   U_K(h) starts at element 128 * sum_{h' < h} (rank_k[h'] + rank_v[h']).  A code
+ *   is x U: column c of a code is the dot product of x with basis row c.
  *
  * codes_k, codes_v (device): the heads in order; head h owns `batch * cap * r`
  *   elements (r = rank_k[h] resp. rank_v[h]), starting at element

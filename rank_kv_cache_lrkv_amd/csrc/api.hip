@@ -61,7 +61,8 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   return LRKV_OK;
 }
 
-int32_t rec_floats(const LayerArgs &A) { return 4 + ((A.rv_max + 3) / 4) * 4; }
+int32_t rvp_floats(const LayerArgs &A) { return ((A.rv_max + 3) / 4) * 4; }
+int32_t rec_floats(const LayerArgs &A) { return 4 + rvp_floats(A) + kD; }
 
 int32_t auto_splits(const LayerArgs &A, int32_t n_ctx) {
   const int64_t c = n_ctx - 1 - A.window;
@@ -79,7 +80,7 @@ int32_t auto_splits(const LayerArgs &A, int32_t n_ctx) {
 
 size_t ws_bytes(const LayerArgs &A, int32_t S) {
   const size_t rows = size_t(A.batch) * A.n_q;
-  return (rows * S * rec_floats(A) + rows * kAnchorRec) * sizeof(float);
+  return rows * S * rec_floats(A) * sizeof(float);
 }
 
 lrkv_status check_strides(const lrkv_layer *L, const void *x, int64_t sb, int64_t sh, int64_t st) {
@@ -109,11 +110,11 @@ lrkv_status make_decode(const lrkv_layer *L, const LayerArgs &A, int32_t n_ctx,
   D->n_ctx = n_ctx;
   D->n_splits = S;
   D->rec = rec_floats(A);
+  D->oa = 4 + rvp_floats(A);
   D->scale_log2 = sm_scale * kLog2e;
   D->ctx_lens = ctx_lens;
   D->q = q;
-  D->ws_codes = static_cast<float *>(ws);
-  D->ws_anchor = static_cast<float *>(ws) + size_t(A.batch) * A.n_q * S * D->rec;
+  D->ws = static_cast<float *>(ws);
   return LRKV_OK;
 }
 

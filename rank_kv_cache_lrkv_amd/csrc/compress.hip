@@ -15,7 +15,7 @@ namespace lrkv {
 // Generic projection: float32 storage (and any storage type as a plain path).
 // One workgroup per (64-token tile, batch row, KV head).  The 64x128 input tile
 // is staged in LDS as float32; each thread produces code columns with a float32
-// dot product over the 128 features; the basis is read through the cache.
+// dot product over the 128 features against a basis row (read through the cache).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void k_compress_generic(LayerArgs L, int which, const T *x,
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void k_compress_generic(LayerArgs L, int which
   for (int o = threadIdx.x; o < nt * r; o += blockDim.x) {
     const int t = o / r, c = o % r;
     float acc = 0.f;
-    for (int k = 0; k < kD; ++k) acc = fmaf(sx[t][k], to_f32(U[k * r + c]), acc);
+    for (int k = 0; k < kD; ++k) acc = fmaf(sx[t][k], to_f32(U[c * kD + k]), acc);
     const int j = slot0 + t0 + t;
     codes[which ? vslot(j, c, r) : kslot(j, c, r)] = from_f32<T>(acc);
   }
@@ -103,12 +103,12 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
     T *cv = static_cast<T *>(L.codes_v) + hd.cv + int64_t(b) * L.cap * hd.rv;
     if (tid < hd.rk) {
       float acc = 0.f;
-      for (int k = 0; k < kD; ++k) acc = fmaf(rk_row[k], to_f32(Uk[k * hd.rk + tid]), acc);
+      for (int k = 0; k < kD; ++k) acc = fmaf(rk_row[k], to_f32(Uk[tid * kD + k]), acc);
       ck[kslot(code_slot, tid, hd.rk)] = from_f32<T>(acc);
     }
     if (tid < hd.rv) {
       float acc = 0.f;
-      for (int k = 0; k < kD; ++k) acc = fmaf(rv_row[k], to_f32(Uv[k * hd.rv + tid]), acc);
+      for (int k = 0; k < kD; ++k) acc = fmaf(rv_row[k], to_f32(Uv[tid * kD + k]), acc);
       cv[vslot(code_slot, tid, hd.rv)] = from_f32<T>(acc);
     }
   }

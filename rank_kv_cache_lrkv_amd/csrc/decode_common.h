@@ -1,0 +1,110 @@
+// Device pieces shared by the decode kernels: wave reductions, the split
+// records and the chunked float32 online-softmax pass.
+#pragma once
+
+#include "lrkv_internal.h"
+
+namespace lrkv {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// record of query head qi = b * n_q + i for split s
+__device__ __forceinline__ float *split_record(const DecodeArgs &d, int64_t qi, int split) {
+  return d.ws + (qi * d.n_splits + split) * d.rec;
+}
+
+// anchor rows [lo, hi) of split s out of a anchors: consecutive runs of at
+// least 16 rows on the first splits, so most splits carry no anchors at all
+constexpr int kMinAnchorRows = 16;
+__device__ __forceinline__ int anchor_rows_per_split(int a, int S) {
+  const int even = (a + S - 1) / S;
+  return even > kMinAnchorRows ? even : kMinAnchorRows;
+}
+__device__ __forceinline__ void anchor_share(int a, int split, int S, int &lo, int &hi) {
+  const int per = anchor_rows_per_split(a, S);
+  lo = min(split * per, a);
+  hi = min(lo + per, a);
+}
+
+// code blocks [lo, hi) of split s out of nblk (contiguous ranges)
+__device__ __forceinline__ void block_share(int nblk, int split, int S, int &lo, int &hi) {
+  lo = int((int64_t(split) * nblk) / S);
+  hi = int((int64_t(split + 1) * nblk) / S);
+}
+
+// LDS of the chunked (64-row) online-softmax pass
+struct ChunkSmem {
+  float sq[LRKV_MAX_GROUP][kD];   // query side (scaled into log2 units)
+  float sp[LRKV_MAX_GROUP][64];   // scores, then weights, of the current chunk
+  float m[LRKV_MAX_GROUP], l[LRKV_MAX_GROUP], alpha[LRKV_MAX_GROUP];
+};
+
+// One online-softmax pass over rows [lo, hi) for the g query heads of a group,
+// 256 threads: chunks of 64 rows, scores for every head into LDS, then one
+// softmax update per head (a wave per head), then the value sums, each thread
+// owning up to eight (head, column) accumulators.  kval(t, c) and vval(t, c)
+// read row t's key (dk columns) and value (dv columns) as float.  The query
+// side must already be in sm.sq, and sm.m / sm.l hold the running state (set
+// them to -inf / 0 before a first pass).  acc is zeroed on entry.
+template <typename KF, typename VF>
+__device__ __forceinline__ void chunked_softmax_pass(ChunkSmem &sm, int g, int lo, int hi, int dk,
+                                                     int dv, KF kval, VF vval, float (&acc)[8]) {
+  constexpr int CH = 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  __syncthreads();
+  for (int base = lo; base < hi; base += CH) {
+    const int nv = min(CH, hi - base);
+    for (int p = tid; p < g * CH; p += blockDim.x) {
+      const int hh = p / CH, j = p % CH;
+      float s = kNegInf;
+      if (j < nv) {
+        float a = 0.f;
+        for (int c = 0; c < dk; ++c) a = fmaf(sm.sq[hh][c], kval(base + j, c), a);
+        s = a;
+      }
+      sm.sp[hh][j] = s;
+    }
+    __syncthreads();
+    for (int hh = wave; hh < g; hh += 4) {
+      const float s = sm.sp[hh][lane];
+      const float mo = sm.m[hh];
+      const float mn = fmaxf(mo, wave_max(s));  // finite: the chunk has nv >= 1 rows
+      const float p = exp2f(s - mn);             // s = -inf gives 0
+      sm.sp[hh][lane] = p;
+      const float ps = wave_sum(p);
+      if (lane == 0) {
+        const float al = exp2f(mo - mn);  // mo = -inf gives 0
+        sm.alpha[hh] = al;
+        sm.l[hh] = sm.l[hh] * al + ps;
+        sm.m[hh] = mn;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int o = threadIdx.x + e * 256;
+      if (o < g * dv) {
+        const int hh = o / dv, c = o % dv;
+        float a = acc[e] * sm.alpha[hh];
+        for (int j = 0; j < nv; ++j) a = fmaf(sm.sp[hh][j], vval(base + j, c), a);
+        acc[e] = a;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace lrkv

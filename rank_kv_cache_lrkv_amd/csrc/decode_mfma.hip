@@ -1,0 +1,533 @@
+// Stage 1 of decode attention for bfloat16 caches on the gfx950 matrix cores.
+//
+// One workgroup of four waves per (split, batch row, KV head).  For one 32-slot
+// code block a wave computes
+//
+//   scores   S[t][h] = C_K[t] . q~_h   two 16-token tiles, K = 32 rank columns
+//            per MFMA; q~ is split into a bf16 hi + lo pair (two MFMAs) so the
+//            projected query keeps ~16 significant bits
+//   softmax  block max per head across the wave, running max and denominator,
+//            exp2 of scores already in log2 units
+//   values   o~[h][c] += sum_t p[h][t] C_V[t][c]   16 columns per MFMA, K = the
+//            32 tokens, the weights split into bf16 hi + lo (two MFMAs)
+//
+// The code layout (lrkv.h) puts the 16 bytes each lane feeds a matrix core next
+// to each other, so a key block is read as one contiguous 1 KiB per 32 rank
+// columns and a value block as four contiguous 256-byte runs per 16 columns.
+// The score result lands, with no lane exchange, where the value MFMA takes its
+// weights: lane (q, t) holds head t's weights of tokens 16 h + 4 q + v, which
+// the value layout files as k-slot 4 h + v of lane group q.
+//
+// Memory schedule.  Split s, wave w streams blocks 4 s + w + k 4S, so all the
+// waves of a (row, head) sweep its codes together as one moving front (DRAM rows
+// stay open), and every wave keeps the next block in flight while it computes
+// the current one (double buffering keeps the kernel at four waves per SIMD, so
+// all workgroups of a 32-split, 32-unit decode are resident at once).  Loads are raw buffer loads: a per-lane constant offset plus a scalar
+// block offset.  The first splits also take the anchor rows (token 0 and the
+// recent window, full rank) in runs of at least 16; they are staged in LDS in the
+// prologue together with the group's queries and the query projection
+// q~ = U_K^T q, and wave 0 folds them in before its code blocks while the other
+// waves already stream.
+
+#include "decode_common.h"
+
+namespace lrkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// word 3 of a raw buffer resource on gfx9-family parts (32-bit data format)
+constexpr int kBufferWord3 = 0x00020000;
+
+// 2^x with the hardware exp2 (v_exp_f32): results below 2^-126 flush to zero,
+// 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// x = hi + lo: hi keeps the top 16 bits (truncation), lo is the remainder
+// rounded to nearest bf16; hi + lo matches x to about 2^-16 relative.
+__device__ __forceinline__ float bf16_trunc(float x) {
+  return __uint_as_float(__float_as_uint(x) & 0xffff0000u);
+}
+__device__ __forceinline__ uint32_t pack_hi(float a, float b) {
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+__device__ __forceinline__ uint32_t pack_rne(float a, float b) {
+  return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)a)) |
+         (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)b)) << 16);
+}
+
+// LDS traffic of one wave is processed in order: a wave-scope fence orders it
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses complete
+// (lgkmcnt 0; vmcnt and expcnt left at their maxima, i.e. not waited for), then
+// all waves meet.  Global loads in flight stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+constexpr int kAnchorChunk = kMinAnchorRows;  // anchor rows staged in LDS at a time
+
+template <int RKMAX, int RVMAX>
+struct MfmaSmem {
+  union {
+    float qt[LRKV_MAX_GROUP][RKMAX];  // prologue: projected queries (log2 units)
+    float oa[LRKV_MAX_GROUP][kD];     // epilogue: anchor value sums
+  } u;
+  u32x4 bq[(RKMAX + 31) / 32][2][64];       // score B operands of each lane (hi, lo)
+  uint32_t ak[kAnchorChunk][kD / 2];        // anchor rows (bf16 pairs)
+  uint32_t av[kAnchorChunk][kD / 2];
+  uint32_t sq[LRKV_MAX_GROUP][kD / 2];      // the group's queries (bf16 pairs), zero rows past G
+  float m[5][LRKV_MAX_GROUP];               // per wave; [4] = the anchors
+  float l[5][LRKV_MAX_GROUP];
+  float o[4][LRKV_MAX_GROUP][RVMAX];        // per-wave rank-space sums
+  float pa[LRKV_MAX_GROUP][kAnchorChunk];   // anchor weights of the current chunk
+  float alpha_a[LRKV_MAX_GROUP];
+};
+
+template <int NKC, int NVC>
+struct BlockRegs {
+  u32x4 k[2][NKC];
+  u32x4 v[NVC];
+};
+
+// EXACT: every head of the layer has rank_k == RKMAX and rank_v == RVMAX, so all
+// rank tests fold at compile time; otherwise ranks are read per head (<= the max).
+template <int RKMAX, int RVMAX, bool EXACT>
+__global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d) {
+  constexpr int NKC = (RKMAX + 31) / 32;  // score MFMAs per 16-token tile (K = 32 each)
+  constexpr int NVC = RVMAX / 16;         // value MFMAs per block (16 columns each)
+  __shared__ MfmaSmem<RKMAX, RVMAX> sm;
+
+  const int S = d.n_splits;
+  const int split = blockIdx.x;
+  const int unit = blockIdx.y;
+  const int b = unit / L.n_kv, h = unit % L.n_kv;
+  const int G = L.group;
+  const int W = L.window;
+  const HeadInfo hd = L.heads[h];
+  const int rk = EXACT ? RKMAX : hd.rk, rv = EXACT ? RVMAX : hd.rv;
+  const int nkg = rk >> 3;   // 8-column groups of a key code
+  const int nvt = rv >> 4;   // 16-column tiles of a value code
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q4 = lane >> 4, t16 = lane & 15;
+  const int n = row_ctx(d, b);
+  const int c = max(0, n - 1 - W);
+  const int nblk = (c + kBlock - 1) / kBlock;
+  int alo, ahi;
+  anchor_share(min(n, 1 + W), split, S, alo, ahi);
+  const int na = ahi - alo;
+  const int64_t q0 = int64_t(b) * L.n_q + h * G;
+  const int first = 4 * split + wave, step = 4 * S;
+
+  if (4 * split >= nblk && na == 0) {  // nothing for this split
+    for (int i = tid; i < G; i += blockDim.x) {
+      float *rec = split_record(d, q0 + i, split);
+      rec[0] = kNegInf;
+      rec[1] = rec[2] = rec[3] = 0.f;
+    }
+    for (int i = tid; i < G * rv; i += blockDim.x) split_record(d, q0 + i / rv, split)[4 + i % rv] = 0.f;
+    return;
+  }
+
+  // this (row, head)'s key and value code regions as buffer resources
+  const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t *>(static_cast<const bf16_t *>(L.codes_k) + hd.ck + int64_t(b) * L.cap * rk),
+      0, L.cap * rk * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t *>(static_cast<const bf16_t *>(L.codes_v) + hd.cv + int64_t(b) * L.cap * rv),
+      0, L.cap * rv * 2, kBufferWord3);
+  const int kblk_bytes = kBlock * rk * 2, vblk_bytes = kBlock * rv * 2;
+  int koff[2][NKC];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const int kg = min(4 * kc + q4, nkg - 1);  // absent groups re-read a present one, then zero
+      koff[h2][kc] = ((h2 * nkg + kg) * 16 + t16) * 16;
+    }
+  int voff[NVC];
+#pragma unroll
+  for (int ni = 0; ni < NVC; ++ni) voff[ni] = (q4 * rv + 16 * min(ni, nvt - 1) + t16) * 16;
+
+  auto load = [&](int blk, BlockRegs<NKC, NVC> &r) {
+    // the block offsets are wave-uniform: keep them in scalar registers
+    const int ks = __builtin_amdgcn_readfirstlane(blk * kblk_bytes);
+    const int vs = __builtin_amdgcn_readfirstlane(blk * vblk_bytes);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+        r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b128(kres, koff[h2][kc], ks, 0);
+#pragma unroll
+    for (int ni = 0; ni < NVC; ++ni) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b128(vres, voff[ni], vs, 0);
+  };
+
+  // ---- prologue.  Loads are issued in this order: the operands of q~ (q and
+  // this wave's share of the U_K^T rows), the queries and first anchor rows for
+  // LDS, and only then the wave's first code block.  Vector-memory loads
+  // complete in order, so waiting for the prologue operands never waits for the
+  // code blocks, and the barriers below wait for LDS traffic only.
+  const bf16_t *qb = static_cast<const bf16_t *>(d.q) + q0 * kD;
+  const bf16_t *ut = static_cast<const bf16_t *>(L.bases) + hd.u_k;
+  constexpr int NT = RKMAX / 16;
+  constexpr int NTW = (NT + 3) / 4;  // column tiles of q~ per wave
+  // every load below is unconditional, from a clamped in-bounds address; what is
+  // absent is zeroed afterwards (no divergent branches around the loads)
+  u32x4 aq[4];                       // A = q: lane (q4, t16) holds head t16, features 32 kc + 8 q4 ..
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc)
+    aq[kc] = *reinterpret_cast<const u32x4 *>(qb + min(t16, G - 1) * kD + 32 * kc + 8 * q4);
+  u32x4 bu[NTW][4];                  // B = rows of U_K^T
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) {
+    const int nt = min(wave + 4 * i, rk / 16 - 1);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+      bu[i][kc] = *reinterpret_cast<const u32x4 *>(ut + (16 * nt + t16) * kD + 32 * kc + 8 * q4);
+  }
+  const int r16 = tid >> 4, piece = tid & 15;  // 16 rows x 16 pieces of 16 bytes
+  u32x4 qq = *reinterpret_cast<const u32x4 *>(qb + min(r16, G - 1) * kD + piece * 8);
+  const int64_t arow = int64_t(unit) * (1 + W) + (na > 0 ? alo + min(r16, na - 1) : 0);
+  u32x4 kk = *reinterpret_cast<const u32x4 *>(static_cast<const bf16_t *>(L.anchor_k) + arow * kD + piece * 8);
+  u32x4 vv = *reinterpret_cast<const u32x4 *>(static_cast<const bf16_t *>(L.anchor_v) + arow * kD + piece * 8);
+  __builtin_amdgcn_sched_barrier(0);
+  // the wave's first block (clamped to the last block; with no blocks at all
+  // block 0 is read and never used, which the region bound makes harmless)
+  BlockRegs<NKC, NVC> r0, r1;
+  {
+    const int last = max(nblk - 1, 0);
+    load(min(first, last), r0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+  if (t16 >= G) {
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) aq[kc] = zero4;
+  }
+  if (r16 >= G) qq = zero4;
+  if (r16 >= min(na, kAnchorChunk)) kk = vv = zero4;
+  *reinterpret_cast<u32x4 *>(&sm.sq[r16][piece * 4]) = qq;
+  *reinterpret_cast<u32x4 *>(&sm.ak[r16][piece * 4]) = kk;
+  *reinterpret_cast<u32x4 *>(&sm.av[r16][piece * 4]) = vv;
+  // D[head][col] = sum_k q[head][k] U_K[k][col]; the waves share the column tiles
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) {
+    const int nt = wave + 4 * i;
+    if (nt < rk / 16) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) acc = mfma16x16x32(aq[kc], bu[i][kc], acc);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int head = 4 * q4 + v;
+        if (head < G) sm.u.qt[head][16 * nt + t16] = acc[v] * d.scale_log2;
+      }
+    }
+  }
+  lds_barrier();
+  // score B operands: lane (q4, t16) holds head t16's columns 8 (4 kc + q4) .. +7
+  // as bf16 hi and lo parts, zero for absent heads/columns
+  if (wave == 0) {
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const int kg = 4 * kc + q4;
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = (t16 < G && kg < nkg) ? sm.u.qt[t16][kg * 8 + i] : 0.f;
+      u32x4 hi, lo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[i] = pack_hi(x[2 * i], x[2 * i + 1]);
+        lo[i] = pack_rne(x[2 * i] - bf16_trunc(x[2 * i]), x[2 * i + 1] - bf16_trunc(x[2 * i + 1]));
+      }
+      sm.bq[kc][0][lane] = hi;
+      sm.bq[kc][1][lane] = lo;
+    }
+  }
+  lds_barrier();
+
+  // ---- the split's anchor rows (wave 0, before its code blocks, while the other
+  // waves already stream): scores on the matrix cores against q, 128-dim value
+  // sums on the vector ALUs (lane = features 2 lane, 2 lane + 1).  The results go
+  // to LDS slot 4 of the merge.
+  if (wave == 0) {
+    float mA = kNegInf, lA = 0.f;
+    float acc[LRKV_MAX_GROUP][2];
+#pragma unroll
+    for (int hh = 0; hh < LRKV_MAX_GROUP; ++hh) acc[hh][0] = acc[hh][1] = 0.f;
+    for (int r0 = 0; r0 < na; r0 += kAnchorChunk) {
+      const int nr = min(kAnchorChunk, na - r0);
+      if (r0 > 0) {  // rows past the first chunk: stage them now
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int idx = lane + 64 * i, r = idx >> 4, piece = idx & 15;
+          u32x4 kk = u32x4{0u, 0u, 0u, 0u}, vv = kk;
+          if (r < nr) {
+            const int64_t row = int64_t(unit) * (1 + W) + alo + r0 + r;
+            kk = *reinterpret_cast<const u32x4 *>(static_cast<const bf16_t *>(L.anchor_k) + row * kD + piece * 8);
+            vv = *reinterpret_cast<const u32x4 *>(static_cast<const bf16_t *>(L.anchor_v) + row * kD + piece * 8);
+          }
+          *reinterpret_cast<u32x4 *>(&sm.ak[r][piece * 4]) = kk;
+          *reinterpret_cast<u32x4 *>(&sm.av[r][piece * 4]) = vv;
+        }
+        wave_lds_fence();
+      }
+      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        s = mfma16x16x32(*reinterpret_cast<const u32x4 *>(&sm.ak[t16][16 * kc + 4 * q4]),
+                         *reinterpret_cast<const u32x4 *>(&sm.sq[t16][16 * kc + 4 * q4]), s);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s[v] = 4 * q4 + v < nr ? s[v] * d.scale_log2 : kNegInf;
+      float cm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+      const float mn = fmaxf(mA, cm);  // finite: nr >= 1
+      const float al = fast_exp2(mA - mn);
+      float p[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) p[v] = fast_exp2(s[v] - mn);
+      float ps = (p[0] + p[1]) + (p[2] + p[3]);
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      lA = lA * al + ps;
+      mA = mn;
+      if (t16 < G) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sm.pa[t16][4 * q4 + v] = p[v];
+        if (q4 == 0) sm.alpha_a[t16] = al;
+      }
+      wave_lds_fence();
+#pragma unroll
+      for (int hh = 0; hh < LRKV_MAX_GROUP; ++hh) {
+        if (hh < G) {
+          const float a = sm.alpha_a[hh];
+          acc[hh][0] *= a;
+          acc[hh][1] *= a;
+        }
+      }
+      for (int r = 0; r < nr; ++r) {
+        const uint32_t vv = sm.av[r][lane];
+        const float v0 = __uint_as_float(vv << 16), v1 = __uint_as_float(vv & 0xffff0000u);
+#pragma unroll
+        for (int hh = 0; hh < LRKV_MAX_GROUP; ++hh) {
+          if (hh < G) {
+            const float pw = sm.pa[hh][r];
+            acc[hh][0] = fmaf(pw, v0, acc[hh][0]);
+            acc[hh][1] = fmaf(pw, v1, acc[hh][1]);
+          }
+        }
+      }
+      wave_lds_fence();
+    }
+    if (q4 == 0 && t16 < G) {
+      sm.m[4][t16] = mA;
+      sm.l[4][t16] = lA;
+    }
+#pragma unroll
+    for (int hh = 0; hh < LRKV_MAX_GROUP; ++hh) {
+      if (hh < G) {
+        sm.u.oa[hh][2 * lane] = acc[hh][0];
+        sm.u.oa[hh][2 * lane + 1] = acc[hh][1];
+      }
+    }
+  }
+
+  // ---- the code blocks
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 o[NVC];
+#pragma unroll
+  for (int ni = 0; ni < NVC; ++ni) o[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto process = [&](int blk, BlockRegs<NKC, NVC> &r) {
+    f32x4 s[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) s[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      if (4 * kc < nkg) {
+        const u32x4 bh = sm.bq[kc][0][lane], bl = sm.bq[kc][1][lane];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          u32x4 a = r.k[h2][kc];
+          if (4 * kc + q4 >= nkg) a = u32x4{0u, 0u, 0u, 0u};
+          s[h2] = mfma16x16x32(a, bh, s[h2]);
+          s[h2] = mfma16x16x32(a, bl, s[h2]);
+        }
+      }
+    }
+    const int tok0 = blk * kBlock;
+    if (tok0 + kBlock > c) {  // the ragged last block: mask slots >= c
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (tok0 + 16 * h2 + 4 * q4 + v >= c) s[h2][v] = kNegInf;
+      uint32_t keep[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j0 = 2 * i, j1 = 2 * i + 1;
+        const bool v0 = tok0 + 16 * (j0 >> 2) + 4 * q4 + (j0 & 3) < c;
+        const bool v1 = tok0 + 16 * (j1 >> 2) + 4 * q4 + (j1 & 3) < c;
+        keep[i] = (v0 ? 0x0000ffffu : 0u) | (v1 ? 0xffff0000u : 0u);
+      }
+#pragma unroll
+      for (int ni = 0; ni < NVC; ++ni)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.v[ni][i] &= keep[i];
+    }
+    // online softmax of head t16 over its 8 scores in this lane, 32 per block
+    float bm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    const float mn = fmaxf(m_run, bm);  // finite: a block holds at least one slot < c
+    const float alpha = fast_exp2(m_run - mn);
+    // lanes of absent heads (t16 >= G) score 0 against zero queries: their weights
+    // stay finite and only feed accumulator rows that are never read
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = fast_exp2(s[j >> 2][j & 3] - mn);
+    l_run = l_run * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+    m_run = mn;
+    // rescale the sums: lane (q4, t16) holds heads 4 q4 + v
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float a = __shfl(alpha, 4 * q4 + v, 64);
+#pragma unroll
+      for (int ni = 0; ni < NVC; ++ni) o[ni][v] *= a;
+    }
+    // weights as the A operand (k-slot j = 4 h + v), hi and lo parts
+    u32x4 a_hi, a_lo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a_hi[i] = pack_hi(p[2 * i], p[2 * i + 1]);
+      a_lo[i] = pack_rne(p[2 * i] - bf16_trunc(p[2 * i]), p[2 * i + 1] - bf16_trunc(p[2 * i + 1]));
+    }
+#pragma unroll
+    for (int ni = 0; ni < NVC; ++ni) {
+      if (ni < nvt) {
+        o[ni] = mfma16x16x32(a_hi, r.v[ni], o[ni]);
+        o[ni] = mfma16x16x32(a_lo, r.v[ni], o[ni]);
+      }
+    }
+  };
+
+  // double-buffered sweep
+  int j = first;
+  if (j < nblk) {
+    while (true) {
+      load(j + step < nblk ? j + step : j, r1);
+      process(j, r0);
+      j += step;
+      if (j >= nblk) break;
+      load(j + step < nblk ? j + step : j, r0);
+      process(j, r1);
+      j += step;
+      if (j >= nblk) break;
+    }
+  }
+
+  // ---- per-wave state to LDS
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (q4 == 0 && t16 < G) {
+    sm.m[wave][t16] = m_run;
+    sm.l[wave][t16] = l_run;
+  }
+#pragma unroll
+  for (int ni = 0; ni < NVC; ++ni) {
+    if (ni < nvt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int head = 4 * q4 + v;
+        if (head < G) sm.o[wave][head][16 * ni + t16] = o[ni][v];
+      }
+    }
+  }
+
+  __syncthreads();
+
+  // ---- merge the four waves and the anchors into the split's records
+  auto weight = [&](int w, int hh, float M) {
+    const float mw = sm.m[w][hh];
+    return mw == kNegInf ? 0.f : fast_exp2(mw - M);
+  };
+  auto head_max = [&](int hh) {
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 5; ++w) M = fmaxf(M, sm.m[w][hh]);
+    return M;
+  };
+  for (int i = tid; i < G * rv; i += blockDim.x) {
+    const int hh = i / rv, cc = i - hh * rv;
+    const float M = head_max(hh);
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc = fmaf(weight(w, hh, M), sm.o[w][hh][cc], acc);
+    split_record(d, q0 + hh, split)[4 + cc] = acc;
+  }
+  if (na > 0) {  // anchor-free splits leave o_A unwritten; the combine skips it
+    for (int i = tid; i < G * kD; i += blockDim.x) {
+      const int hh = i / kD, cc = i - hh * kD;
+      split_record(d, q0 + hh, split)[d.oa + cc] = weight(4, hh, head_max(hh)) * sm.u.oa[hh][cc];
+    }
+  }
+  for (int hh = tid; hh < G; hh += blockDim.x) {
+    const float M = head_max(hh);
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < 5; ++w) l = fmaf(weight(w, hh, M), sm.l[w][hh], l);
+    float *rec = split_record(d, q0 + hh, split);
+    rec[0] = M;
+    rec[1] = l;
+    rec[2] = rec[3] = 0.f;
+  }
+}
+
+template <int RKMAX, int RVMAX>
+static hipError_t launch_rv(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
+  bool exact = true;
+  for (int h = 0; h < L.n_kv; ++h) exact = exact && L.heads[h].rk == RKMAX && L.heads[h].rv == RVMAX;
+  dim3 grid(d.n_splits, L.batch * L.n_kv);
+  if (exact)
+    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, true>), grid, dim3(256), 0, s, L, d);
+  else
+    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, false>), grid, dim3(256), 0, s, L, d);
+  return hipGetLastError();
+}
+
+template <int RKMAX>
+static hipError_t launch_rk(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
+  if (L.rv_max <= 16) return launch_rv<RKMAX, 16>(L, d, s);
+  if (L.rv_max <= 32) return launch_rv<RKMAX, 32>(L, d, s);
+  if (L.rv_max <= 64) return launch_rv<RKMAX, 64>(L, d, s);
+  return launch_rv<RKMAX, 128>(L, d, s);
+}
+
+hipError_t launch_partials_mfma(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
+  int rk_max = 0;
+  for (int h = 0; h < L.n_kv; ++h) rk_max = L.heads[h].rk > rk_max ? L.heads[h].rk : rk_max;
+  if (rk_max <= 32) return launch_rk<32>(L, d, s);
+  if (rk_max <= 64) return launch_rk<64>(L, d, s);
+  if (rk_max <= 96) return launch_rk<96>(L, d, s);
+  return launch_rk<128>(L, d, s);
+}
+
+}  // namespace lrkv

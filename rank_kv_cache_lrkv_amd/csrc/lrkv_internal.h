@@ -26,18 +26,23 @@ struct LayerArgs {
   HeadInfo heads[LRKV_MAX_KV_HEADS];
 };
 
+// Split s of a (batch row, KV head) covers a share of its code blocks and the
+// anchor rows [s a / S, (s + 1) a / S) of its a anchors; per query head it leaves
+// one record in the workspace:
+//   [m, l, 0, 0, o~[rvp], o_A[128]]
+// m: running max of the scores (log2 units, -inf if the split saw nothing),
+// l: sum of 2^(s - m), o~: rank-space value sum of the codes (rvp = rv_max
+// rounded up to 4), o_A: 128-dim value sum of the anchors.
 struct DecodeArgs {
   int32_t n_ctx;
   int32_t n_splits;
-  int32_t rec;           // floats per code-split record: 4 + rv_max (rounded to 4)
+  int32_t rec;           // floats per record: 4 + rvp + 128
+  int32_t oa;            // offset of o_A in a record: 4 + rvp
   float scale_log2;      // sm_scale * log2(e): scores are kept in log2 units
   const int32_t *ctx_lens;
   const void *q;
-  float *ws_codes;       // [batch][n_q][n_splits][rec]
-  float *ws_anchor;      // [batch][n_q][4 + 128]
+  float *ws;             // [batch][n_q][n_splits][rec]
 };
-
-constexpr int kAnchorRec = 4 + kD;
 
 // ---------------------------------------------------------------------------
 // storage types
@@ -92,6 +97,7 @@ hipError_t launch_store_anchors(const LayerArgs &L, const void *k, const void *v
                                 int64_t sh, int64_t st, int pos0, int n_tok, hipStream_t s);
 hipError_t launch_append(const LayerArgs &L, const void *k, const void *v, int pos, hipStream_t s);
 hipError_t launch_decode_partials(const LayerArgs &L, const DecodeArgs &d, hipStream_t s);
+hipError_t launch_partials_mfma(const LayerArgs &L, const DecodeArgs &d, hipStream_t s);
 hipError_t launch_decode_combine(const LayerArgs &L, const DecodeArgs &d, float *out, hipStream_t s);
 
 }  // namespace lrkv

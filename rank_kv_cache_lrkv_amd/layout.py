@@ -34,6 +34,15 @@ def bases_offsets(rank_k: Sequence[int], rank_v: Sequence[int]):
     return np.array(uk), np.array(uv)
 
 
+def pack_bases(u_k: Sequence[np.ndarray], u_v: Sequence[np.ndarray]) -> np.ndarray:
+    """Flat bases buffer from per-head (128, r) matrices: head by head, U_K^T then
+    U_V^T, each basis direction as 128 contiguous elements."""
+    parts = []
+    for uk, uv in zip(u_k, u_v):
+        parts += [np.asarray(uk).T.ravel(), np.asarray(uv).T.ravel()]
+    return np.concatenate(parts) if parts else np.zeros(0)
+
+
 def codes_elems(ranks: Sequence[int], batch: int, cap: int) -> int:
     return int(batch) * int(cap) * int(np.sum(ranks))
 

@@ -108,8 +108,7 @@ def gpu_layer(hc: HostCase, cap: Optional[int] = None, with_codes: bool = True):
     W = w.window
     cmax = max(0, hc.n - 1 - W)
     cap = layout.round_cap(cmax) if cap is None else cap
-    bases = np.concatenate([np.concatenate([hc.u_k[h].ravel(), hc.u_v[h].ravel()])
-                            for h in range(w.n_kv_heads)])
+    bases = layout.pack_bases(hc.u_k, hc.u_v)
     L = B.Layer.allocate(dtype=B.LRKV_F32 if w.dtype == "f32" else B.LRKV_BF16, batch=w.batch,
                          n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, window=W, cap=cap,
                          rank_k=hc.rk, rank_v=hc.rv, bases=dev(bases, w.dtype))

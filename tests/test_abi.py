@@ -100,8 +100,8 @@ def test_decode_argument_validation():
 def test_workspace_size_formula():
     L = layer()
     lib = B.lib()
-    # records: 4 + max r_v (32) floats per (row, query head, split) plus 132 per (row, query head)
-    assert lib.lrkv_decode_workspace_size(ctypes.byref(L), 3) == (2 * 8 * 3 * 36 + 2 * 8 * 132) * 4
+    # one record of 4 + max r_v (32) + 128 floats per (row, query head, split)
+    assert lib.lrkv_decode_workspace_size(ctypes.byref(L), 3) == 2 * 8 * 3 * (4 + 32 + 128) * 4
     assert lib.lrkv_decode_workspace_size(ctypes.byref(L), 0) == 0
     assert lib.lrkv_decode_workspace_size(ctypes.byref(layer(batch=0)), 3) == 0
 

@@ -28,11 +28,8 @@ def full_rows(w, layer, which):
 
 def bases_flat(w, layer):
     rk, rv = synth.ranks(w, layer)
-    parts = []
-    for h in range(w.n_kv_heads):
-        parts += [synth.basis(w, layer, h, "k", int(rk[h])).ravel(),
-                  synth.basis(w, layer, h, "v", int(rv[h])).ravel()]
-    return rk, rv, np.concatenate(parts)
+    return rk, rv, layout.pack_bases([synth.basis(w, layer, h, "k", int(rk[h])) for h in range(w.n_kv_heads)],
+                                     [synth.basis(w, layer, h, "v", int(rv[h])) for h in range(w.n_kv_heads)])
 
 
 def prefill(w, layer, n, cap=None):

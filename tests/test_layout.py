@@ -51,3 +51,17 @@ def test_offsets():
     assert layout.code_offsets(rk, 2, 64).tolist() == [0, 2 * 64 * 64, 2 * 64 * 96]
     assert layout.round_cap(0) == 0 and layout.round_cap(1) == 32 and layout.round_cap(64) == 64
     assert [layout.anchor_slot(p, 4) for p in range(9)] == [0, 1, 2, 3, 4, 1, 2, 3, 4]
+
+
+def test_pack_bases_rows_are_basis_directions():
+    rng = np.random.default_rng(1)
+    uk = [rng.standard_normal((128, 32)), rng.standard_normal((128, 16))]
+    uv = [rng.standard_normal((128, 16)), rng.standard_normal((128, 48))]
+    flat = layout.pack_bases(uk, uv)
+    assert flat.shape == (layout.bases_elems([32, 16], [16, 48]),)
+    ok, ov = layout.bases_offsets([32, 16], [16, 48])
+    for h in range(2):
+        for c in range(uk[h].shape[1]):
+            assert np.array_equal(flat[ok[h] + 128 * c: ok[h] + 128 * (c + 1)], uk[h][:, c])
+        for c in range(uv[h].shape[1]):
+            assert np.array_equal(flat[ov[h] + 128 * c: ov[h] + 128 * (c + 1)], uv[h][:, c])
