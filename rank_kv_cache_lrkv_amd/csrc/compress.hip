@@ -12,7 +12,8 @@
 namespace lrkv {
 
 // ---------------------------------------------------------------------------
-// Generic projection: float32 storage (and any storage type as a plain path).
+// Generic projection (float32 storage; bf16 runs on the matrix cores, see
+// compress_mfma.hip).
 // One workgroup per (64-token tile, batch row, KV head).  The 64x128 input tile
 // is staged in LDS as float32; each thread produces code columns with a float32
 // dot product over the 128 features against a basis row (read through the cache).
@@ -123,13 +124,10 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
 // ---------------------------------------------------------------------------
 hipError_t launch_compress(const LayerArgs &L, int which, const void *x, int64_t sb, int64_t sh,
                            int64_t st, int n_tok, int slot0, hipStream_t s) {
+  if (L.dtype == LRKV_BF16) return launch_compress_mfma(L, which, x, sb, sh, st, n_tok, slot0, s);
   dim3 grid((n_tok + 63) / 64, L.batch * L.n_kv);
-  if (L.dtype == LRKV_F32)
-    hipLaunchKernelGGL(k_compress_generic<float>, grid, dim3(256), 0, s, L, which,
-                       static_cast<const float *>(x), sb, sh, st, n_tok, slot0);
-  else
-    hipLaunchKernelGGL(k_compress_generic<bf16_t>, grid, dim3(256), 0, s, L, which,
-                       static_cast<const bf16_t *>(x), sb, sh, st, n_tok, slot0);
+  hipLaunchKernelGGL(k_compress_generic<float>, grid, dim3(256), 0, s, L, which,
+                     static_cast<const float *>(x), sb, sh, st, n_tok, slot0);
   return hipGetLastError();
 }
 

@@ -93,6 +93,8 @@ __device__ __forceinline__ int row_ctx(const DecodeArgs &d, int b) {
 // ---------------------------------------------------------------------------
 hipError_t launch_compress(const LayerArgs &L, int which, const void *x, int64_t sb, int64_t sh,
                            int64_t st, int n_tok, int slot0, hipStream_t s);
+hipError_t launch_compress_mfma(const LayerArgs &L, int which, const void *x, int64_t sb,
+                                int64_t sh, int64_t st, int n_tok, int slot0, hipStream_t s);
 hipError_t launch_store_anchors(const LayerArgs &L, const void *k, const void *v, int64_t sb,
                                 int64_t sh, int64_t st, int pos0, int n_tok, hipStream_t s);
 hipError_t launch_append(const LayerArgs &L, const void *k, const void *v, int pos, hipStream_t s);

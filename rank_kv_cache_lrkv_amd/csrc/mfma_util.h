@@ -1,0 +1,37 @@
+// Matrix-core helpers shared by the gfx950 kernels.
+#pragma once
+
+#include "lrkv_internal.h"
+
+namespace lrkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// word 3 of a raw buffer resource on gfx9-family parts (32-bit data format)
+constexpr int kBufferWord3 = 0x00020000;
+
+// 2^x with the hardware exp2 (v_exp_f32): results below 2^-126 flush to zero,
+// 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// x = hi + lo: hi keeps the top 16 bits (truncation), lo is the remainder
+// rounded to nearest bf16; hi + lo matches x to about 2^-16 relative.
+__device__ __forceinline__ float bf16_trunc(float x) {
+  return __uint_as_float(__float_as_uint(x) & 0xffff0000u);
+}
+__device__ __forceinline__ uint32_t pack_hi(float a, float b) {
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+__device__ __forceinline__ uint32_t pack_rne(float a, float b) {
+  return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)a)) |
+         (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)b)) << 16);
+}
+
+}  // namespace lrkv
