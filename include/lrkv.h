@@ -94,7 +94,8 @@ typedef struct lrkv_layer {
   int32_t n_q_heads;      /* multiple of n_kv_heads, group <= LRKV_MAX_GROUP */
   int32_t n_kv_heads;     /* 1 .. LRKV_MAX_KV_HEADS */
   int32_t window;         /* W >= 0 recent tokens kept at full rank */
-  int32_t cap;            /* code slots per (batch row, KV head); multiple of 32, >= 0 */
+  int32_t cap;            /* code slots per (batch row, KV head); multiple of 32, >= 0,
+                             cap * 128 * element size < 2^31 */
   const int32_t *rank_k;  /* host [n_kv_heads] */
   const int32_t *rank_v;  /* host [n_kv_heads] */
   const void *bases;      /* device, see above */
@@ -167,15 +168,21 @@ lrkv_status lrkv_append(const lrkv_layer *L, const void *k_new, const void *v_ne
 size_t lrkv_decode_workspace_size(const lrkv_layer *L, int32_t n_splits);
 int32_t lrkv_decode_auto_splits(const lrkv_layer *L, int32_t n_ctx);
 
-/* Stage 1: per (row, query head, split) the running max (log2 units), the
- * softmax denominator and the rank-space value sum; per (row, query head) the
- * same over the anchors with a 128-dim value sum. */
+/* Stage 1: one workgroup per (split, row, KV head) scores its share of the code
+ * blocks and its share of the anchors (runs of at least 16 anchor rows on the
+ * first splits, none on the rest) for the g query heads of the group, and writes
+ * per (row, query head, split) one float32 record: the running max (log2 units),
+ * the softmax denominator, the rank-space value sum of its codes and, on splits
+ * that hold anchors, the 128-dim value sum of its anchors, all relative to that
+ * max.  The workspace is private to the library between the two stages. */
 lrkv_status lrkv_decode_partials(const lrkv_layer *L, int32_t n_ctx, const int32_t *ctx_lens,
                                  const void *q, float sm_scale, int32_t n_splits,
                                  void *workspace, size_t workspace_bytes, lrkv_stream_t stream);
 
-/* Stage 2: merge the partials of each (row, query head), up-project the
- * rank-space sum once with U_V, add the anchor part and normalise. */
+/* Stage 2: merge the split records of each (row, query head) under their common
+ * max, up-project the merged rank-space sum once with U_V, add the merged anchor
+ * sum and normalise by the merged denominator.  n_splits must be the value the
+ * partials call used (after resolving 0). */
 lrkv_status lrkv_decode_combine(const lrkv_layer *L, int32_t n_splits, const void *workspace,
                                 size_t workspace_bytes, float *out, lrkv_stream_t stream);
 

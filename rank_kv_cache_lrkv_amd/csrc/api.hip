@@ -21,6 +21,8 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   if (L->n_q_heads < L->n_kv_heads || L->n_q_heads % L->n_kv_heads) return LRKV_ERR_SHAPE;
   if (L->n_q_heads / L->n_kv_heads > LRKV_MAX_GROUP) return LRKV_ERR_SHAPE;
   if (L->window < 0 || L->cap < 0 || L->cap % LRKV_BLOCK) return LRKV_ERR_SHAPE;
+  // one (row, head) code region is addressed with 32-bit byte offsets
+  if (int64_t(L->cap) * kD * elem_bytes(L->dtype) > INT32_MAX) return LRKV_ERR_SHAPE;
   if (!L->rank_k || !L->rank_v || !L->bases || !L->codes_k || !L->codes_v || !L->anchor_k ||
       !L->anchor_v)
     return LRKV_ERR_NULL;

@@ -70,6 +70,8 @@ def decode(L, n_ctx=50, q=FAKE, out=FAKE, scale=0.088, S=2, ws=FAKE, ws_bytes=1 
     (dict(n_q_heads=2 * 17, n_kv_heads=2), 2),
     (dict(window=-1), 2),
     (dict(cap=40), 2),
+    (dict(cap=(1 << 31) // 256 // 32 * 32 + 32), 2),          # bf16 code region past 2^31 bytes
+    (dict(dtype=0, cap=(1 << 31) // 512 // 32 * 32 + 32), 2),
     (dict(rank_k=[64, 24]), 3),
     (dict(rank_v=[32, 0]), 3),
     (dict(rank_k=[144, 32]), 3),
