@@ -162,7 +162,8 @@ lrkv_status lrkv_append(const lrkv_layer *L, const void *k_new, const void *v_ne
  *   (1 .. LRKV_MAX_SPLITS; 0 = lrkv_decode_auto_splits).  Results agree across
  *   n_splits to rounding; a fixed n_splits is bitwise reproducible.
  * workspace: device, >= lrkv_decode_workspace_size(L, n_splits) bytes, float32
- *   partial results; fully rewritten by each call.
+ *   split records; needs no initialisation, and lrkv_decode_partials rewrites
+ *   every record lrkv_decode_combine reads.
  * out: device float32 [batch][n_q_heads][128].
  */
 size_t lrkv_decode_workspace_size(const lrkv_layer *L, int32_t n_splits);
@@ -181,11 +182,14 @@ lrkv_status lrkv_decode_partials(const lrkv_layer *L, int32_t n_ctx, const int32
 
 /* Stage 2: merge the split records of each (row, query head) under their common
  * max, up-project the merged rank-space sum once with U_V, add the merged anchor
- * sum and normalise by the merged denominator.  n_splits must be the value the
- * partials call used (after resolving 0). */
-lrkv_status lrkv_decode_combine(const lrkv_layer *L, int32_t n_splits, const void *workspace,
-                                size_t workspace_bytes, float *out, lrkv_stream_t stream);
+ * sum and normalise by the merged denominator.  n_ctx, ctx_lens and n_splits
+ * must be the values the partials call used (n_splits after resolving 0): they
+ * fix which splits hold anchor sums. */
+lrkv_status lrkv_decode_combine(const lrkv_layer *L, int32_t n_ctx, const int32_t *ctx_lens,
+                                int32_t n_splits, const void *workspace, size_t workspace_bytes,
+                                float *out, lrkv_stream_t stream);
 
+/* The whole decode step: stage 1 then stage 2 on `stream`. */
 lrkv_status lrkv_decode_attn(const lrkv_layer *L, int32_t n_ctx, const int32_t *ctx_lens,
                              const void *q, float *out, float sm_scale, int32_t n_splits,
                              void *workspace, size_t workspace_bytes, lrkv_stream_t stream);

@@ -61,7 +61,8 @@ SIGNATURES = [
     ("lrkv_decode_workspace_size", c_size_t, [_P, c_int32]),
     ("lrkv_decode_auto_splits", c_int32, [_P, c_int32]),
     ("lrkv_decode_partials", c_int32, [_P, c_int32, c_void_p, c_void_p, c_float, c_int32, c_void_p, c_size_t, c_void_p]),
-    ("lrkv_decode_combine", c_int32, [_P, c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
+    ("lrkv_decode_combine", c_int32, [_P, c_int32, c_void_p, c_int32, c_void_p, c_size_t, c_void_p,
+                                      c_void_p]),
     ("lrkv_decode_attn", c_int32, [_P, c_int32, c_void_p, c_void_p, c_void_p, c_float, c_int32, c_void_p, c_size_t, c_void_p]),
     ("lrkv_status_string", ctypes.c_char_p, [c_int32]),
     ("lrkv_version", c_int32, []),
@@ -226,9 +227,10 @@ def lrkv_decode_partials(layer: Layer, n_ctx: int, q, sm_scale: float, n_splits:
                                       _stream(stream)), "lrkv_decode_partials")
 
 
-def lrkv_decode_combine(layer: Layer, n_splits: int, ws, out, stream=None):
-    _check(lib().lrkv_decode_combine(ctypes.byref(layer.struct), n_splits, _ptr(ws),
-                                     ws.numel() * ws.element_size(), _ptr(out), _stream(stream)),
+def lrkv_decode_combine(layer: Layer, n_ctx: int, n_splits: int, ws, out, ctx_lens=None, stream=None):
+    _check(lib().lrkv_decode_combine(ctypes.byref(layer.struct), n_ctx, _ptr(ctx_lens), n_splits,
+                                     _ptr(ws), ws.numel() * ws.element_size(), _ptr(out),
+                                     _stream(stream)),
            "lrkv_decode_combine")
 
 

@@ -200,8 +200,9 @@ lrkv_status lrkv_decode_partials(const lrkv_layer *L, int32_t n_ctx, const int32
   return hip_status(launch_decode_partials(A, D, reinterpret_cast<hipStream_t>(stream)));
 }
 
-lrkv_status lrkv_decode_combine(const lrkv_layer *L, int32_t n_splits, const void *workspace,
-                                size_t workspace_bytes, float *out, lrkv_stream_t stream) {
+lrkv_status lrkv_decode_combine(const lrkv_layer *L, int32_t n_ctx, const int32_t *ctx_lens,
+                                int32_t n_splits, const void *workspace, size_t workspace_bytes,
+                                float *out, lrkv_stream_t stream) {
   LayerArgs A;
   lrkv_status st = make_layer(L, &A);
   if (st != LRKV_OK) return st;
@@ -209,8 +210,7 @@ lrkv_status lrkv_decode_combine(const lrkv_layer *L, int32_t n_splits, const voi
   if (!aligned16(out)) return LRKV_ERR_ALIGN;
   if (n_splits < 1 || n_splits > LRKV_MAX_SPLITS) return LRKV_ERR_SHAPE;
   DecodeArgs D;
-  // the context length does not enter the combine; 1 passes every check
-  st = make_decode(L, A, 1, nullptr, nullptr, 1.f, n_splits, const_cast<void *>(workspace),
+  st = make_decode(L, A, n_ctx, ctx_lens, nullptr, 1.f, n_splits, const_cast<void *>(workspace),
                    workspace_bytes, &D);
   if (st != LRKV_OK) return st;
   return hip_status(launch_decode_combine(A, D, out, reinterpret_cast<hipStream_t>(stream)));

@@ -95,99 +95,120 @@ __global__ __launch_bounds__(256) void k_partials_generic(LayerArgs L, DecodeArg
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2: one workgroup (128 threads = the 128 output features) per
-// (query head, batch row), two dependent rounds of loads.  Round 1: the split
-// maxima and denominators, and the U_V column of this thread's output feature.
-// Round 2: every weighted sum at once.  M = max of the split maxima (finite:
-// token 0 is an anchor of every row); weights 2^(m - M); the rank-space sums are
-// merged and up-projected once with U_V, the anchor sums (present on the first
-// splits only) are merged in the 128-dim space, and the total is normalised.
+// Stage 2: one workgroup of 128 threads (t = the output features) per (query
+// head i, batch row b) merges that head's split records, with a single
+// round of loads: every term a thread needs (split maxima and denominators,
+// rank-space sums, anchor sums, its U_V column) is loaded at once from clamped
+// in-bounds indices and masked when used.  The threads form `groups` groups of
+// rv threads; group g merges splits g, g + groups, ... under its own max, then
+// the groups are merged under the common max M (finite: token 0 is an anchor
+// of every row, held by split 0).  The merged rank-space sum is up-projected
+// once with U_V, the anchor sums (on the first splits only) are added in the
+// 128-dim space, and the total is normalised.
+// Loads go through buffer resources (32-bit offsets).
 // ---------------------------------------------------------------------------
+struct CombineSmem {
+  float m[128 / 16], l[128 / 16];  // per group of rv threads
+  float o[128];                    // per thread: its group's rank-space sum
+  float ot[128];                   // the merged rank-space sum
+};
+
 template <typename T>
 __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, float *out) {
-  constexpr int UPRE = 32;  // U_V columns loaded in round 1 (the rest, if any, later)
-  constexpr int PRE = 16;   // weighted-sum terms per thread loaded in one go
-  __shared__ float s_w[LRKV_MAX_SPLITS];
-  __shared__ float s_l[LRKV_MAX_SPLITS];
-  __shared__ float s_part[128];
-  __shared__ float s_o[kD];
-  __shared__ float s_red[2][2];
-  const int i = blockIdx.x, b = blockIdx.y;
+  constexpr int UPRE = 32;  // U_V columns loaded up front (the rest, if any, later)
+  constexpr int PRE = 16;   // terms per thread loaded up front (the rest, if any, later)
+  __shared__ CombineSmem cs;
+  const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int h = i / L.group;
   const HeadInfo hd = L.heads[h];
   const int rv = hd.rv;
   const int S = d.n_splits;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t qi = int64_t(b) * L.n_q + i;
   const float *rc = split_record(d, qi, 0);
+  const __amdgpu_buffer_rsrc_t rr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(rc), 0, S * d.rec * 4, kBufferWord3);
+  auto rec = [&](int s, int f) {  // float f of split s's record
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, (s * d.rec + f) * 4, 0, 0));
+  };
   const int a = min(row_ctx(d, b), 1 + L.window);
   const int per = anchor_rows_per_split(a, S);
   const int sa = min(S, (a + per - 1) / per);  // splits 0 .. sa-1 carry anchor sums
-  const T *Uv = static_cast<const T *>(L.bases) + hd.u_v + tid;  // column tid of the U_V^T rows
-
-  // round 1
-  float upre[UPRE];
-#pragma unroll
-  for (int c = 0; c < UPRE; ++c) upre[c] = to_f32(Uv[min(c, rv - 1) * kD]);  // masked at use
-  float m = kNegInf;
-  for (int s = tid; s < S; s += blockDim.x) {
-    const float ms = rc[int64_t(s) * d.rec];
-    s_w[s] = ms;
-    s_l[s] = rc[int64_t(s) * d.rec + 1];
-    m = fmaxf(m, ms);
-  }
-  m = wave_max(m);
-  if (lane == 0) s_red[0][wave] = m;
-  __syncthreads();
-  const float M = fmaxf(s_red[0][0], s_red[0][1]);
-  float l = 0.f;
-  for (int s = tid; s < S; s += blockDim.x) {
-    const float w = exp2f(s_w[s] - M);  // empty splits: 2^-inf = 0
-    s_w[s] = w;
-    l = fmaf(w, s_l[s], l);
-  }
-  l = wave_sum(l);
-  if (lane == 0) s_red[1][wave] = l;
-  __syncthreads();
-  const float Ltot = s_red[1][0] + s_red[1][1];
-
-  // round 2: rank-space sums in `groups` groups of rv threads (group g takes
-  // splits g, g + groups, ...) and the anchor sums.  The loads are issued first,
-  // unconditionally from clamped in-bounds indices (masked when summed), so that
-  // none waits on another.
-  const int groups = int(blockDim.x) / rv;
-  const int col = tid % rv, grp = tid / rv;
+  // U_V^T rows: element (c, t) is column c of output feature t
+  const __amdgpu_buffer_rsrc_t ur = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T *>(static_cast<const T *>(L.bases) + hd.u_v), 0, rv * kD * int(sizeof(T)), kBufferWord3);
+  auto uv = [&](int c) { return buffer_elem<T>(ur, (c * kD + t) * int(sizeof(T))); };
+  const int groups = 128 / rv;
+  const int col = t % rv, grp = t / rv;
   const int grp_c = min(grp, groups - 1);
-  float ov[PRE], av[PRE];
+
+  float upre[UPRE];
+  float2 ml[PRE];
+  float ov[PRE], ma[PRE], av[PRE];
+  float mg = kNegInf, lg = 0.f, og = 0.f;
+#pragma unroll
+  for (int c = 0; c < UPRE; ++c) upre[c] = uv(min(c, rv - 1));
 #pragma unroll
   for (int k = 0; k < PRE; ++k) {
     const int s = min(grp_c + k * groups, S - 1);
-    ov[k] = rc[int64_t(s) * d.rec + 4 + col];
-    av[k] = rc[int64_t(min(k, sa - 1)) * d.rec + d.oa + tid];
+    ml[k] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rr, s * d.rec * 4, 0, 0));
+    ov[k] = rec(s, 4 + col);
+    const int sk = min(k, sa - 1);
+    ma[k] = rec(sk, 0);
+    av[k] = rec(sk, d.oa + t);
   }
-  float oc = 0.f, oa = 0.f;
+  // this group's splits under the group's own max
+#pragma unroll
+  for (int k = 0; k < PRE; ++k)
+    if (grp_c + k * groups < S) mg = fmaxf(mg, ml[k].x);
 #pragma unroll
   for (int k = 0; k < PRE; ++k) {
-    const int s = grp + k * groups;
-    if (grp < groups && s < S) oc = fmaf(s_w[s], ov[k], oc);
-    if (k < sa) oa = fmaf(s_w[k], av[k], oa);
+    if (grp_c + k * groups < S && ml[k].x != kNegInf) {  // empty splits hold nothing
+      const float w = fast_exp2(ml[k].x - mg);
+      lg = fmaf(w, ml[k].y, lg);
+      og = fmaf(w, ov[k], og);
+    }
   }
-  if (grp < groups)
-    for (int s = grp + PRE * groups; s < S; s += groups) oc = fmaf(s_w[s], rc[int64_t(s) * d.rec + 4 + col], oc);
-  for (int s = PRE; s < sa; ++s) oa = fmaf(s_w[s], rc[int64_t(s) * d.rec + d.oa + tid], oa);
-  s_part[tid] = oc;
+  for (int s = grp_c + PRE * groups; s < S; s += groups) {  // more splits than loaded up front
+    const float ms = rec(s, 0);
+    if (ms == kNegInf) continue;
+    const float mn = fmaxf(mg, ms);
+    const float a0 = fast_exp2(mg - mn), a1 = fast_exp2(ms - mn);  // mg = -inf gives a0 = 0
+    lg = fmaf(a1, rec(s, 1), lg * a0);
+    og = fmaf(a1, rec(s, 4 + col), og * a0);
+    mg = mn;
+  }
+  if (grp < groups) {
+    cs.o[t] = og;
+    if (col == 0) {
+      cs.m[grp] = mg;
+      cs.l[grp] = lg;
+    }
+  }
   __syncthreads();
-  if (tid < rv) {
+
+  float M = kNegInf, Ltot = 0.f, oa = 0.f;
+  for (int g = 0; g < groups; ++g) M = fmaxf(M, cs.m[g]);
+  for (int g = 0; g < groups; ++g)
+    if (cs.m[g] != kNegInf) Ltot = fmaf(fast_exp2(cs.m[g] - M), cs.l[g], Ltot);
+  if (t < rv) {
     float o = 0.f;
-    for (int g = 0; g < groups; ++g) o += s_part[g * rv + tid];
-    s_o[tid] = o;
+    for (int g = 0; g < groups; ++g)
+      if (cs.m[g] != kNegInf) o = fmaf(fast_exp2(cs.m[g] - M), cs.o[g * rv + t], o);
+    cs.ot[t] = o;
   }
+  // anchor sums of output feature t (anchor splits hold at least one row: finite maxima)
+#pragma unroll
+  for (int k = 0; k < PRE; ++k)
+    if (k < sa) oa = fmaf(fast_exp2(ma[k] - M), av[k], oa);
+  for (int s = PRE; s < sa; ++s)
+    oa = fmaf(fast_exp2(rec(s, 0) - M), rec(s, d.oa + t), oa);
   __syncthreads();
+
   float y = 0.f;
 #pragma unroll
-  for (int c = 0; c < UPRE; ++c) y = fmaf(upre[c], c < rv ? s_o[c] : 0.f, y);
-  for (int c = UPRE; c < rv; ++c) y = fmaf(to_f32(Uv[c * kD]), s_o[c], y);
-  out[qi * kD + tid] = (y + oa) / Ltot;
+  for (int c = 0; c < UPRE; ++c) y = fmaf(upre[c], c < rv ? cs.ot[c] : 0.f, y);
+  for (int c = UPRE; c < rv; ++c) y = fmaf(uv(c), cs.ot[c], y);
+  out[qi * kD + t] = (y + oa) / Ltot;
 }
 
 // ---------------------------------------------------------------------------

@@ -8,6 +8,22 @@ namespace lrkv {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// word 3 of a raw buffer resource on gfx9-family parts (32-bit data format)
+constexpr int kBufferWord3 = 0x00020000;
+
+// one element of storage type T at a byte offset of a buffer resource
+template <typename T> __device__ __forceinline__ float buffer_elem(__amdgpu_buffer_rsrc_t r, int off);
+template <> __device__ __forceinline__ float buffer_elem<float>(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+template <> __device__ __forceinline__ float buffer_elem<bf16_t>(__amdgpu_buffer_rsrc_t r, int off) {
+  return to_f32(bf16_t(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0)));
+}
+
+// 2^x with the hardware exp2 (v_exp_f32): results below 2^-126 flush to zero,
+// 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -66,8 +66,6 @@ struct MfmaSmem {
   float m[5][LRKV_MAX_GROUP];               // per wave; [4] = the anchors
   float l[5][LRKV_MAX_GROUP];
   float o[4][LRKV_MAX_GROUP][RVMAX];        // per-wave rank-space sums
-  float pa[LRKV_MAX_GROUP][kAnchorChunk];   // anchor weights of the current chunk
-  float alpha_a[LRKV_MAX_GROUP];
 };
 
 template <int NKC, int NVC>
@@ -160,10 +158,6 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   constexpr int NTW = (NT + 3) / 4;  // column tiles of q~ per wave
   // every load below is unconditional, from a clamped in-bounds address; what is
   // absent is zeroed afterwards (no divergent branches around the loads)
-  u32x4 aq[4];                       // A = q: lane (q4, t16) holds head t16, features 32 kc + 8 q4 ..
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc)
-    aq[kc] = *reinterpret_cast<const u32x4 *>(qb + min(t16, G - 1) * kD + 32 * kc + 8 * q4);
   u32x4 bu[NTW][4];                  // B = rows of U_K^T
 #pragma unroll
   for (int i = 0; i < NTW; ++i) {
@@ -188,15 +182,16 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   __builtin_amdgcn_sched_barrier(0);
 
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
-  if (t16 >= G) {
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) aq[kc] = zero4;
-  }
   if (r16 >= G) qq = zero4;
   if (r16 >= min(na, kAnchorChunk)) kk = vv = zero4;
   *reinterpret_cast<u32x4 *>(&sm.sq[r16][piece * 4]) = qq;
   *reinterpret_cast<u32x4 *>(&sm.ak[r16][piece * 4]) = kk;
   *reinterpret_cast<u32x4 *>(&sm.av[r16][piece * 4]) = vv;
+  lds_barrier();
+  // A = q from LDS: lane (q4, t16) holds head t16, features 32 kc + 8 q4 .. (zero past G)
+  u32x4 aq[4];
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) aq[kc] = *reinterpret_cast<const u32x4 *>(&sm.sq[t16][16 * kc + 4 * q4]);
   // D[head][col] = sum_k q[head][k] U_K[k][col]; the waves share the column tiles
 #pragma unroll
   for (int i = 0; i < NTW; ++i) {
@@ -235,26 +230,22 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   lds_barrier();
 
   // ---- the split's anchor rows (wave 0, before its code blocks, while the other
-  // waves already stream): scores on the matrix cores against q, 128-dim value
-  // sums on the vector ALUs (lane = features 2 lane, 2 lane + 1).  The results go
-  // to LDS slot 4 of the merge.
+  // waves already stream): scores on the matrix cores against q; the 128-dim
+  // value sums are accumulated in LDS (slot 4 of the merge), one head at a time,
+  // every lane taking features 2 lane and 2 lane + 1.  Head hh's weight of row r
+  // sits in lane 16 (r / 4) + hh, register r % 4, and its rescale factor in lane
+  // hh: both are read as scalars.
   if (wave == 0) {
     float mA = kNegInf, lA = 0.f;
-    float acc[LRKV_MAX_GROUP][2];
-#pragma unroll
-    for (int hh = 0; hh < LRKV_MAX_GROUP; ++hh) acc[hh][0] = acc[hh][1] = 0.f;
     for (int r0 = 0; r0 < na; r0 += kAnchorChunk) {
       const int nr = min(kAnchorChunk, na - r0);
       if (r0 > 0) {  // rows past the first chunk: stage them now
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int idx = lane + 64 * i, r = idx >> 4, piece = idx & 15;
-          u32x4 kk = u32x4{0u, 0u, 0u, 0u}, vv = kk;
-          if (r < nr) {
-            const int64_t row = int64_t(unit) * (1 + W) + alo + r0 + r;
-            kk = *reinterpret_cast<const u32x4 *>(static_cast<const bf16_t *>(L.anchor_k) + row * kD + piece * 8);
-            vv = *reinterpret_cast<const u32x4 *>(static_cast<const bf16_t *>(L.anchor_v) + row * kD + piece * 8);
-          }
+          const int64_t row = int64_t(unit) * (1 + W) + alo + r0 + min(r, nr - 1);
+          const u32x4 kk = *reinterpret_cast<const u32x4 *>(static_cast<const bf16_t *>(L.anchor_k) + row * kD + piece * 8);
+          const u32x4 vv = *reinterpret_cast<const u32x4 *>(static_cast<const bf16_t *>(L.anchor_v) + row * kD + piece * 8);
           *reinterpret_cast<u32x4 *>(&sm.ak[r][piece * 4]) = kk;
           *reinterpret_cast<u32x4 *>(&sm.av[r][piece * 4]) = vv;
         }
@@ -280,44 +271,33 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
       ps += __shfl_xor(ps, 32, 64);
       lA = lA * al + ps;
       mA = mn;
-      if (t16 < G) {
+      uint32_t vrow[kAnchorChunk];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) sm.pa[t16][4 * q4 + v] = p[v];
-        if (q4 == 0) sm.alpha_a[t16] = al;
-      }
-      wave_lds_fence();
-#pragma unroll
-      for (int hh = 0; hh < LRKV_MAX_GROUP; ++hh) {
-        if (hh < G) {
-          const float a = sm.alpha_a[hh];
-          acc[hh][0] *= a;
-          acc[hh][1] *= a;
+      for (int r = 0; r < kAnchorChunk; ++r) vrow[r] = sm.av[r][lane];
+      for (int hh = 0; hh < G; ++hh) {
+        float a0 = 0.f, a1 = 0.f;
+        if (r0 > 0) {
+          const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, al), hh));
+          a0 = sm.u.oa[hh][2 * lane] * a;
+          a1 = sm.u.oa[hh][2 * lane + 1] * a;
         }
-      }
-      for (int r = 0; r < nr; ++r) {
-        const uint32_t vv = sm.av[r][lane];
-        const float v0 = __uint_as_float(vv << 16), v1 = __uint_as_float(vv & 0xffff0000u);
 #pragma unroll
-        for (int hh = 0; hh < LRKV_MAX_GROUP; ++hh) {
-          if (hh < G) {
-            const float pw = sm.pa[hh][r];
-            acc[hh][0] = fmaf(pw, v0, acc[hh][0]);
-            acc[hh][1] = fmaf(pw, v1, acc[hh][1]);
+        for (int r = 0; r < kAnchorChunk; ++r) {
+          if (r < nr) {
+            const float pw = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p[r & 3]), 16 * (r >> 2) + hh));
+            a0 = fmaf(pw, __uint_as_float(vrow[r] << 16), a0);
+            a1 = fmaf(pw, __uint_as_float(vrow[r] & 0xffff0000u), a1);
           }
         }
+        sm.u.oa[hh][2 * lane] = a0;
+        sm.u.oa[hh][2 * lane + 1] = a1;
       }
       wave_lds_fence();
     }
     if (q4 == 0 && t16 < G) {
       sm.m[4][t16] = mA;
       sm.l[4][t16] = lA;
-    }
-#pragma unroll
-    for (int hh = 0; hh < LRKV_MAX_GROUP; ++hh) {
-      if (hh < G) {
-        sm.u.oa[hh][2 * lane] = acc[hh][0];
-        sm.u.oa[hh][2 * lane + 1] = acc[hh][1];
-      }
     }
   }
 

@@ -26,13 +26,14 @@ struct LayerArgs {
   HeadInfo heads[LRKV_MAX_KV_HEADS];
 };
 
-// Split s of a (batch row, KV head) covers a share of its code blocks and the
-// anchor rows [s a / S, (s + 1) a / S) of its a anchors; per query head it leaves
-// one record in the workspace:
+// Split s of a (batch row, KV head) covers a share of its code blocks and a
+// share of its a anchors (runs of at least 16 rows on the first splits); per
+// query head it leaves one record in the workspace:
 //   [m, l, 0, 0, o~[rvp], o_A[128]]
 // m: running max of the scores (log2 units, -inf if the split saw nothing),
 // l: sum of 2^(s - m), o~: rank-space value sum of the codes (rvp = rv_max
-// rounded up to 4), o_A: 128-dim value sum of the anchors.
+// rounded up to 4), o_A: 128-dim value sum of the anchors (written only by
+// splits that hold anchors).
 struct DecodeArgs {
   int32_t n_ctx;
   int32_t n_splits;

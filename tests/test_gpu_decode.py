@@ -8,8 +8,9 @@ Sizes are reduced so the oracle finishes in seconds while still spanning many
 import numpy as np
 import pytest
 
+import oracle
 import synth
-from cases import announce, check_decode, gpu_decode, gpu_layer, host_case
+from cases import D, announce, check_decode, dev, gpu_decode, gpu_layer, host_case
 
 pytestmark = pytest.mark.gpu
 
@@ -106,3 +107,28 @@ def test_bitwise_reproducible_and_split_invariant():
     want = hc.expected()
     for S in (1, 5, 64):
         check_decode(gpu_decode(L, hc, n_splits=S), want, "bf16", f"splits{S}")
+
+
+@pytest.mark.parametrize("S,window,ragged", [(3, 64, False), (40, 64, True), (300, 600, False)])
+def test_two_stage_entry_points(S, window, ragged):
+    """Stage 1 and stage 2 called on their own (lrkv_decode_partials, then
+    lrkv_decode_combine with the same context lengths) give the whole call's
+    bits.  S = 40 and S = 300 take the merge past the terms it loads up front;
+    window 600 puts anchor sums on many splits; the ragged case gives rows
+    different anchor splits."""
+    import torch
+    from rank_kv_cache_lrkv_amd import binding as B
+    w = W["qwen3_1p7b_4k"].scaled(batch=3 if ragged else 2, n_ctx=2500, window=window)
+    announce(f"two-stage entry points S={S} W={window} ragged={ragged}")
+    hc = host_case(w, lens=[2500, 700, 40] if ragged else None)
+    L = gpu_layer(hc)
+    whole = gpu_decode(L, hc, n_splits=S, ragged=ragged)
+    q = dev(hc.q, w.dtype)
+    lens = torch.tensor(hc.lens, dtype=torch.int32, device="cuda") if ragged else None
+    ws = B.workspace(L, S)
+    two = torch.empty((w.batch, w.n_q_heads, D), dtype=torch.float32, device="cuda")
+    B.lrkv_decode_partials(L, hc.n, q, oracle.default_scale(), S, ws, ctx_lens=lens)
+    B.lrkv_decode_combine(L, hc.n, S, ws, two, ctx_lens=lens)
+    torch.cuda.synchronize()
+    assert np.array_equal(two.cpu().numpy().astype(np.float64), whole), "stage 1 + stage 2 != whole call"
+    check_decode(whole, hc.expected(), "bf16", f"two-stage S{S}")
