@@ -83,8 +83,16 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   __shared__ MfmaSmem<RKMAX, RVMAX> sm;
 
   const int S = d.n_splits;
-  const int split = blockIdx.x;
-  const int unit = blockIdx.y;
+  // Workgroup i of the launch runs on XCD i % 8, and each XCD has its own L2:
+  // when the units divide evenly, each XCD takes whole (row, head) units, so the
+  // query, U_K and anchor rows a unit's splits read are fetched into one L2.
+  int split = blockIdx.x, unit = blockIdx.y;
+  if (gridDim.y % 8 == 0) {
+    const int i = blockIdx.x + S * blockIdx.y;
+    const int k = i >> 3;
+    unit = (i & 7) * (gridDim.y >> 3) + k / S;
+    split = k % S;
+  }
   const int b = unit / L.n_kv, h = unit % L.n_kv;
   const int G = L.group;
   const int W = L.window;
