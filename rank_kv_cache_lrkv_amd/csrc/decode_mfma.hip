@@ -111,6 +111,20 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   const int na = ahi - alo;
   const int64_t q0 = int64_t(b) * L.n_q + h * G;
   const int first = 4 * split + wave, step = 4 * S;
+  // When every workgroup is resident at once, the older workgroups on a compute unit
+  // get their loads served first and the youngest would stream alone at the end;
+  // the waves with the larger share of their blocks still to read get the higher
+  // issue priority instead, so all of them finish together.
+  const int total = first < nblk ? (nblk - first + step - 1) / step : 0;  // this wave's blocks
+  auto set_priority = [&](int blk) {
+    if (!d.balance) return;
+    const int left = (4 * ((nblk - blk + step - 1) / step)) / (total + 1);  // 0..3
+    if (left >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (left == 2) __builtin_amdgcn_s_setprio(2);
+    else if (left == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  };
+  if (d.balance) __builtin_amdgcn_s_setprio(3);
 
   if (4 * split >= nblk && na == 0) {  // nothing for this split
     for (int i = tid; i < G; i += blockDim.x) {
@@ -143,6 +157,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   for (int ni = 0; ni < NVC; ++ni) voff[ni] = (q4 * rv + 16 * min(ni, nvt - 1) + t16) * 16;
 
   auto load = [&](int blk, BlockRegs<NKC, NVC> &r) {
+    set_priority(blk);
     // the block offsets are wave-uniform: keep them in scalar registers
     const int ks = __builtin_amdgcn_readfirstlane(blk * kblk_bytes);
     const int vs = __builtin_amdgcn_readfirstlane(blk * vblk_bytes);
@@ -481,7 +496,23 @@ static hipError_t launch_rk(const LayerArgs &L, const DecodeArgs &d, hipStream_t
   return launch_rv<RKMAX, 128>(L, d, s);
 }
 
-hipError_t launch_partials_mfma(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
+// compute units of the current device (cached per device)
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+hipError_t launch_partials_mfma(const LayerArgs &L, const DecodeArgs &d0, hipStream_t s) {
+  DecodeArgs d = d0;
+  // balancing pays when the whole grid is resident at once (four workgroups per CU)
+  d.balance = int64_t(d.n_splits) * L.batch * L.n_kv <= 4 * int64_t(cu_count());
   int rk_max = 0;
   for (int h = 0; h < L.n_kv; ++h) rk_max = L.heads[h].rk > rk_max ? L.heads[h].rk : rk_max;
   if (rk_max <= 32) return launch_rk<32>(L, d, s);

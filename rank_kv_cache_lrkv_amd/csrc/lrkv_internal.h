@@ -43,6 +43,7 @@ struct DecodeArgs {
   const int32_t *ctx_lens;
   const void *q;
   float *ws;             // [batch][n_q][n_splits][rec]
+  int32_t balance;       // stage 1: raise the wave priority of the waves with more work left
 };
 
 // ---------------------------------------------------------------------------
