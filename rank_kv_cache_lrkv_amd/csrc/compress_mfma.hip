@@ -40,18 +40,11 @@ __global__ __launch_bounds__(256) void k_compress_mfma(LayerArgs L, int which, c
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, t16 = lane & 15;
 
-  for (int p = tid; p < r * 16; p += blockDim.x) {
-    const int row = p >> 4, piece = p & 15;
-    *reinterpret_cast<u32x4 *>(&su[row * kUStride + piece * 8]) =
-        *reinterpret_cast<const u32x4 *>(ut + row * kD + piece * 8);
-  }
-  __syncthreads();
-
+  // this wave's input rows first (their HBM latency overlaps the staging of U^T):
+  // lane (q4, t16) holds token t16's features 32 kc + 8 q4 .. +7 of the two 16-token
+  // tiles; rows past n_tok re-read the last one and are not stored
   const int t_base = blockIdx.x * 128 + wave * 32;
-  if (t_base >= n_tok) return;  // no barrier follows
   const bf16_t *xb = x + b * sb + h * sh;
-  // operands of the two 16-token tiles: lane (q4, t16) holds token t16's features
-  // 32 kc + 8 q4 .. +7; rows past n_tok re-read the last one and are not stored
   u32x4 xo[2][4];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
@@ -60,6 +53,20 @@ __global__ __launch_bounds__(256) void k_compress_mfma(LayerArgs L, int which, c
     for (int kc = 0; kc < 4; ++kc)
       xo[tt][kc] = *reinterpret_cast<const u32x4 *>(xb + int64_t(tok) * st + 32 * kc + 8 * q4);
   }
+  // U^T rows, r x 16 pieces of 16 bytes, all requested before any is stored
+  u32x4 uu[kD * 16 / 256];
+#pragma unroll
+  for (int k = 0; k < kD * 16 / 256; ++k) {
+    const int p = min(tid + 256 * k, r * 16 - 1);
+    uu[k] = *reinterpret_cast<const u32x4 *>(ut + (p >> 4) * kD + (p & 15) * 8);
+  }
+#pragma unroll
+  for (int k = 0; k < kD * 16 / 256; ++k) {
+    const int p = tid + 256 * k;
+    if (p < r * 16) *reinterpret_cast<u32x4 *>(&su[(p >> 4) * kUStride + (p & 15) * 8]) = uu[k];
+  }
+  __syncthreads();
+  if (t_base >= n_tok) return;  // no barrier follows
   for (int nt = 0; nt < r / 16; ++nt) {
     u32x4 uo[4];
 #pragma unroll
