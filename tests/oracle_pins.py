@@ -321,6 +321,43 @@ def pin_payload_ratios_blog():
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
+def pin_q8_hand_examples():
+    """Int8 rows whose scale comes out a power of two, so every quotient is exact
+    and the rounding rule shows: halves go to the even integer."""
+    x = np.array([[127.0, -63.5, 0.25, 0.0, 62.5], [254.0, 1.0, -3.0, 5.0, -254.0]], np.float32)
+    q, s = oracle.quantize_codes_q8(x)
+    assert s.tolist() == [1.0, 2.0], s
+    assert q[0].tolist() == [127, -64, 0, 0, 62], q[0]
+    assert q[1].tolist() == [127, 0, -2, 2, -127], q[1]
+
+
+def pin_q8_invariants():
+    """Every non-zero row reaches +-127 at its largest entry, each entry is
+    reconstructed to within half a step, signs are kept, a zero row stays zero,
+    and a power-of-two factor moves into the scale only."""
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((200, 48)) * rng.uniform(0.01, 50, (200, 1))).astype(np.float32)
+    x[7] = 0
+    q, s = oracle.quantize_codes_q8(x)
+    assert s[7] == 0 and not q[7].any()
+    nz = s > 0
+    assert np.all(np.abs(q[nz].astype(int)).max(axis=1) == 127)
+    err = np.abs(oracle.dequantize_codes_q8(q, s) - x.astype(np.float64))
+    assert np.all(err <= (0.5 + 1e-5) * s.astype(np.float64)[:, None])
+    assert np.all((np.sign(q) == np.sign(x)) | (q == 0))
+    q2, s2 = oracle.quantize_codes_q8(x * np.float32(8))
+    assert np.array_equal(q2, q) and np.array_equal(s2, s * np.float32(8))
+
+
+def pin_q8_unit_bytes():
+    """An int8 code row is r bytes plus a 4-byte scale: r 64/32 reads 104 bytes
+    per compressed token per KV head instead of 192."""
+    n, w = 1000, 16
+    c, a = len(oracle.code_positions(n, w)), len(oracle.anchor_positions(n, w))
+    assert oracle.compressed_unit_bytes(n, w, 64, 32, q8=True) == c * 104 + a * 512
+    assert oracle.compressed_unit_bytes(n, w, 64, 32) == c * 192 + a * 512
+
+
 def pin_layer_gqa_sdpa():
     """Whole-layer decode with distinct KV heads against the library's GQA
     attention (query head i reads KV head i // g)."""

@@ -44,7 +44,21 @@ MUTANTS = {
     "two_separate_softmaxes": ("oracle_decode_unit", _two_softmaxes),
     "gqa_modulo_mapping": ("oracle_decode_layer", None),
     "missing_scale": ("anchor_scores", lambda q, ka, scale: np.asarray(q, float) @ np.asarray(ka, float).T),
+    "q8_ties_away_from_zero": ("quantize_codes_q8", lambda x: _q8_variant(x, rounding="away")),
+    "q8_scale_over_128": ("quantize_codes_q8", lambda x: _q8_variant(x, divisor=128)),
+    "q8_divisor_127_5": ("quantize_codes_q8", lambda x: _q8_variant(x, divisor=127.5)),
 }
+
+
+def _q8_variant(x, rounding="even", divisor=127):
+    x = np.asarray(x, np.float32)
+    s = (np.max(np.abs(x), axis=1) / np.float32(divisor)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1)).astype(np.float32)
+    t = x / safe[:, None]
+    qf = np.sign(t) * np.floor(np.abs(t) + 0.5) if rounding == "away" else np.rint(t)
+    q = np.clip(qf, -127, 127)
+    q[s == 0] = 0
+    return q.astype(np.int8), s
 
 
 def _gqa_modulo(q, bases_k, bases_v, codes_k, codes_v, anchors_k, anchors_v, scale=None):
