@@ -49,8 +49,10 @@ typedef enum lrkv_status {
 } lrkv_status;
 
 typedef enum lrkv_dtype {
-  LRKV_F32 = 0,  /* float32 storage and float32 arithmetic */
-  LRKV_BF16 = 1  /* bfloat16 storage, float32 accumulation */
+  LRKV_F32 = 0,     /* float32 storage and float32 arithmetic */
+  LRKV_BF16 = 1,    /* bfloat16 storage, float32 accumulation */
+  LRKV_BF16_Q8 = 2  /* bfloat16 bases, anchors, queries and compress/append inputs;
+                       int8 codes with one float32 scale per code slot (see below) */
 } lrkv_dtype;
 
 #define LRKV_HEAD_DIM 128
@@ -87,10 +89,20 @@ typedef enum lrkv_dtype {
  * anchor_k, anchor_v (device): [batch][n_kv_heads][1 + window][128].  Slot 0 is
  *   token 0; a token p >= 1 inside the window sits in slot 1 + (p - 1) % window.
  *   At context n the valid slots are the prefix [0, min(n, 1 + window)).
+ *
+ * Int8 codes (dtype LRKV_BF16_Q8).  The pages pair low-rank caches with
+ * quantisation (LowRAM and Palu abstracts) but fix no quantiser; this one is a
+ * design choice.  A code row x (the float32 projection of one token, r columns)
+ * is stored as q = x / s rounded to nearest even and clipped to [-127, 127], with
+ * s = max_c |x_c| / 127, all in float32 (a zero row: s = 0, q = 0); the code it
+ * stands for is s q.  codes_k / codes_v keep the blocked positions above with
+ * one-byte elements; the scales are float32:
+ *   scales_k, scales_v (device): slot j of batch row b, KV head h at element
+ *   (h * batch + b) * cap + j.
  */
 typedef struct lrkv_layer {
   int32_t dtype;          /* lrkv_dtype */
-  int32_t batch;          /* >= 1 */
+  int32_t batch;          /* >= 1, batch * n_kv_heads <= 65535 */
   int32_t n_q_heads;      /* multiple of n_kv_heads, group <= LRKV_MAX_GROUP */
   int32_t n_kv_heads;     /* 1 .. LRKV_MAX_KV_HEADS */
   int32_t window;         /* W >= 0 recent tokens kept at full rank */
@@ -103,6 +115,8 @@ typedef struct lrkv_layer {
   void *codes_v;          /* device */
   void *anchor_k;         /* device [batch][n_kv_heads][1 + window][128] */
   void *anchor_v;         /* device */
+  float *scales_k;        /* device, LRKV_BF16_Q8 only (may be NULL otherwise) */
+  float *scales_v;        /* device, LRKV_BF16_Q8 only */
 } lrkv_layer;
 
 /*
@@ -110,7 +124,8 @@ typedef struct lrkv_layer {
  * after RoPE).  For every (batch row b, KV head h) and t in [0, n_tok): code slot
  * slot0 + t of `which` (0 = keys with U_K, 1 = values with U_V) receives
  * x[b, h, t, :] U, rounded to the storage type (bf16: round to nearest even of
- * the float32 accumulation).
+ * the float32 accumulation; LRKV_BF16_Q8: the float32 accumulation quantised to
+ * int8 with its scale, as described above).
  *   x: device, element (b, h, t, i) at x + b*stride_b + h*stride_h + t*stride_t + i
  *      (strides in elements of the storage type; the 128 features contiguous).
  * Errors: LRKV_ERR_SHAPE if n_tok < 0, slot0 < 0 or a stride is negative;
@@ -118,6 +133,18 @@ typedef struct lrkv_layer {
  * not 16-byte aligned.  n_tok == 0 is a no-op.
  */
 lrkv_status lrkv_compress(const lrkv_layer *L, int32_t which, const void *x,
+                          int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                          int32_t n_tok, int32_t slot0, lrkv_stream_t stream);
+
+/*
+ * The int8 step of lrkv_compress on given float32 code rows (LRKV_BF16_Q8 layers
+ * only): slot slot0 + t of head h, row b receives the quantisation of
+ * x[b, h, t, 0 .. r-1] (r = the head's rank for `which`) and its scale.
+ *   x: device float32, element (b, h, t, c) at x + b*stride_b + h*stride_h + t*stride_t + c.
+ * Errors: LRKV_ERR_DTYPE for other layer types; otherwise as lrkv_compress
+ * (strides and x need only 4-byte alignment).
+ */
+lrkv_status lrkv_quantize(const lrkv_layer *L, int32_t which, const float *x,
                           int64_t stride_b, int64_t stride_h, int64_t stride_t,
                           int32_t n_tok, int32_t slot0, lrkv_stream_t stream);
 
@@ -138,8 +165,8 @@ lrkv_status lrkv_store_anchors(const lrkv_layer *L, const void *k, const void *v
  * Cache maintenance of one decode step, the same for every batch row: the new
  * token at position `pos` (k_new, v_new: device [batch][n_kv_heads][128]).
  *  - window >= 1 and pos > window: token pos - window leaves the window; its anchor
- *    slot is compressed into code slot pos - window - 1 (keys and values), then the
- *    new token takes over that slot.
+ *    slot is compressed into code slot pos - window - 1 (keys and values; int8 with
+ *    its scale for LRKV_BF16_Q8), then the new token takes over that slot.
  *  - window == 0 and pos >= 1: the new token is compressed into code slot pos - 1.
  *  - otherwise the new token is stored into its anchor slot.
  * Errors: LRKV_ERR_SHAPE if pos < 0; LRKV_ERR_CAPACITY if the code slot >= cap.
@@ -155,7 +182,7 @@ lrkv_status lrkv_append(const lrkv_layer *L, const void *k_new, const void *v_ne
  *   1 .. n_ctx - window - 1 and need cap >= max(0, n_ctx - 1 - window).
  * ctx_lens: optional device int32 [batch] of per-row lengths (ragged batches);
  *   each is clamped into [1, n_ctx].  NULL: every row has n_ctx tokens.
- * q: device [batch][n_q_heads][128] in the storage type.
+ * q: device [batch][n_q_heads][128] in the storage type (bfloat16 for LRKV_BF16_Q8).
  * sm_scale: score scale, normally 1/sqrt(128).
  * n_splits: the compressed tokens of each (row, KV head) are cut into this many
  *   contiguous ranges of 32-slot blocks, each scored by its own workgroup

@@ -22,7 +22,7 @@ from . import layout
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblrkv.so")
 
-LRKV_F32, LRKV_BF16 = 0, 1
+LRKV_F32, LRKV_BF16, LRKV_BF16_Q8 = 0, 1, 2
 HEAD_DIM = 128
 BLOCK = 32
 
@@ -46,6 +46,7 @@ class lrkv_layer(ctypes.Structure):
         ("rank_k", POINTER(c_int32)), ("rank_v", POINTER(c_int32)),
         ("bases", c_void_p), ("codes_k", c_void_p), ("codes_v", c_void_p),
         ("anchor_k", c_void_p), ("anchor_v", c_void_p),
+        ("scales_k", c_void_p), ("scales_v", c_void_p),
     ]
 
 
@@ -56,6 +57,7 @@ _lock = threading.Lock()
 _P = POINTER(lrkv_layer)
 SIGNATURES = [
     ("lrkv_compress", c_int32, [_P, c_int32, c_void_p, c_int64, c_int64, c_int64, c_int32, c_int32, c_void_p]),
+    ("lrkv_quantize", c_int32, [_P, c_int32, c_void_p, c_int64, c_int64, c_int64, c_int32, c_int32, c_void_p]),
     ("lrkv_store_anchors", c_int32, [_P, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int32, c_int32, c_void_p]),
     ("lrkv_append", c_int32, [_P, c_void_p, c_void_p, c_int32, c_void_p]),
     ("lrkv_decode_workspace_size", c_size_t, [_P, c_int32]),
@@ -133,6 +135,8 @@ class Layer:
     codes_v: "object"
     anchor_k: "object"
     anchor_v: "object"
+    scales_k: "object" = None  # int8 codes only: float32 [n_kv_heads][batch][cap]
+    scales_v: "object" = None
     _rk: object = field(default=None, repr=False)
     _rv: object = field(default=None, repr=False)
     struct: lrkv_layer = field(default=None, repr=False)
@@ -144,7 +148,7 @@ class Layer:
             self.dtype, self.batch, self.n_q_heads, self.n_kv_heads, self.window, self.cap,
             ctypes.cast(self._rk, POINTER(c_int32)), ctypes.cast(self._rv, POINTER(c_int32)),
             _ptr(self.bases), _ptr(self.codes_k), _ptr(self.codes_v),
-            _ptr(self.anchor_k), _ptr(self.anchor_v))
+            _ptr(self.anchor_k), _ptr(self.anchor_v), _ptr(self.scales_k), _ptr(self.scales_v))
 
     @property
     def group(self) -> int:
@@ -152,17 +156,24 @@ class Layer:
 
     @property
     def torch_dtype(self):
+        """Storage type of bases, anchors, queries and compress inputs."""
         import torch
         return torch.float32 if self.dtype == LRKV_F32 else torch.bfloat16
+
+    @property
+    def code_dtype(self):
+        import torch
+        return torch.int8 if self.dtype == LRKV_BF16_Q8 else self.torch_dtype
 
     @classmethod
     def allocate(cls, *, dtype: int, batch: int, n_q_heads: int, n_kv_heads: int, window: int,
                  cap: int, rank_k: Sequence[int], rank_v: Sequence[int], device="cuda",
                  bases=None) -> "Layer":
-        """Allocate zeroed codes and anchors (torch) for the given geometry.
-        ``bases`` (optional) is the flat bases tensor; otherwise zeros."""
+        """Allocate zeroed codes and anchors (and int8 scales) (torch) for the given
+        geometry.  ``bases`` (optional) is the flat bases tensor; otherwise zeros."""
         import torch
         td = torch.float32 if dtype == LRKV_F32 else torch.bfloat16
+        cd = torch.int8 if dtype == LRKV_BF16_Q8 else td
         rk = np.asarray(rank_k, np.int32)
         rv = np.asarray(rank_v, np.int32)
         cap = layout.round_cap(cap)
@@ -170,11 +181,16 @@ class Layer:
         if bases is None:
             bases = torch.zeros(nb, dtype=td, device=device)
         assert bases.numel() == nb and bases.dtype == td
-        ck = torch.zeros(max(1, layout.codes_elems(rk, batch, cap)), dtype=td, device=device)
-        cv = torch.zeros(max(1, layout.codes_elems(rv, batch, cap)), dtype=td, device=device)
+        ck = torch.zeros(max(1, layout.codes_elems(rk, batch, cap)), dtype=cd, device=device)
+        cv = torch.zeros(max(1, layout.codes_elems(rv, batch, cap)), dtype=cd, device=device)
         ak = torch.zeros((batch, n_kv_heads, 1 + window, HEAD_DIM), dtype=td, device=device)
         av = torch.zeros_like(ak)
-        return cls(dtype, batch, n_q_heads, n_kv_heads, window, cap, rk, rv, bases, ck, cv, ak, av)
+        sk = sv = None
+        if dtype == LRKV_BF16_Q8:
+            sk = torch.zeros(max(1, layout.scales_elems(n_kv_heads, batch, cap)), dtype=torch.float32,
+                             device=device)
+            sv = torch.zeros_like(sk)
+        return cls(dtype, batch, n_q_heads, n_kv_heads, window, cap, rk, rv, bases, ck, cv, ak, av, sk, sv)
 
 
 # ---------------------------------------------------------------------------
@@ -188,6 +204,16 @@ def lrkv_compress(layer: Layer, which: int, x, n_tok: int, slot0: int, stream=No
     assert si == 1
     _check(lib().lrkv_compress(ctypes.byref(layer.struct), which, _ptr(x), sb, sh, st, n_tok, slot0,
                                _stream(stream)), "lrkv_compress")
+
+
+def lrkv_quantize(layer: Layer, which: int, x, n_tok: int, slot0: int, stream=None):
+    """x: float32 device tensor viewed as [batch][n_kv_heads][>= n_tok][>= r]
+    (any strides, last dimension contiguous): code rows to quantise into int8
+    slots slot0 .. slot0 + n_tok - 1."""
+    sb, sh, st, si = x.stride()
+    assert si == 1
+    _check(lib().lrkv_quantize(ctypes.byref(layer.struct), which, _ptr(x), sb, sh, st, n_tok, slot0,
+                               _stream(stream)), "lrkv_quantize")
 
 
 def lrkv_store_anchors(layer: Layer, k, v, pos0: int, n_tok: int, stream=None):

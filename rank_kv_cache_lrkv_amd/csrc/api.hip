@@ -16,8 +16,10 @@ int elem_bytes(int32_t dtype) { return dtype == LRKV_F32 ? 4 : 2; }
 // Checks the layer description and fills the kernel-side copy.
 lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   if (!L) return LRKV_ERR_NULL;
-  if (L->dtype != LRKV_F32 && L->dtype != LRKV_BF16) return LRKV_ERR_DTYPE;
+  if (L->dtype != LRKV_F32 && L->dtype != LRKV_BF16 && L->dtype != LRKV_BF16_Q8) return LRKV_ERR_DTYPE;
   if (L->batch < 1 || L->n_kv_heads < 1 || L->n_kv_heads > LRKV_MAX_KV_HEADS) return LRKV_ERR_SHAPE;
+  // (row, head) units are the second launch dimension
+  if (int64_t(L->batch) * L->n_kv_heads > 65535) return LRKV_ERR_SHAPE;
   if (L->n_q_heads < L->n_kv_heads || L->n_q_heads % L->n_kv_heads) return LRKV_ERR_SHAPE;
   if (L->n_q_heads / L->n_kv_heads > LRKV_MAX_GROUP) return LRKV_ERR_SHAPE;
   if (L->window < 0 || L->cap < 0 || L->cap % LRKV_BLOCK) return LRKV_ERR_SHAPE;
@@ -29,6 +31,10 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   if (!aligned16(L->bases) || !aligned16(L->codes_k) || !aligned16(L->codes_v) ||
       !aligned16(L->anchor_k) || !aligned16(L->anchor_v))
     return LRKV_ERR_ALIGN;
+  if (L->dtype == LRKV_BF16_Q8) {
+    if (!L->scales_k || !L->scales_v) return LRKV_ERR_NULL;
+    if (!aligned16(L->scales_k) || !aligned16(L->scales_v)) return LRKV_ERR_ALIGN;
+  }
   std::memset(A, 0, sizeof(*A));
   A->dtype = L->dtype;
   A->batch = L->batch;
@@ -42,6 +48,8 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   A->codes_v = L->codes_v;
   A->anchor_k = L->anchor_k;
   A->anchor_v = L->anchor_v;
+  A->scales_k = L->dtype == LRKV_BF16_Q8 ? L->scales_k : nullptr;
+  A->scales_v = L->dtype == LRKV_BF16_Q8 ? L->scales_v : nullptr;
   int64_t ub = 0, ck = 0, cv = 0;
   int rv_max = 0;
   for (int h = 0; h < L->n_kv_heads; ++h) {
@@ -140,6 +148,24 @@ lrkv_status lrkv_compress(const lrkv_layer *L, int32_t which, const void *x, int
   st = check_strides(L, x, stride_b, stride_h, stride_t);
   if (st != LRKV_OK) return st;
   return hip_status(launch_compress(A, which, x, stride_b, stride_h, stride_t, n_tok, slot0,
+                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
+lrkv_status lrkv_quantize(const lrkv_layer *L, int32_t which, const float *x, int64_t stride_b,
+                          int64_t stride_h, int64_t stride_t, int32_t n_tok, int32_t slot0,
+                          lrkv_stream_t stream) {
+  LayerArgs A;
+  lrkv_status st = make_layer(L, &A);
+  if (st != LRKV_OK) return st;
+  if (L->dtype != LRKV_BF16_Q8) return LRKV_ERR_DTYPE;
+  if (which != 0 && which != 1) return LRKV_ERR_SHAPE;
+  if (n_tok < 0 || slot0 < 0) return LRKV_ERR_SHAPE;
+  if (int64_t(slot0) + n_tok > L->cap) return LRKV_ERR_CAPACITY;
+  if (n_tok == 0) return LRKV_OK;
+  if (!x) return LRKV_ERR_NULL;
+  if (stride_b < 0 || stride_h < 0 || stride_t < 0) return LRKV_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(x) & 3u) return LRKV_ERR_ALIGN;
+  return hip_status(launch_quantize(A, which, x, stride_b, stride_h, stride_t, n_tok, slot0,
                                     reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -7,13 +7,13 @@
 // anchor policy follows the OjaKV article's FAQ (first token and the most recent
 // tokens stay at full rank).
 
-#include "lrkv_internal.h"
+#include "decode_common.h"
 
 namespace lrkv {
 
 // ---------------------------------------------------------------------------
-// Generic projection (float32 storage; bf16 runs on the matrix cores, see
-// compress_mfma.hip).
+// Generic projection (float32 storage; bf16 and int8 codes run on the matrix
+// cores, see compress_mfma.hip).
 // One workgroup per (64-token tile, batch row, KV head).  The 64x128 input tile
 // is staged in LDS as float32; each thread produces code columns with a float32
 // dot product over the 128 features against a basis row (read through the cache).
@@ -70,9 +70,20 @@ __global__ __launch_bounds__(128) void k_store_anchors(LayerArgs L, const T *k, 
 // to compress is staged in LDS before the anchor slot is overwritten, so the
 // read of the leaving token and the write of the new one cannot overlap.
 // ---------------------------------------------------------------------------
-template <typename T>
+// largest |x| over the 128 threads of the workgroup (every thread calls it)
+__device__ __forceinline__ float block_absmax(float x, float *red) {
+  const float w = wave_max(fabsf(x));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
+  __syncthreads();
+  const float a = fmaxf(red[0], red[1]);
+  __syncthreads();
+  return a;
+}
+
+template <typename T, bool Q8>
 __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, const T *vnew, int pos) {
   __shared__ float rk_row[kD], rv_row[kD];
+  __shared__ float red[2];
   const int unit = blockIdx.x;
   const int b = unit / L.n_kv, h = unit % L.n_kv;
   const int W = L.window;
@@ -97,20 +108,30 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
     slot = anchor_slot(pos, W);
   }
   __syncthreads();
-  if (code_slot >= 0) {
+  if (code_slot >= 0) {  // uniform over the workgroup
     const T *Uk = static_cast<const T *>(L.bases) + hd.u_k;
     const T *Uv = static_cast<const T *>(L.bases) + hd.u_v;
-    T *ck = static_cast<T *>(L.codes_k) + hd.ck + int64_t(b) * L.cap * hd.rk;
-    T *cv = static_cast<T *>(L.codes_v) + hd.cv + int64_t(b) * L.cap * hd.rv;
-    if (tid < hd.rk) {
-      float acc = 0.f;
-      for (int k = 0; k < kD; ++k) acc = fmaf(rk_row[k], to_f32(Uk[tid * kD + k]), acc);
-      ck[kslot(code_slot, tid, hd.rk)] = from_f32<T>(acc);
-    }
-    if (tid < hd.rv) {
-      float acc = 0.f;
-      for (int k = 0; k < kD; ++k) acc = fmaf(rv_row[k], to_f32(Uv[tid * kD + k]), acc);
-      cv[vslot(code_slot, tid, hd.rv)] = from_f32<T>(acc);
+    float acck = 0.f, accv = 0.f;
+    if (tid < hd.rk)
+      for (int k = 0; k < kD; ++k) acck = fmaf(rk_row[k], to_f32(Uk[tid * kD + k]), acck);
+    if (tid < hd.rv)
+      for (int k = 0; k < kD; ++k) accv = fmaf(rv_row[k], to_f32(Uv[tid * kD + k]), accv);
+    if constexpr (Q8) {
+      int8_t *ck = static_cast<int8_t *>(L.codes_k) + hd.ck + int64_t(b) * L.cap * hd.rk;
+      int8_t *cv = static_cast<int8_t *>(L.codes_v) + hd.cv + int64_t(b) * L.cap * hd.rv;
+      const float sk = q8_scale(block_absmax(tid < hd.rk ? acck : 0.f, red));
+      const float sv = q8_scale(block_absmax(tid < hd.rv ? accv : 0.f, red));
+      if (tid < hd.rk) ck[kslot(code_slot, tid, hd.rk)] = int8_t(q8_value(acck, sk));
+      if (tid < hd.rv) cv[vslot(code_slot, tid, hd.rv)] = int8_t(q8_value(accv, sv));
+      if (tid == 0) {
+        L.scales_k[scale_index(L, h, b, code_slot)] = sk;
+        L.scales_v[scale_index(L, h, b, code_slot)] = sv;
+      }
+    } else {
+      T *ck = static_cast<T *>(L.codes_k) + hd.ck + int64_t(b) * L.cap * hd.rk;
+      T *cv = static_cast<T *>(L.codes_v) + hd.cv + int64_t(b) * L.cap * hd.rv;
+      if (tid < hd.rk) ck[kslot(code_slot, tid, hd.rk)] = from_f32<T>(acck);
+      if (tid < hd.rv) cv[vslot(code_slot, tid, hd.rv)] = from_f32<T>(accv);
     }
   }
   if (slot >= 0) {
@@ -120,11 +141,43 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
 }
 
 // ---------------------------------------------------------------------------
+// Int8 quantisation of given float32 code rows: one wave per (token, row, head),
+// lane l holding columns l and l + 64.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quantize(LayerArgs L, int which, const float *x, int64_t sb,
+                                                  int64_t sh, int64_t st, int n_tok, int slot0) {
+  const int t = blockIdx.x * 4 + int(threadIdx.x >> 6);
+  const int unit = blockIdx.y;
+  const int b = unit / L.n_kv, h = unit % L.n_kv;
+  if (t >= n_tok) return;  // no barrier follows
+  const HeadInfo hd = L.heads[h];
+  const int r = which ? hd.rv : hd.rk;
+  const int lane = threadIdx.x & 63;
+  const float *row = x + b * sb + h * sh + int64_t(t) * st;
+  const float v0 = lane < r ? row[lane] : 0.f;
+  const float v1 = lane + 64 < r ? row[lane + 64] : 0.f;
+  const float s = q8_scale(wave_max(fmaxf(fabsf(v0), fabsf(v1))));
+  int8_t *codes = static_cast<int8_t *>(which ? L.codes_v : L.codes_k) + (which ? hd.cv : hd.ck) +
+                  int64_t(b) * L.cap * r;
+  const int j = slot0 + t;
+  if (lane < r) codes[which ? vslot(j, lane, r) : kslot(j, lane, r)] = int8_t(q8_value(v0, s));
+  if (lane + 64 < r) codes[which ? vslot(j, lane + 64, r) : kslot(j, lane + 64, r)] = int8_t(q8_value(v1, s));
+  if (lane == 0) (which ? L.scales_v : L.scales_k)[scale_index(L, h, b, j)] = s;
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+hipError_t launch_quantize(const LayerArgs &L, int which, const float *x, int64_t sb, int64_t sh,
+                           int64_t st, int n_tok, int slot0, hipStream_t s) {
+  dim3 grid((n_tok + 3) / 4, L.batch * L.n_kv);
+  hipLaunchKernelGGL(k_quantize, grid, dim3(256), 0, s, L, which, x, sb, sh, st, n_tok, slot0);
+  return hipGetLastError();
+}
+
 hipError_t launch_compress(const LayerArgs &L, int which, const void *x, int64_t sb, int64_t sh,
                            int64_t st, int n_tok, int slot0, hipStream_t s) {
-  if (L.dtype == LRKV_BF16) return launch_compress_mfma(L, which, x, sb, sh, st, n_tok, slot0, s);
+  if (L.dtype != LRKV_F32) return launch_compress_mfma(L, which, x, sb, sh, st, n_tok, slot0, s);
   dim3 grid((n_tok + 63) / 64, L.batch * L.n_kv);
   hipLaunchKernelGGL(k_compress_generic<float>, grid, dim3(256), 0, s, L, which,
                      static_cast<const float *>(x), sb, sh, st, n_tok, slot0);
@@ -146,10 +199,13 @@ hipError_t launch_store_anchors(const LayerArgs &L, const void *k, const void *v
 hipError_t launch_append(const LayerArgs &L, const void *k, const void *v, int pos, hipStream_t s) {
   dim3 grid(L.batch * L.n_kv);
   if (L.dtype == LRKV_F32)
-    hipLaunchKernelGGL(k_append<float>, grid, dim3(kD), 0, s, L, static_cast<const float *>(k),
+    hipLaunchKernelGGL((k_append<float, false>), grid, dim3(kD), 0, s, L, static_cast<const float *>(k),
                        static_cast<const float *>(v), pos);
+  else if (L.dtype == LRKV_BF16)
+    hipLaunchKernelGGL((k_append<bf16_t, false>), grid, dim3(kD), 0, s, L, static_cast<const bf16_t *>(k),
+                       static_cast<const bf16_t *>(v), pos);
   else
-    hipLaunchKernelGGL(k_append<bf16_t>, grid, dim3(kD), 0, s, L, static_cast<const bf16_t *>(k),
+    hipLaunchKernelGGL((k_append<bf16_t, true>), grid, dim3(kD), 0, s, L, static_cast<const bf16_t *>(k),
                        static_cast<const bf16_t *>(v), pos);
   return hipGetLastError();
 }

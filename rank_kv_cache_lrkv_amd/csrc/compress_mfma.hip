@@ -18,6 +18,9 @@
 //
 // The work is bound by reading the 256-byte input rows: 16 MFMAs per 32 tokens
 // and 16 columns keep the matrix cores a small fraction busy.
+//
+// Int8 codes (LRKV_BF16_Q8) take the same products; each token's row is then
+// quantised with its own scale (largest |code| / 127).
 
 #include "mfma_util.h"
 
@@ -25,6 +28,17 @@ namespace lrkv {
 
 constexpr int kUStride = kD + 8;  // padded LDS row of one basis direction
 
+// 4 int8 values in the bytes of one word, first value in the low byte
+__device__ __forceinline__ uint32_t pack_q8(f32x4 v, float s0, float s1, float s2, float s3) {
+  return (uint32_t(q8_value(v[0], s0)) & 0xffu) | ((uint32_t(q8_value(v[1], s1)) & 0xffu) << 8) |
+         ((uint32_t(q8_value(v[2], s2)) & 0xffu) << 16) | (uint32_t(q8_value(v[3], s3)) << 24);
+}
+
+// Q8: int8 codes with one float32 scale per token and matrix.  The largest
+// |code| of a token is known only once every column tile is done, so the tiles
+// are swept twice (the products are cheap next to reading the rows): the first
+// sweep takes the maxima and writes the scales, the second quantises.
+template <bool Q8>
 __global__ __launch_bounds__(256) void k_compress_mfma(LayerArgs L, int which, const bf16_t *x,
                                                        int64_t sb, int64_t sh, int64_t st,
                                                        int n_tok, int slot0) {
@@ -34,8 +48,7 @@ __global__ __launch_bounds__(256) void k_compress_mfma(LayerArgs L, int which, c
   const HeadInfo hd = L.heads[h];
   const int r = which ? hd.rv : hd.rk;
   const bf16_t *ut = static_cast<const bf16_t *>(L.bases) + (which ? hd.u_v : hd.u_k);
-  bf16_t *codes = static_cast<bf16_t *>(which ? L.codes_v : L.codes_k) + (which ? hd.cv : hd.ck) +
-                  int64_t(b) * L.cap * r;
+  const int64_t region = (which ? hd.cv : hd.ck) + int64_t(b) * L.cap * r;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, t16 = lane & 15;
@@ -67,41 +80,129 @@ __global__ __launch_bounds__(256) void k_compress_mfma(LayerArgs L, int which, c
   }
   __syncthreads();
   if (t_base >= n_tok) return;  // no barrier follows
-  for (int nt = 0; nt < r / 16; ++nt) {
-    u32x4 uo[4];
+
+  // column tile nt of the basis, then the 16 x 16 product with token tile tt
+  // (keys: lane (q4, t16) gets columns 16 nt + 4 q4 + v of token t16; values:
+  // tokens 4 q4 + v of column 16 nt + t16)
+  auto basis_tile = [&](int nt, u32x4 (&uo)[4]) {
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
       uo[kc] = *reinterpret_cast<const u32x4 *>(&su[(16 * nt + t16) * kUStride + 32 * kc + 8 * q4]);
+  };
+  auto product = [&](const u32x4 (&uo)[4], int tt) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (which == 0) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (which == 0) {
+      for (int kc = 0; kc < 4; ++kc) acc = mfma16x16x32(uo[kc], xo[tt][kc], acc);
+    } else {
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) acc = mfma16x16x32(uo[kc], xo[tt][kc], acc);
-        // lane (q4, t16): columns 16 nt + 4 q4 + v of token t16
-        const int tok = t_base + 16 * tt + t16;
-        if (tok < n_tok) {
-          uint2 v2;
-          v2.x = pack_rne(acc[0], acc[1]);
-          v2.y = pack_rne(acc[2], acc[3]);
-          *reinterpret_cast<uint2 *>(codes + kslot(slot0 + tok, 16 * nt + 4 * q4, r)) = v2;
+      for (int kc = 0; kc < 4; ++kc) acc = mfma16x16x32(xo[tt][kc], uo[kc], acc);
+    }
+    return acc;
+  };
+
+  if constexpr (!Q8) {
+    bf16_t *codes = static_cast<bf16_t *>(which ? L.codes_v : L.codes_k) + region;
+    for (int nt = 0; nt < r / 16; ++nt) {
+      u32x4 uo[4];
+      basis_tile(nt, uo);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const f32x4 acc = product(uo, tt);
+        if (which == 0) {
+          const int tok = t_base + 16 * tt + t16;
+          if (tok < n_tok) {
+            uint2 v2;
+            v2.x = pack_rne(acc[0], acc[1]);
+            v2.y = pack_rne(acc[2], acc[3]);
+            *reinterpret_cast<uint2 *>(codes + kslot(slot0 + tok, 16 * nt + 4 * q4, r)) = v2;
+          }
+        } else {
+          // 8 contiguous bytes when the 4 slots are 4-aligned and present
+          const int tok0 = t_base + 16 * tt + 4 * q4;
+          const int col = 16 * nt + t16;
+          const int j0 = slot0 + tok0;
+          if (tok0 + 3 < n_tok && (j0 & 3) == 0) {
+            uint2 v2;
+            v2.x = pack_rne(acc[0], acc[1]);
+            v2.y = pack_rne(acc[2], acc[3]);
+            *reinterpret_cast<uint2 *>(codes + vslot(j0, col, r)) = v2;
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (tok0 + v < n_tok) codes[vslot(j0 + v, col, r)] = from_f32<bf16_t>(acc[v]);
+          }
         }
-      } else {
+      }
+    }
+  } else {
+    int8_t *codes = static_cast<int8_t *>(which ? L.codes_v : L.codes_k) + region;
+    float *scales = (which ? L.scales_v : L.scales_k) + scale_index(L, h, b, 0);
+    // sweep 1: amax[tt][v] = largest |code| of this lane's token(s) (keys: v = 0 only)
+    float amax[2][4] = {};
+    for (int nt = 0; nt < r / 16; ++nt) {
+      u32x4 uo[4];
+      basis_tile(nt, uo);
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) acc = mfma16x16x32(xo[tt][kc], uo[kc], acc);
-        // lane (q4, t16): tokens 4 q4 + v of column 16 nt + t16
-        const int tok0 = t_base + 16 * tt + 4 * q4;
-        const int col = 16 * nt + t16;
-        const int j0 = slot0 + tok0;
-        if (tok0 + 3 < n_tok && (j0 & 3) == 0) {
-          uint2 v2;
-          v2.x = pack_rne(acc[0], acc[1]);
-          v2.y = pack_rne(acc[2], acc[3]);
-          *reinterpret_cast<uint2 *>(codes + vslot(j0, col, r)) = v2;
+      for (int tt = 0; tt < 2; ++tt) {
+        const f32x4 acc = product(uo, tt);
+        if (which == 0) {
+          amax[tt][0] = fmaxf(amax[tt][0], fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])),
+                                                 fmaxf(fabsf(acc[2]), fabsf(acc[3]))));
         } else {
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (tok0 + v < n_tok) codes[vslot(j0 + v, col, r)] = from_f32<bf16_t>(acc[v]);
+          for (int v = 0; v < 4; ++v) amax[tt][v] = fmaxf(amax[tt][v], fabsf(acc[v]));
+        }
+      }
+    }
+    // keys: a token's columns are spread over the 4 lanes q4 (xor 16, 32);
+    // values: over the 16 lanes t16 (xor 1 .. 8)
+    float sc[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      if (which == 0) {
+        float a = amax[tt][0];
+        a = fmaxf(a, __shfl_xor(a, 16, 64));
+        a = fmaxf(a, __shfl_xor(a, 32, 64));
+        sc[tt][0] = sc[tt][1] = sc[tt][2] = sc[tt][3] = q8_scale(a);
+        const int tok = t_base + 16 * tt + t16;
+        if (q4 == 0 && tok < n_tok) scales[slot0 + tok] = sc[tt][0];
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float a = amax[tt][v];
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+          sc[tt][v] = q8_scale(a);
+          const int tok = t_base + 16 * tt + 4 * q4 + v;
+          if (t16 == 0 && tok < n_tok) scales[slot0 + tok] = sc[tt][v];
+        }
+      }
+    }
+    // sweep 2: quantise and store (4 bytes of one word where they are contiguous)
+    for (int nt = 0; nt < r / 16; ++nt) {
+      u32x4 uo[4];
+      basis_tile(nt, uo);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const f32x4 acc = product(uo, tt);
+        if (which == 0) {
+          const int tok = t_base + 16 * tt + t16;
+          if (tok < n_tok)
+            *reinterpret_cast<uint32_t *>(codes + kslot(slot0 + tok, 16 * nt + 4 * q4, r)) =
+                pack_q8(acc, sc[tt][0], sc[tt][0], sc[tt][0], sc[tt][0]);
+        } else {
+          const int tok0 = t_base + 16 * tt + 4 * q4;
+          const int col = 16 * nt + t16;
+          const int j0 = slot0 + tok0;
+          if (tok0 + 3 < n_tok && (j0 & 3) == 0) {
+            *reinterpret_cast<uint32_t *>(codes + vslot(j0, col, r)) =
+                pack_q8(acc, sc[tt][0], sc[tt][1], sc[tt][2], sc[tt][3]);
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (tok0 + v < n_tok) codes[vslot(j0 + v, col, r)] = int8_t(q8_value(acc[v], sc[tt][v]));
+          }
         }
       }
     }
@@ -111,8 +212,12 @@ __global__ __launch_bounds__(256) void k_compress_mfma(LayerArgs L, int which, c
 hipError_t launch_compress_mfma(const LayerArgs &L, int which, const void *x, int64_t sb,
                                 int64_t sh, int64_t st, int n_tok, int slot0, hipStream_t s) {
   dim3 grid((n_tok + 127) / 128, L.batch * L.n_kv);
-  hipLaunchKernelGGL(k_compress_mfma, grid, dim3(256), 0, s, L, which,
-                     static_cast<const bf16_t *>(x), sb, sh, st, n_tok, slot0);
+  if (L.dtype == LRKV_BF16_Q8)
+    hipLaunchKernelGGL(k_compress_mfma<true>, grid, dim3(256), 0, s, L, which,
+                       static_cast<const bf16_t *>(x), sb, sh, st, n_tok, slot0);
+  else
+    hipLaunchKernelGGL(k_compress_mfma<false>, grid, dim3(256), 0, s, L, which,
+                       static_cast<const bf16_t *>(x), sb, sh, st, n_tok, slot0);
   return hipGetLastError();
 }
 

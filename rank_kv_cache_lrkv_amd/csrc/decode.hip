@@ -215,7 +215,7 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, floa
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_decode_partials(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
-  if (L.dtype == LRKV_BF16) return launch_partials_mfma(L, d, s);
+  if (L.dtype != LRKV_F32) return launch_partials_mfma(L, d, s);
   dim3 grid(d.n_splits, L.batch * L.n_kv);
   hipLaunchKernelGGL(k_partials_generic<float>, grid, dim3(256), 0, s, L, d);
   return hipGetLastError();

@@ -1,4 +1,5 @@
-// Stage 1 of decode attention for bfloat16 caches on the gfx950 matrix cores.
+// Stage 1 of decode attention for bfloat16 caches (and int8 codes with per-token
+// scales, converted to bf16 on the way in) on the gfx950 matrix cores.
 //
 // One workgroup of four waves per (split, batch row, KV head).  For one 32-slot
 // code block a wave computes
@@ -22,8 +23,8 @@
 // waves of a (row, head) sweep its codes together as one moving front (DRAM rows
 // stay open), and every wave keeps the next block in flight while it computes
 // the current one (double buffering keeps the kernel at four waves per SIMD, so
-// all workgroups of a 32-split, 32-unit decode are resident at once).  Loads are raw buffer loads: a per-lane constant offset plus a scalar
-// block offset.  The first splits also take the anchor rows (token 0 and the
+// all workgroups of a 32-split, 32-unit decode are resident at once).  Loads are
+// raw buffer loads: a per-lane constant offset plus a scalar block offset.  The first splits also take the anchor rows (token 0 and the
 // recent window, full rank) in runs of at least 16; they are staged in LDS in the
 // prologue together with the group's queries and the query projection
 // q~ = U_K^T q, and wave 0 folds them in before its code blocks while the other
@@ -68,15 +69,41 @@ struct MfmaSmem {
   float o[4][LRKV_MAX_GROUP][RVMAX];        // per-wave rank-space sums
 };
 
-template <int NKC, int NVC>
+template <int NKC, int NVC, bool Q8>
 struct BlockRegs {
   u32x4 k[2][NKC];
   u32x4 v[NVC];
 };
+// int8 codes: 8 bytes per lane and operand, and the scales of the lane's 8
+// tokens 16 h2 + 4 q4 + v (keys, values)
+template <int NKC, int NVC>
+struct BlockRegs<NKC, NVC, true> {
+  u32x2 k[2][NKC];
+  u32x2 v[NVC];
+  u32x4 sk[2], sv[2];
+};
+
+// 8 int8 values (low byte first) as the 8 bf16 values of an MFMA operand: exact,
+// every integer of [-128, 127] has a bfloat16 representation
+__device__ __forceinline__ u32x4 i8x8_to_bf16(u32x2 w) {
+  auto pair = [](float a, float b) {  // the high halves of two float32 values
+    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+  };
+  u32x4 r;
+  r[0] = pair(float(int8_t(w[0])), float(int8_t(w[0] >> 8)));
+  r[1] = pair(float(int8_t(w[0] >> 16)), float(int32_t(w[0]) >> 24));
+  r[2] = pair(float(int8_t(w[1])), float(int8_t(w[1] >> 8)));
+  r[3] = pair(float(int8_t(w[1] >> 16)), float(int32_t(w[1]) >> 24));
+  return r;
+}
 
 // EXACT: every head of the layer has rank_k == RKMAX and rank_v == RVMAX, so all
 // rank tests fold at compile time; otherwise ranks are read per head (<= the max).
-template <int RKMAX, int RVMAX, bool EXACT>
+// Q8: int8 codes with a float32 scale per token (keys and values): the codes
+// enter the MFMAs converted to bf16 (exact), a score is the product times the
+// key scale, and a token's weight is multiplied by its value scale before it
+// becomes the value MFMA's A operand (the denominator keeps the plain weight).
+template <int RKMAX, int RVMAX, bool EXACT, bool Q8>
 __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d) {
   constexpr int NKC = (RKMAX + 31) / 32;  // score MFMAs per 16-token tile (K = 32 each)
   constexpr int NVC = RVMAX / 16;         // value MFMAs per block (16 columns each)
@@ -136,38 +163,61 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
     return;
   }
 
-  // this (row, head)'s key and value code regions as buffer resources
+  // this (row, head)'s key and value code regions (and int8 scales) as buffer
+  // resources; EB = bytes per code element
+  constexpr int EB = Q8 ? 1 : 2;
   const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t *>(static_cast<const bf16_t *>(L.codes_k) + hd.ck + int64_t(b) * L.cap * rk),
-      0, L.cap * rk * 2, kBufferWord3);
+      static_cast<char *>(L.codes_k) + (hd.ck + int64_t(b) * L.cap * rk) * EB, 0, L.cap * rk * EB,
+      kBufferWord3);
   const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t *>(static_cast<const bf16_t *>(L.codes_v) + hd.cv + int64_t(b) * L.cap * rv),
-      0, L.cap * rv * 2, kBufferWord3);
-  const int kblk_bytes = kBlock * rk * 2, vblk_bytes = kBlock * rv * 2;
+      static_cast<char *>(L.codes_v) + (hd.cv + int64_t(b) * L.cap * rv) * EB, 0, L.cap * rv * EB,
+      kBufferWord3);
+  __amdgpu_buffer_rsrc_t skres = kres, svres = vres;
+  if constexpr (Q8) {
+    skres = __builtin_amdgcn_make_buffer_rsrc(L.scales_k + scale_index(L, h, b, 0), 0, L.cap * 4, kBufferWord3);
+    svres = __builtin_amdgcn_make_buffer_rsrc(L.scales_v + scale_index(L, h, b, 0), 0, L.cap * 4, kBufferWord3);
+  }
+  const int kblk_bytes = kBlock * rk * EB, vblk_bytes = kBlock * rv * EB;
   int koff[2][NKC];
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       const int kg = min(4 * kc + q4, nkg - 1);  // absent groups re-read a present one, then zero
-      koff[h2][kc] = ((h2 * nkg + kg) * 16 + t16) * 16;
+      koff[h2][kc] = ((h2 * nkg + kg) * 16 + t16) * 8 * EB;
     }
   int voff[NVC];
 #pragma unroll
-  for (int ni = 0; ni < NVC; ++ni) voff[ni] = (q4 * rv + 16 * min(ni, nvt - 1) + t16) * 16;
+  for (int ni = 0; ni < NVC; ++ni) voff[ni] = (q4 * rv + 16 * min(ni, nvt - 1) + t16) * 8 * EB;
 
-  auto load = [&](int blk, BlockRegs<NKC, NVC> &r) {
+  auto load = [&](int blk, BlockRegs<NKC, NVC, Q8> &r) {
     set_priority(blk);
     // the block offsets are wave-uniform: keep them in scalar registers
     const int ks = __builtin_amdgcn_readfirstlane(blk * kblk_bytes);
     const int vs = __builtin_amdgcn_readfirstlane(blk * vblk_bytes);
+    if constexpr (Q8) {
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc)
-        r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b128(kres, koff[h2][kc], ks, 0);
+        for (int kc = 0; kc < NKC; ++kc)
+          r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b64(kres, koff[h2][kc], ks, 0);
 #pragma unroll
-    for (int ni = 0; ni < NVC; ++ni) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b128(vres, voff[ni], vs, 0);
+      for (int ni = 0; ni < NVC; ++ni) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b64(vres, voff[ni], vs, 0);
+      const int ss = __builtin_amdgcn_readfirstlane(blk * kBlock * 4);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        r.sk[h2] = __builtin_amdgcn_raw_buffer_load_b128(skres, (16 * h2 + 4 * q4) * 4, ss, 0);
+        r.sv[h2] = __builtin_amdgcn_raw_buffer_load_b128(svres, (16 * h2 + 4 * q4) * 4, ss, 0);
+      }
+    } else {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc)
+          r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b128(kres, koff[h2][kc], ks, 0);
+#pragma unroll
+      for (int ni = 0; ni < NVC; ++ni) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b128(vres, voff[ni], vs, 0);
+    }
   };
 
   // ---- prologue.  Loads are issued in this order: the operands of q~ (q and
@@ -197,7 +247,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   __builtin_amdgcn_sched_barrier(0);
   // the wave's first block (clamped to the last block; with no blocks at all
   // block 0 is read and never used, which the region bound makes harmless)
-  BlockRegs<NKC, NVC> r0, r1;
+  BlockRegs<NKC, NVC, Q8> r0, r1;
   {
     const int last = max(nblk - 1, 0);
     load(min(first, last), r0);
@@ -330,7 +380,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
 #pragma unroll
   for (int ni = 0; ni < NVC; ++ni) o[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto process = [&](int blk, BlockRegs<NKC, NVC> &r) {
+  auto process = [&](int blk, BlockRegs<NKC, NVC, Q8> &r) {
     f32x4 s[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) s[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -340,12 +390,20 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
         const u32x4 bh = sm.bq[kc][0][lane], bl = sm.bq[kc][1][lane];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          u32x4 a = r.k[h2][kc];
+          u32x4 a;
+          if constexpr (Q8) a = i8x8_to_bf16(r.k[h2][kc]);
+          else a = r.k[h2][kc];
           if (4 * kc + q4 >= nkg) a = u32x4{0u, 0u, 0u, 0u};
           s[h2] = mfma16x16x32(a, bh, s[h2]);
           s[h2] = mfma16x16x32(a, bl, s[h2]);
         }
       }
+    }
+    if constexpr (Q8) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s[h2][v] *= __uint_as_float(r.sk[h2][v]);
     }
     const int tok0 = blk * kBlock;
     if (tok0 + kBlock > c) {  // the ragged last block: mask slots >= c
@@ -353,7 +411,12 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          if (tok0 + 16 * h2 + 4 * q4 + v >= c) s[h2][v] = kNegInf;
+          if (tok0 + 16 * h2 + 4 * q4 + v >= c) {
+            s[h2][v] = kNegInf;
+            if constexpr (Q8) r.sv[h2][v] = 0u;  // int8 codes are finite: a zero weight suffices
+          }
+    }
+    if (!Q8 && tok0 + kBlock > c) {  // bf16 slots past c may hold any bits: zero them
       uint32_t keep[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -389,6 +452,10 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
       for (int ni = 0; ni < NVC; ++ni) o[ni][v] *= a;
     }
     // weights as the A operand (k-slot j = 4 h + v), hi and lo parts
+    if constexpr (Q8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] *= __uint_as_float(r.sv[j >> 2][j & 3]);
+    }
     u32x4 a_hi, a_lo;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -398,8 +465,11 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
 #pragma unroll
     for (int ni = 0; ni < NVC; ++ni) {
       if (ni < nvt) {
-        o[ni] = mfma16x16x32(a_hi, r.v[ni], o[ni]);
-        o[ni] = mfma16x16x32(a_lo, r.v[ni], o[ni]);
+        u32x4 bv;
+        if constexpr (Q8) bv = i8x8_to_bf16(r.v[ni]);
+        else bv = r.v[ni];
+        o[ni] = mfma16x16x32(a_hi, bv, o[ni]);
+        o[ni] = mfma16x16x32(a_lo, bv, o[ni]);
       }
     }
   };
@@ -481,10 +551,15 @@ static hipError_t launch_rv(const LayerArgs &L, const DecodeArgs &d, hipStream_t
   bool exact = true;
   for (int h = 0; h < L.n_kv; ++h) exact = exact && L.heads[h].rk == RKMAX && L.heads[h].rv == RVMAX;
   dim3 grid(d.n_splits, L.batch * L.n_kv);
-  if (exact)
-    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, true>), grid, dim3(256), 0, s, L, d);
+  const bool q8 = L.dtype == LRKV_BF16_Q8;
+  if (exact && q8)
+    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, true, true>), grid, dim3(256), 0, s, L, d);
+  else if (exact)
+    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, true, false>), grid, dim3(256), 0, s, L, d);
+  else if (q8)
+    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, false, true>), grid, dim3(256), 0, s, L, d);
   else
-    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, false>), grid, dim3(256), 0, s, L, d);
+    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, false, false>), grid, dim3(256), 0, s, L, d);
   return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@ struct LayerArgs {
   int32_t dtype, batch, n_q, n_kv, group, window, cap, rv_max;
   const void *bases;
   void *codes_k, *codes_v, *anchor_k, *anchor_v;
+  float *scales_k, *scales_v;  // int8 codes: one scale per (head, row, slot)
   HeadInfo heads[LRKV_MAX_KV_HEADS];
 };
 
@@ -83,6 +84,20 @@ __device__ __forceinline__ int anchor_slot(int p, int window) {
   return p == 0 ? 0 : 1 + (p - 1) % window;
 }
 
+// int8 codes: element of the scale of slot j of (KV head h, batch row b)
+__device__ __forceinline__ int64_t scale_index(const LayerArgs &L, int h, int b, int j) {
+  return (int64_t(h) * L.batch + b) * L.cap + j;
+}
+// the scale of a code row with largest magnitude a, and one quantised value:
+// x / s rounded to nearest even and clipped to [-127, 127] (float32 divisions,
+// correctly rounded); a zero row (s = 0) quantises to 0
+__device__ __forceinline__ float q8_scale(float absmax) { return absmax / 127.f; }
+__device__ __forceinline__ int q8_value(float x, float s) {
+  if (!(s > 0.f)) return 0;
+  const float t = __builtin_rintf(x / s);
+  return int(fminf(fmaxf(t, -127.f), 127.f));
+}
+
 // context length of batch row b
 __device__ __forceinline__ int row_ctx(const DecodeArgs &d, int b) {
   if (!d.ctx_lens) return d.n_ctx;
@@ -97,6 +112,8 @@ hipError_t launch_compress(const LayerArgs &L, int which, const void *x, int64_t
                            int64_t st, int n_tok, int slot0, hipStream_t s);
 hipError_t launch_compress_mfma(const LayerArgs &L, int which, const void *x, int64_t sb,
                                 int64_t sh, int64_t st, int n_tok, int slot0, hipStream_t s);
+hipError_t launch_quantize(const LayerArgs &L, int which, const float *x, int64_t sb, int64_t sh,
+                           int64_t st, int n_tok, int slot0, hipStream_t s);
 hipError_t launch_store_anchors(const LayerArgs &L, const void *k, const void *v, int64_t sb,
                                 int64_t sh, int64_t st, int pos0, int n_tok, hipStream_t s);
 hipError_t launch_append(const LayerArgs &L, const void *k, const void *v, int pos, hipStream_t s);

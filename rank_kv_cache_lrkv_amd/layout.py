@@ -53,6 +53,16 @@ def code_offsets(ranks: Sequence[int], batch: int, cap: int) -> np.ndarray:
     return np.concatenate([[0], np.cumsum(int(batch) * int(cap) * r)[:-1]]).astype(np.int64)
 
 
+def scales_elems(n_kv_heads: int, batch: int, cap: int) -> int:
+    """Elements of one int8-code scales buffer: float32 [n_kv_heads][batch][cap]."""
+    return int(n_kv_heads) * int(batch) * int(cap)
+
+
+def scale_offset(h: int, b: int, cap: int, batch: int) -> int:
+    """Element offset of slot 0 of (KV head h, batch row b) in a scales buffer."""
+    return (int(h) * int(batch) + int(b)) * int(cap)
+
+
 def block_positions(r: int, which: str) -> np.ndarray:
     """In-block element position of (slot t in 0..31, column c in 0..r-1)."""
     t = np.arange(BLOCK)[:, None]

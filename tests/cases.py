@@ -27,6 +27,18 @@ def to_storage(x, dtype: str) -> np.ndarray:
     return np.asarray(x, np.float64).astype(np.float32).astype(np.float64)
 
 
+def oracle_q8(exact) -> tuple:
+    """Int8 codes and scales of exact code rows: the float32 projection, quantised."""
+    return oracle.quantize_codes_q8(np.asarray(exact, np.float64).astype(np.float32))
+
+
+def code_storage(exact, codes: str) -> np.ndarray:
+    """The code values a cache of kind ``codes`` ("f32", "bf16" or "q8") holds."""
+    if codes == "q8":
+        return oracle.dequantize_codes_q8(*oracle_q8(exact))
+    return to_storage(exact, codes)
+
+
 @dataclass
 class HostCase:
     w: synth.Workload
@@ -40,17 +52,25 @@ class HostCase:
     v: list
     q: np.ndarray                # (batch, Hq, 128)
     layer: int = 0
+    q8: bool = False             # int8 codes with per-token scales (bf16 everything else)
+
+    @property
+    def codes_kind(self) -> str:
+        return "q8" if self.q8 else self.w.dtype
 
     @property
     def window(self):
         return self.w.window
 
-    def oracle_codes(self, b, h, which, n=None):
+    def exact_codes(self, b, h, which, n=None):
         n = self.lens[b] if n is None else n
         pos = oracle.code_positions(n, self.window)
         x = (self.k if which == "k" else self.v)[b][h][pos]
         u = (self.u_k if which == "k" else self.u_v)[h]
-        return to_storage(oracle.oracle_compress(x, u), self.w.dtype)
+        return oracle.oracle_compress(x, u)
+
+    def oracle_codes(self, b, h, which, n=None):
+        return code_storage(self.exact_codes(b, h, which, n), self.codes_kind)
 
     def oracle_anchors(self, b, h, which, n=None):
         n = self.lens[b] if n is None else n
@@ -73,7 +93,8 @@ class HostCase:
 
 
 def host_case(w: synth.Workload, n: Optional[int] = None, layer: int = 0, step: int = 0,
-              q_scale: float = 1.0, lens: Optional[List[int]] = None) -> HostCase:
+              q_scale: float = 1.0, lens: Optional[List[int]] = None, q8: bool = False) -> HostCase:
+    assert not (q8 and w.dtype != "bf16"), "int8 codes come with bf16 bases and anchors"
     n = w.n_ctx if n is None else n
     rk, rv = synth.ranks(w, layer)
     u_k = [synth.basis(w, layer, h, "k", int(rk[h])).astype(np.float64) for h in range(w.n_kv_heads)]
@@ -84,7 +105,7 @@ def host_case(w: synth.Workload, n: Optional[int] = None, layer: int = 0, step: 
          for b in range(w.batch)]
     q = np.stack([synth.queries(w, layer, step, b, q_scale) for b in range(w.batch)]).astype(np.float64)
     lens = [n] * w.batch if lens is None else list(lens)
-    return HostCase(w, n, lens, rk, rv, u_k, u_v, k, v, q, layer)
+    return HostCase(w, n, lens, rk, rv, u_k, u_v, k, v, q, layer, q8)
 
 
 # ---------------------------------------------------------------------------
@@ -109,13 +130,17 @@ def gpu_layer(hc: HostCase, cap: Optional[int] = None, with_codes: bool = True):
     cmax = max(0, hc.n - 1 - W)
     cap = layout.round_cap(cmax) if cap is None else cap
     bases = layout.pack_bases(hc.u_k, hc.u_v)
-    L = B.Layer.allocate(dtype=B.LRKV_F32 if w.dtype == "f32" else B.LRKV_BF16, batch=w.batch,
+    dtype = B.LRKV_BF16_Q8 if hc.q8 else B.LRKV_F32 if w.dtype == "f32" else B.LRKV_BF16
+    L = B.Layer.allocate(dtype=dtype, batch=w.batch,
                          n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, window=W, cap=cap,
                          rank_k=hc.rk, rank_v=hc.rv, bases=dev(bases, w.dtype))
     if not with_codes:
         return L
-    ck = np.zeros(max(1, layout.codes_elems(hc.rk, w.batch, cap)), np.float32)
-    cv = np.zeros(max(1, layout.codes_elems(hc.rv, w.batch, cap)), np.float32)
+    cdt = np.int8 if hc.q8 else np.float32
+    ck = np.zeros(max(1, layout.codes_elems(hc.rk, w.batch, cap)), cdt)
+    cv = np.zeros(max(1, layout.codes_elems(hc.rv, w.batch, cap)), cdt)
+    sk = np.zeros(max(1, layout.scales_elems(w.n_kv_heads, w.batch, cap)), np.float32)
+    sv = np.zeros_like(sk)
     ok, ov = layout.code_offsets(hc.rk, w.batch, cap), layout.code_offsets(hc.rv, w.batch, cap)
     ak = np.zeros((w.batch, w.n_kv_heads, 1 + W, D), np.float32)
     av = np.zeros_like(ak)
@@ -123,16 +148,29 @@ def gpu_layer(hc: HostCase, cap: Optional[int] = None, with_codes: bool = True):
         nb = hc.lens[b]
         apos = oracle.anchor_positions(nb, W)
         for h in range(w.n_kv_heads):
-            for which, flat, off, r in (("k", ck, ok, hc.rk), ("v", cv, ov, hc.rv)):
-                codes = hc.oracle_codes(b, h, which)
+            for which, flat, off, r, sc in (("k", ck, ok, hc.rk, sk), ("v", cv, ov, hc.rv, sv)):
                 base = off[h] + b * cap * int(r[h])
-                flat[base:base + cap * int(r[h])] = layout.pack_codes(codes.astype(np.float32), cap, which)
+                if hc.q8:
+                    q, s = oracle_q8(hc.exact_codes(b, h, which))
+                    flat[base:base + cap * int(r[h])] = layout.pack_codes(q, cap, which)
+                    s0 = layout.scale_offset(h, b, cap, w.batch)
+                    sc[s0:s0 + len(s)] = s
+                else:
+                    codes = hc.oracle_codes(b, h, which)
+                    flat[base:base + cap * int(r[h])] = layout.pack_codes(codes.astype(np.float32), cap, which)
             for p in apos:
                 s = layout.anchor_slot(int(p), W)
                 ak[b, h, s] = hc.k[b][h][p]
                 av[b, h, s] = hc.v[b][h][p]
-    L.codes_k.copy_(dev(ck, w.dtype))
-    L.codes_v.copy_(dev(cv, w.dtype))
+    if hc.q8:
+        import torch
+        L.codes_k.copy_(torch.from_numpy(ck).cuda())
+        L.codes_v.copy_(torch.from_numpy(cv).cuda())
+        L.scales_k.copy_(torch.from_numpy(sk).cuda())
+        L.scales_v.copy_(torch.from_numpy(sv).cuda())
+    else:
+        L.codes_k.copy_(dev(ck, w.dtype))
+        L.codes_v.copy_(dev(cv, w.dtype))
     L.anchor_k.copy_(dev(ak, w.dtype))
     L.anchor_v.copy_(dev(av, w.dtype))
     return L
@@ -163,8 +201,8 @@ def abs_err(got, want) -> float:
 
 
 def check_decode(got, want, dtype: str, label: str):
-    """The parity bar: float32 storage max abs error <= 1e-5; bf16 codes with
-    float32 accumulation max abs error <= 2e-3 of max |out|."""
+    """The parity bar: float32 storage max abs error <= 1e-5; bf16 (or int8)
+    codes with float32 accumulation max abs error <= 2e-3 of max |out|."""
     assert not np.any(np.isnan(got[~np.isnan(want)])), f"{label}: NaN in GPU output"
     if dtype == "f32":
         e = abs_err(got, want)

@@ -54,7 +54,8 @@ def layer(**kw):
                      ctypes.cast(rk, ctypes.POINTER(ctypes.c_int32)),
                      ctypes.cast(rv, ctypes.POINTER(ctypes.c_int32)),
                      d.get("bases", FAKE), d.get("codes_k", FAKE), d.get("codes_v", FAKE),
-                     d.get("anchor_k", FAKE), d.get("anchor_v", FAKE))
+                     d.get("anchor_k", FAKE), d.get("anchor_v", FAKE),
+                     d.get("scales_k", FAKE), d.get("scales_v", FAKE))
     s._keep = (rk, rv)
     return s
 
@@ -66,6 +67,7 @@ def decode(L, n_ctx=50, q=FAKE, out=FAKE, scale=0.088, S=2, ws=FAKE, ws_bytes=1 
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=7), 4),
     (dict(batch=0), 2),
+    (dict(batch=32768), 2),                                     # 65536 (row, head) units
     (dict(n_q_heads=7), 2),
     (dict(n_q_heads=2 * 17, n_kv_heads=2), 2),
     (dict(window=-1), 2),
@@ -78,6 +80,9 @@ def decode(L, n_ctx=50, q=FAKE, out=FAKE, scale=0.088, S=2, ws=FAKE, ws_bytes=1 
     (dict(bases=None), 1),
     (dict(codes_v=None), 1),
     (dict(anchor_k=FAKE + 8), 5),
+    (dict(dtype=2, scales_k=None), 1),                          # int8 codes need their scales
+    (dict(dtype=2, scales_v=FAKE + 4), 5),
+    (dict(dtype=2, cap=(1 << 31) // 256 // 32 * 32 + 32), 2),
 ])
 def test_layer_validation(kw, status):
     assert decode(layer(**kw)) == status
@@ -152,3 +157,30 @@ def test_store_and_append_validation():
     L0 = layer(window=0)
     assert lib.lrkv_store_anchors(ctypes.byref(L0), FAKE, FAKE, 1024, 512, 128, 1, 1, None) == 2
     assert lib.lrkv_append(ctypes.byref(L0), FAKE, FAKE, 65, None) == 6
+
+
+def test_scales_ignored_unless_int8():
+    # bf16 and f32 layers never read the scale pointers: null is fine
+    L = layer(scales_k=None, scales_v=None)
+    assert decode(L, q=None) == 1     # fails on q, not on the scales
+    L8 = layer(dtype=2)
+    assert decode(L8, q=None) == 1
+
+
+def test_quantize_validation():
+    lib = B.lib()
+    L8 = layer(dtype=2)
+    f = lambda L=L8, **k: lib.lrkv_quantize(ctypes.byref(L), k.get("which", 0), k.get("x", FAKE),
+                                           k.get("sb", 1024), k.get("sh", 512), k.get("st", 65),
+                                           k.get("n", 10), k.get("slot0", 0), None)
+    assert f(L=layer(dtype=1)) == 4      # only int8-code layers
+    assert f(L=layer(dtype=0)) == 4
+    assert f(which=2) == 2
+    assert f(n=-1) == 2
+    assert f(slot0=-1) == 2
+    assert f(n=60, slot0=5) == 6
+    assert f(n=0, x=None) == 0           # empty range is a no-op
+    assert f(x=None) == 1
+    assert f(sh=-512) == 2
+    assert f(x=FAKE + 2) == 5            # float32 rows need 4-byte alignment only
+    assert f(L=layer(dtype=2, scales_v=None)) == 1
