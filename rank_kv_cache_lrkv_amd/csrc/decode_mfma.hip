@@ -74,14 +74,33 @@ struct BlockRegs {
   u32x4 k[2][NKC];
   u32x4 v[NVC];
 };
-// int8 codes: 8 bytes per lane and operand, and the scales of the lane's 8
-// tokens 16 h2 + 4 q4 + v (keys, values)
+// int8 codes: 8 bytes per lane and operand, and one key and one value scale per
+// lane: lane (q4, t16) of the 16-lane row q4 holds those of token
+// 16 ((t16 >> 2) & 1) + 4 q4 + (t16 & 3), so lanes 0 .. 7 of the row hold the
+// row's 8 tokens 16 h2 + 4 q4 + v in the order 4 h2 + v
 template <int NKC, int NVC>
 struct BlockRegs<NKC, NVC, true> {
   u32x2 k[2][NKC];
   u32x2 v[NVC];
-  u32x4 sk[2], sv[2];
+  uint32_t sk, sv;
 };
+
+// lane N of this lane's 16-lane row (DPP row_newbcast)
+template <int N>
+__device__ __forceinline__ float row_lane(uint32_t x) {
+  return __uint_as_float(uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x150 + N, 0xf, 0xf, false)));
+}
+// the 8 scales of the row's tokens, in the order 4 h2 + v
+__device__ __forceinline__ void row_scales(uint32_t x, float (&o)[8]) {
+  o[0] = row_lane<0>(x);
+  o[1] = row_lane<1>(x);
+  o[2] = row_lane<2>(x);
+  o[3] = row_lane<3>(x);
+  o[4] = row_lane<4>(x);
+  o[5] = row_lane<5>(x);
+  o[6] = row_lane<6>(x);
+  o[7] = row_lane<7>(x);
+}
 
 // 8 int8 values (low byte first) as the 8 bf16 values of an MFMA operand: exact,
 // every integer of [-128, 127] has a bfloat16 representation
@@ -177,6 +196,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
     skres = __builtin_amdgcn_make_buffer_rsrc(L.scales_k + scale_index(L, h, b, 0), 0, L.cap * 4, kBufferWord3);
     svres = __builtin_amdgcn_make_buffer_rsrc(L.scales_v + scale_index(L, h, b, 0), 0, L.cap * 4, kBufferWord3);
   }
+  const int soff = (16 * ((t16 >> 2) & 1) + 4 * q4 + (t16 & 3)) * 4;  // this lane's scale in a block
   const int kblk_bytes = kBlock * rk * EB, vblk_bytes = kBlock * rv * EB;
   int koff[2][NKC];
 #pragma unroll
@@ -204,11 +224,8 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
 #pragma unroll
       for (int ni = 0; ni < NVC; ++ni) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b64(vres, voff[ni], vs, 0);
       const int ss = __builtin_amdgcn_readfirstlane(blk * kBlock * 4);
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        r.sk[h2] = __builtin_amdgcn_raw_buffer_load_b128(skres, (16 * h2 + 4 * q4) * 4, ss, 0);
-        r.sv[h2] = __builtin_amdgcn_raw_buffer_load_b128(svres, (16 * h2 + 4 * q4) * 4, ss, 0);
-      }
+      r.sk = __builtin_amdgcn_raw_buffer_load_b32(skres, soff, ss, 0);
+      r.sv = __builtin_amdgcn_raw_buffer_load_b32(svres, soff, ss, 0);
     } else {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
@@ -400,21 +417,21 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
       }
     }
     if constexpr (Q8) {
+      float ksc[8];
+      row_scales(r.sk, ksc);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) s[h2][v] *= __uint_as_float(r.sk[h2][v]);
+        for (int v = 0; v < 4; ++v) s[h2][v] *= ksc[4 * h2 + v];
     }
     const int tok0 = blk * kBlock;
-    if (tok0 + kBlock > c) {  // the ragged last block: mask slots >= c
+    const bool ragged = tok0 + kBlock > c;
+    if (ragged) {  // the ragged last block: mask slots >= c
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          if (tok0 + 16 * h2 + 4 * q4 + v >= c) {
-            s[h2][v] = kNegInf;
-            if constexpr (Q8) r.sv[h2][v] = 0u;  // int8 codes are finite: a zero weight suffices
-          }
+          if (tok0 + 16 * h2 + 4 * q4 + v >= c) s[h2][v] = kNegInf;
     }
     if (!Q8 && tok0 + kBlock > c) {  // bf16 slots past c may hold any bits: zero them
       uint32_t keep[4];
@@ -436,6 +453,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
     bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
     bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
     const float mn = fmaxf(m_run, bm);  // finite: a block holds at least one slot < c
+    const float m_prev = m_run;
     const float alpha = fast_exp2(m_run - mn);
     // lanes of absent heads (t16 >= G) score 0 against zero queries: their weights
     // stay finite and only feed accumulator rows that are never read
@@ -444,17 +462,27 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
     for (int j = 0; j < 8; ++j) p[j] = fast_exp2(s[j >> 2][j & 3] - mn);
     l_run = l_run * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
     m_run = mn;
-    // rescale the sums: lane (q4, t16) holds heads 4 q4 + v
+    // rescale the sums (lane (q4, t16) holds heads 4 q4 + v) unless no head's
+    // maximum moved: then every factor is exactly 1
+    if (__builtin_amdgcn_ballot_w64(mn != m_prev) != 0) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float a = __shfl(alpha, 4 * q4 + v, 64);
+      for (int v = 0; v < 4; ++v) {
+        const float a = __shfl(alpha, 4 * q4 + v, 64);
 #pragma unroll
-      for (int ni = 0; ni < NVC; ++ni) o[ni][v] *= a;
+        for (int ni = 0; ni < NVC; ++ni) o[ni][v] *= a;
+      }
     }
     // weights as the A operand (k-slot j = 4 h + v), hi and lo parts
     if constexpr (Q8) {
+      float vsc[8];
+      row_scales(r.sv, vsc);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) p[j] *= __uint_as_float(r.sv[j >> 2][j & 3]);
+      for (int j = 0; j < 8; ++j) p[j] *= vsc[j];
+      if (ragged) {  // slots past c: weight 0 whatever their scale holds (int8 codes are finite)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (tok0 + 16 * (j >> 2) + 4 * q4 + (j & 3) >= c) p[j] = 0.f;
+      }
     }
     u32x4 a_hi, a_lo;
 #pragma unroll
@@ -474,15 +502,19 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
     }
   };
 
-  // double-buffered sweep
+  // double-buffered sweep.  The scheduling barriers keep the next block's loads
+  // ahead of the current block's work: hoisting that work above them would make
+  // the wave wait for the current block with nothing else in flight.
   int j = first;
   if (j < nblk) {
     while (true) {
       load(j + step < nblk ? j + step : j, r1);
+      __builtin_amdgcn_sched_barrier(0);
       process(j, r0);
       j += step;
       if (j >= nblk) break;
       load(j + step < nblk ? j + step : j, r0);
+      __builtin_amdgcn_sched_barrier(0);
       process(j, r1);
       j += step;
       if (j >= nblk) break;
