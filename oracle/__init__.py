@@ -12,12 +12,14 @@ from .lrkv_oracle import (  # noqa: F401
     code_scores,
     compressed_unit_bytes,
     default_scale,
+    dequantize_codes_q4,
     dequantize_codes_q8,
     full_kv_bytes,
     oracle_compress,
     oracle_decode_layer,
     oracle_decode_unit,
     project_query,
+    quantize_codes_q4,
     quantize_codes_q8,
     rank_space_values,
     softmax_weights,

@@ -28,9 +28,10 @@ Readings where the pages are silent (each also listed in the design doc):
 * query head i of a GQA group reads KV head i // g;
 * codes are ``x @ U`` with U a (128, r) matrix with orthonormal columns.
 
-Int8 codes (the first step past the pages: they name quantisation of the
-low-rank cache but no quantiser) follow a stated design, symmetric with one
-float32 scale per code row, decided in float32; see quantize_codes_q8.
+Int8 and int4 codes (the first step past the pages: they name quantisation of
+the low-rank cache but no quantiser) follow a stated design, symmetric with one
+float32 scale per code row, decided in float32; see quantize_codes_q8 and
+quantize_codes_q4.
 
 Pins (tests/test_oracle.py): full attention at r = d with an orthogonal basis
 (the blog's section 04 plumbing check), brute-force reconstruction on tiny
@@ -214,6 +215,30 @@ def dequantize_codes_q8(q, s) -> np.ndarray:
     return np.asarray(q, np.float64) * np.asarray(s, np.float64)[:, None]
 
 
+def quantize_codes_q4(x32) -> tuple:
+    """Quantise code rows ``x32`` (t, r), given as float32, to 4-bit integers.
+
+    The int8 rule with 7 in place of 127: per row, in float32, a = max |x|,
+    s = a / 7, q = x / s rounded to nearest, ties to even, clipped to [-7, 7]; a
+    row of zeros gets s = 0 and q = 0.  Returns (q int8 holding values in [-7, 7]
+    (t, r), s float32 (t,))."""
+    x = np.asarray(x32, dtype=np.float32)
+    if x.ndim != 2:
+        raise ValueError("x32 must be (t, r)")
+    a = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    s = (a / np.float32(7)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1)).astype(np.float32)
+    q = np.rint(x / safe[:, None])
+    q = np.clip(q, -7, 7)
+    q[s == 0] = 0
+    return q.astype(np.int8), s
+
+
+def dequantize_codes_q4(q, s) -> np.ndarray:
+    """The codes a 4-bit row stands for: s * q, exact in float64."""
+    return np.asarray(q, np.float64) * np.asarray(s, np.float64)[:, None]
+
+
 # ---------------------------------------------------------------------------
 # byte accounting (OjaKV FAQ: ~16 GB of KV for Llama-3.1-8B, 32K tokens, batch 4;
 # blog section 08: the per-request cache shrinks with the code width, plus the
@@ -227,11 +252,15 @@ def full_kv_bytes(n_layers: int, n_kv_heads: int, n_tokens: int, batch: int,
 
 
 def compressed_unit_bytes(n: int, window: int, r_k: int, r_v: int, elem_bytes: int = 2,
-                          head_dim: int = HEAD_DIM, q8: bool = False) -> int:
+                          head_dim: int = HEAD_DIM, q8: bool = False, q4: bool = False) -> int:
     """Bytes one decode step must read for one (batch row, KV head): the codes of
     the compressed tokens plus the full-rank anchors.  With int8 codes each code
-    row is r bytes plus its 4-byte scale; anchors stay at ``elem_bytes``."""
+    row is r bytes plus its 4-byte scale, with 4-bit codes r / 2 bytes plus the
+    scale; anchors stay at ``elem_bytes``."""
     c = len(code_positions(n, window))
     a = len(anchor_positions(n, window))
-    code_bytes = (r_k + r_v + 8) if q8 else (r_k + r_v) * elem_bytes
+    if q4:
+        code_bytes = (r_k + r_v) // 2 + 8
+    else:
+        code_bytes = (r_k + r_v + 8) if q8 else (r_k + r_v) * elem_bytes
     return c * code_bytes + a * 2 * head_dim * elem_bytes

@@ -318,7 +318,6 @@ def pin_payload_ratios_blog():
     assert oracle.compressed_unit_bytes(50, 64, 32, 16) == 50 * full
 
 
-ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
 def pin_q8_hand_examples():
@@ -356,6 +355,46 @@ def pin_q8_unit_bytes():
     c, a = len(oracle.code_positions(n, w)), len(oracle.anchor_positions(n, w))
     assert oracle.compressed_unit_bytes(n, w, 64, 32, q8=True) == c * 104 + a * 512
     assert oracle.compressed_unit_bytes(n, w, 64, 32) == c * 192 + a * 512
+
+
+def pin_q4_hand_examples():
+    """4-bit rows whose scale is a power of two: halves go to the even integer,
+    the extremes land on +-7."""
+    x = np.array([[7.0, -3.5, 0.25, 0.0, 2.5], [14.0, 1.0, -3.0, 5.0, -14.0]], np.float32)
+    q, s = oracle.quantize_codes_q4(x)
+    assert s.tolist() == [1.0, 2.0], s
+    assert q[0].tolist() == [7, -4, 0, 0, 2], q[0]
+    assert q[1].tolist() == [7, 0, -2, 2, -7], q[1]
+
+
+def pin_q4_invariants():
+    """As for int8 with 7 steps: the largest entry of a non-zero row is +-7,
+    every entry within half a step, signs kept, zero rows zero, powers of two
+    move into the scale only; and a 4-bit code is never finer than the int8 one."""
+    rng = np.random.default_rng(22)
+    x = (rng.standard_normal((200, 48)) * rng.uniform(0.01, 50, (200, 1))).astype(np.float32)
+    x[3] = 0
+    q, s = oracle.quantize_codes_q4(x)
+    assert s[3] == 0 and not q[3].any()
+    nz = s > 0
+    assert np.all(np.abs(q[nz].astype(int)).max(axis=1) == 7)
+    assert np.all(np.abs(q.astype(int)) <= 7)
+    err = np.abs(oracle.dequantize_codes_q4(q, s) - x.astype(np.float64))
+    assert np.all(err <= (0.5 + 1e-5) * s.astype(np.float64)[:, None])
+    assert np.all((np.sign(q) == np.sign(x)) | (q == 0))
+    q2, s2 = oracle.quantize_codes_q4(x * np.float32(4))
+    assert np.array_equal(q2, q) and np.array_equal(s2, s * np.float32(4))
+    q8, s8 = oracle.quantize_codes_q8(x)
+    e8 = np.abs(oracle.dequantize_codes_q8(q8, s8) - x.astype(np.float64)).max()
+    assert e8 < err.max()
+
+
+def pin_q4_unit_bytes():
+    """A 4-bit code row is r / 2 bytes plus a 4-byte scale: 56 bytes per
+    compressed token per KV head at r 64/32."""
+    n, w = 1000, 16
+    c, a = len(oracle.code_positions(n, w)), len(oracle.anchor_positions(n, w))
+    assert oracle.compressed_unit_bytes(n, w, 64, 32, q4=True) == c * 56 + a * 512
 
 
 def pin_layer_gqa_sdpa():

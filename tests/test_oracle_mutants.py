@@ -47,16 +47,19 @@ MUTANTS = {
     "q8_ties_away_from_zero": ("quantize_codes_q8", lambda x: _q8_variant(x, rounding="away")),
     "q8_scale_over_128": ("quantize_codes_q8", lambda x: _q8_variant(x, divisor=128)),
     "q8_divisor_127_5": ("quantize_codes_q8", lambda x: _q8_variant(x, divisor=127.5)),
+    "q4_ties_away_from_zero": ("quantize_codes_q4", lambda x: _q8_variant(x, rounding="away", divisor=7, qmax=7)),
+    "q4_scale_over_8": ("quantize_codes_q4", lambda x: _q8_variant(x, divisor=8, qmax=7)),
+    "q4_clip_at_8": ("quantize_codes_q4", lambda x: _q8_variant(x, divisor=7.5, qmax=8)),
 }
 
 
-def _q8_variant(x, rounding="even", divisor=127):
+def _q8_variant(x, rounding="even", divisor=127, qmax=127):
     x = np.asarray(x, np.float32)
     s = (np.max(np.abs(x), axis=1) / np.float32(divisor)).astype(np.float32)
     safe = np.where(s > 0, s, np.float32(1)).astype(np.float32)
     t = x / safe[:, None]
     qf = np.sign(t) * np.floor(np.abs(t) + 0.5) if rounding == "away" else np.rint(t)
-    q = np.clip(qf, -127, 127)
+    q = np.clip(qf, -qmax, qmax)
     q[s == 0] = 0
     return q.astype(np.int8), s
 
