@@ -14,8 +14,9 @@ Prints one JSON line: tokens*heads/s of whole calls, the roofline of the
 dominant kernel (its algorithmic bytes over its event-timed duration) and the
 CPU oracle timed on a bounded sample of the same workload.
 
-``--codes int8`` runs the same workload with int8 codes and per-token float32
-scales (bf16 bases, anchors and queries) instead of bf16 codes.
+``--codes int8`` / ``--codes int4`` run the same workload with int8 or 4-bit
+codes and per-token float32 scales (bf16 bases, anchors and queries) instead of
+bf16 codes.
 """
 
 from __future__ import annotations
@@ -47,16 +48,19 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, n, int8=False):
+def algorithmic_bytes(w, n, bits=16):
     """Bytes the method must move for one decode call of one layer, and the part
-    the partials kernel moves (codes, anchors, U_K, q).  Int8 codes: r bytes per
-    code row plus its 4-byte scale."""
+    the partials kernel moves (codes, anchors, U_K, q).  Quantised codes: r bytes
+    (int8) or r / 2 bytes (4-bit) per code row plus its 4-byte scale."""
     import oracle
     s = 4 if w.dtype == "f32" else 2
     c = len(oracle.code_positions(n, w.window))
     a = len(oracle.anchor_positions(n, w.window))
     units = w.batch * w.n_kv_heads
-    codes = units * c * ((w.rank_k + w.rank_v + 8) if int8 else (w.rank_k + w.rank_v) * s)
+    if bits < 16:
+        codes = units * c * ((w.rank_k + w.rank_v) * bits // 8 + 8)
+    else:
+        codes = units * c * (w.rank_k + w.rank_v) * s
     anchors = units * a * 2 * 128 * s
     u_k = w.n_kv_heads * 128 * w.rank_k * s
     u_v = w.n_kv_heads * 128 * w.rank_v * s
@@ -66,7 +70,7 @@ def algorithmic_bytes(w, n, int8=False):
             "codes": codes, "anchors": anchors}
 
 
-def build_cache(w, B, dev, int8=False):
+def build_cache(w, B, dev, bits=16):
     """Prefill on the GPU: compress tokens 1..n-W-1, store token 0 and the window."""
     import numpy as np
     import torch
@@ -79,7 +83,7 @@ def build_cache(w, B, dev, int8=False):
                               [synth.basis(w, 0, h, "v", int(rv[h])) for h in range(w.n_kv_heads)])
     n = w.n_ctx
     c = max(0, n - 1 - w.window)
-    dtype = B.LRKV_BF16_Q8 if int8 else B.LRKV_BF16 if w.dtype == "bf16" else B.LRKV_F32
+    dtype = {8: B.LRKV_BF16_Q8, 4: B.LRKV_BF16_Q4}.get(bits, B.LRKV_BF16 if w.dtype == "bf16" else B.LRKV_F32)
     L = B.Layer.allocate(dtype=dtype, batch=w.batch,
                          n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, window=w.window,
                          cap=layout.round_cap(c), rank_k=rk, rank_v=rv, bases=dev(bases))
@@ -103,7 +107,7 @@ def build_cache(w, B, dev, int8=False):
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[1])
     s = 2 if w.dtype == "bf16" else 4
-    row = (2 * 128 * s + w.rank_k + w.rank_v + 8) if int8 else (2 * 128 + w.rank_k + w.rank_v) * s
+    row = (2 * 128 * s + (w.rank_k + w.rank_v) * bits // 8 + 8) if bits < 16 else (2 * 128 + w.rank_k + w.rank_v) * s
     moved = w.batch * w.n_kv_heads * c * row
     compress = {"ms": round(ms, 4), "tokens": c, "alg_bytes": moved,
                 "gbps": round(moved / (ms * 1e-3) / 1e9, 1)}
@@ -168,11 +172,11 @@ def cpu_baseline(w, seconds):
                       f"(code preparation untimed)"}
 
 
-def traffic_from_profile(source_hash, int8=False):
+def traffic_from_profile(source_hash, codes="bf16"):
     """HBM traffic per launch of the dominant kernel, from the committed counter
     summary, if it was taken on the current kernel source."""
-    name = "decode_partials_llama31_8b_32k_int8_traffic.json" if int8 else \
-        "decode_partials_llama31_8b_32k_traffic.json"
+    name = "decode_partials_llama31_8b_32k_traffic.json" if codes == "bf16" else \
+        f"decode_partials_llama31_8b_32k_{codes}_traffic.json"
     p = os.path.join(ROOT, "profiles", name)
     try:
         d = json.load(open(p))
@@ -189,8 +193,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama31_8b_32k")
-    ap.add_argument("--codes", choices=("bf16", "int8"), default="bf16",
-                    help="code storage (bf16 workloads): bf16, or int8 with per-token scales")
+    ap.add_argument("--codes", choices=("bf16", "int8", "int4"), default="bf16",
+                    help="code storage (bf16 workloads): bf16, or int8 / int4 with per-token scales")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated (0: >= 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -230,12 +234,12 @@ def main():
     log(f"workload {w.name}: batch {w.batch}, heads {w.n_q_heads}/{w.n_kv_heads}, n {w.n_ctx}, "
         f"ranks {w.rank_k}/{w.rank_v}, window {w.window}")
     t0 = time.time()
-    int8 = args.codes == "int8"
-    assert not (int8 and w.dtype != "bf16"), "int8 codes are for the bf16 workloads"
-    L0, compress = build_cache(w, B, dev, int8)
+    bits = {"bf16": 16, "int8": 8, "int4": 4}[args.codes]
+    assert not (bits < 16 and w.dtype != "bf16"), "quantised codes are for the bf16 workloads"
+    L0, compress = build_cache(w, B, dev, bits)
     log(f"cache built and compressed on the GPU in {time.time() - t0:.1f} s "
         f"(compress {compress['ms']:.3f} ms, {compress['gbps']} GB/s)")
-    nb = algorithmic_bytes(w, w.n_ctx, int8)
+    nb = algorithmic_bytes(w, w.n_ctx, bits)
     R = args.replicas or max(1, math.ceil((1 << 30) / nb["call"]))
     layers = [L0] + [replicate(L0, B) for _ in range(R - 1)]
     n = w.n_ctx
@@ -280,12 +284,12 @@ def main():
     t_call = ms_per_step * 1e-3
     value = w.batch * w.n_q_heads * n / t_call
     kernel = DOMINANT_KERNEL if w.dtype == "bf16" else "k_partials_generic (stage 1)"
-    if int8:
-        kernel = "k_partials_mfma, int8 codes (stage 1: code splits + anchors)"
+    if bits < 16:
+        kernel = f"k_partials_mfma, {args.codes} codes (stage 1: code splits + anchors)"
     k_bytes = nb["partials"]
     achieved = k_bytes / (k_ms * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    traffic = traffic_from_profile(src_hash, int8)
+    traffic = traffic_from_profile(src_hash, args.codes)
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")

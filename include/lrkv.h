@@ -51,8 +51,9 @@ typedef enum lrkv_status {
 typedef enum lrkv_dtype {
   LRKV_F32 = 0,     /* float32 storage and float32 arithmetic */
   LRKV_BF16 = 1,    /* bfloat16 storage, float32 accumulation */
-  LRKV_BF16_Q8 = 2  /* bfloat16 bases, anchors, queries and compress/append inputs;
+  LRKV_BF16_Q8 = 2, /* bfloat16 bases, anchors, queries and compress/append inputs;
                        int8 codes with one float32 scale per code slot (see below) */
+  LRKV_BF16_Q4 = 3  /* as LRKV_BF16_Q8 with 4-bit codes, two per byte (see below) */
 } lrkv_dtype;
 
 #define LRKV_HEAD_DIM 128
@@ -99,6 +100,12 @@ typedef enum lrkv_dtype {
  * one-byte elements; the scales are float32:
  *   scales_k, scales_v (device): slot j of batch row b, KV head h at element
  *   (h * batch + b) * cap + j.
+ *
+ * 4-bit codes (dtype LRKV_BF16_Q4): the same rule with 7 in place of 127
+ * (s = max_c |x_c| / 7, q in [-7, 7]), the same scales.  Element position p of
+ * the blocked layout above sits in byte p / 2 of the region, in the low four
+ * bits for even p and the high four bits for odd p, two's complement; a
+ * (row, head) region of r-column codes is cap * r / 2 bytes.
  */
 typedef struct lrkv_layer {
   int32_t dtype;          /* lrkv_dtype */
@@ -115,8 +122,8 @@ typedef struct lrkv_layer {
   void *codes_v;          /* device */
   void *anchor_k;         /* device [batch][n_kv_heads][1 + window][128] */
   void *anchor_v;         /* device */
-  float *scales_k;        /* device, LRKV_BF16_Q8 only (may be NULL otherwise) */
-  float *scales_v;        /* device, LRKV_BF16_Q8 only */
+  float *scales_k;        /* device, LRKV_BF16_Q8 and _Q4 only (may be NULL otherwise) */
+  float *scales_v;        /* device, LRKV_BF16_Q8 and _Q4 only */
 } lrkv_layer;
 
 /*
@@ -124,8 +131,8 @@ typedef struct lrkv_layer {
  * after RoPE).  For every (batch row b, KV head h) and t in [0, n_tok): code slot
  * slot0 + t of `which` (0 = keys with U_K, 1 = values with U_V) receives
  * x[b, h, t, :] U, rounded to the storage type (bf16: round to nearest even of
- * the float32 accumulation; LRKV_BF16_Q8: the float32 accumulation quantised to
- * int8 with its scale, as described above).
+ * the float32 accumulation; LRKV_BF16_Q8 / _Q4: the float32 accumulation
+ * quantised to int8 / 4 bits with its scale, as described above).
  *   x: device, element (b, h, t, i) at x + b*stride_b + h*stride_h + t*stride_t + i
  *      (strides in elements of the storage type; the 128 features contiguous).
  * Errors: LRKV_ERR_SHAPE if n_tok < 0, slot0 < 0 or a stride is negative;
@@ -137,8 +144,9 @@ lrkv_status lrkv_compress(const lrkv_layer *L, int32_t which, const void *x,
                           int32_t n_tok, int32_t slot0, lrkv_stream_t stream);
 
 /*
- * The int8 step of lrkv_compress on given float32 code rows (LRKV_BF16_Q8 layers
- * only): slot slot0 + t of head h, row b receives the quantisation of
+ * The quantising step of lrkv_compress on given float32 code rows (LRKV_BF16_Q8
+ * and LRKV_BF16_Q4 layers only): slot slot0 + t of head h, row b receives the
+ * quantisation of
  * x[b, h, t, 0 .. r-1] (r = the head's rank for `which`) and its scale.
  *   x: device float32, element (b, h, t, c) at x + b*stride_b + h*stride_h + t*stride_t + c.
  * Errors: LRKV_ERR_DTYPE for other layer types; otherwise as lrkv_compress
@@ -165,8 +173,8 @@ lrkv_status lrkv_store_anchors(const lrkv_layer *L, const void *k, const void *v
  * Cache maintenance of one decode step, the same for every batch row: the new
  * token at position `pos` (k_new, v_new: device [batch][n_kv_heads][128]).
  *  - window >= 1 and pos > window: token pos - window leaves the window; its anchor
- *    slot is compressed into code slot pos - window - 1 (keys and values; int8 with
- *    its scale for LRKV_BF16_Q8), then the new token takes over that slot.
+ *    slot is compressed into code slot pos - window - 1 (keys and values; quantised
+ *    with its scale for LRKV_BF16_Q8 / _Q4), then the new token takes over that slot.
  *  - window == 0 and pos >= 1: the new token is compressed into code slot pos - 1.
  *  - otherwise the new token is stored into its anchor slot.
  * Errors: LRKV_ERR_SHAPE if pos < 0; LRKV_ERR_CAPACITY if the code slot >= cap.
@@ -182,7 +190,8 @@ lrkv_status lrkv_append(const lrkv_layer *L, const void *k_new, const void *v_ne
  *   1 .. n_ctx - window - 1 and need cap >= max(0, n_ctx - 1 - window).
  * ctx_lens: optional device int32 [batch] of per-row lengths (ragged batches);
  *   each is clamped into [1, n_ctx].  NULL: every row has n_ctx tokens.
- * q: device [batch][n_q_heads][128] in the storage type (bfloat16 for LRKV_BF16_Q8).
+ * q: device [batch][n_q_heads][128] in the storage type (bfloat16 for the
+ *    quantised-code types).
  * sm_scale: score scale, normally 1/sqrt(128).
  * n_splits: the compressed tokens of each (row, KV head) are cut into this many
  *   contiguous ranges of 32-slot blocks, each scored by its own workgroup

@@ -22,7 +22,8 @@ from . import layout
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblrkv.so")
 
-LRKV_F32, LRKV_BF16, LRKV_BF16_Q8 = 0, 1, 2
+LRKV_F32, LRKV_BF16, LRKV_BF16_Q8, LRKV_BF16_Q4 = 0, 1, 2, 3
+QUANTISED = (LRKV_BF16_Q8, LRKV_BF16_Q4)
 HEAD_DIM = 128
 BLOCK = 32
 
@@ -135,7 +136,7 @@ class Layer:
     codes_v: "object"
     anchor_k: "object"
     anchor_v: "object"
-    scales_k: "object" = None  # int8 codes only: float32 [n_kv_heads][batch][cap]
+    scales_k: "object" = None  # quantised codes only: float32 [n_kv_heads][batch][cap]
     scales_v: "object" = None
     _rk: object = field(default=None, repr=False)
     _rv: object = field(default=None, repr=False)
@@ -162,7 +163,10 @@ class Layer:
 
     @property
     def code_dtype(self):
+        """Element type of the codes tensors (4-bit codes: uint8 bytes, two per byte)."""
         import torch
+        if self.dtype == LRKV_BF16_Q4:
+            return torch.uint8
         return torch.int8 if self.dtype == LRKV_BF16_Q8 else self.torch_dtype
 
     @classmethod
@@ -173,7 +177,8 @@ class Layer:
         geometry.  ``bases`` (optional) is the flat bases tensor; otherwise zeros."""
         import torch
         td = torch.float32 if dtype == LRKV_F32 else torch.bfloat16
-        cd = torch.int8 if dtype == LRKV_BF16_Q8 else td
+        cd = {LRKV_BF16_Q8: torch.int8, LRKV_BF16_Q4: torch.uint8}.get(dtype, td)
+        per = 2 if dtype == LRKV_BF16_Q4 else 1  # code elements per tensor element
         rk = np.asarray(rank_k, np.int32)
         rv = np.asarray(rank_v, np.int32)
         cap = layout.round_cap(cap)
@@ -181,12 +186,12 @@ class Layer:
         if bases is None:
             bases = torch.zeros(nb, dtype=td, device=device)
         assert bases.numel() == nb and bases.dtype == td
-        ck = torch.zeros(max(1, layout.codes_elems(rk, batch, cap)), dtype=cd, device=device)
-        cv = torch.zeros(max(1, layout.codes_elems(rv, batch, cap)), dtype=cd, device=device)
+        ck = torch.zeros(max(1, layout.codes_elems(rk, batch, cap) // per), dtype=cd, device=device)
+        cv = torch.zeros(max(1, layout.codes_elems(rv, batch, cap) // per), dtype=cd, device=device)
         ak = torch.zeros((batch, n_kv_heads, 1 + window, HEAD_DIM), dtype=td, device=device)
         av = torch.zeros_like(ak)
         sk = sv = None
-        if dtype == LRKV_BF16_Q8:
+        if dtype in QUANTISED:
             sk = torch.zeros(max(1, layout.scales_elems(n_kv_heads, batch, cap)), dtype=torch.float32,
                              device=device)
             sv = torch.zeros_like(sk)

@@ -12,11 +12,14 @@ namespace {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool valid_rank(int32_t r) { return r >= 16 && r <= 128 && r % 16 == 0; }
 int elem_bytes(int32_t dtype) { return dtype == LRKV_F32 ? 4 : 2; }
+bool quantised(int32_t dtype) { return dtype == LRKV_BF16_Q8 || dtype == LRKV_BF16_Q4; }
 
 // Checks the layer description and fills the kernel-side copy.
 lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   if (!L) return LRKV_ERR_NULL;
-  if (L->dtype != LRKV_F32 && L->dtype != LRKV_BF16 && L->dtype != LRKV_BF16_Q8) return LRKV_ERR_DTYPE;
+  if (L->dtype != LRKV_F32 && L->dtype != LRKV_BF16 && L->dtype != LRKV_BF16_Q8 &&
+      L->dtype != LRKV_BF16_Q4)
+    return LRKV_ERR_DTYPE;
   if (L->batch < 1 || L->n_kv_heads < 1 || L->n_kv_heads > LRKV_MAX_KV_HEADS) return LRKV_ERR_SHAPE;
   // (row, head) units are the second launch dimension
   if (int64_t(L->batch) * L->n_kv_heads > 65535) return LRKV_ERR_SHAPE;
@@ -31,7 +34,7 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   if (!aligned16(L->bases) || !aligned16(L->codes_k) || !aligned16(L->codes_v) ||
       !aligned16(L->anchor_k) || !aligned16(L->anchor_v))
     return LRKV_ERR_ALIGN;
-  if (L->dtype == LRKV_BF16_Q8) {
+  if (quantised(L->dtype)) {
     if (!L->scales_k || !L->scales_v) return LRKV_ERR_NULL;
     if (!aligned16(L->scales_k) || !aligned16(L->scales_v)) return LRKV_ERR_ALIGN;
   }
@@ -48,8 +51,8 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   A->codes_v = L->codes_v;
   A->anchor_k = L->anchor_k;
   A->anchor_v = L->anchor_v;
-  A->scales_k = L->dtype == LRKV_BF16_Q8 ? L->scales_k : nullptr;
-  A->scales_v = L->dtype == LRKV_BF16_Q8 ? L->scales_v : nullptr;
+  A->scales_k = quantised(L->dtype) ? L->scales_k : nullptr;
+  A->scales_v = quantised(L->dtype) ? L->scales_v : nullptr;
   int64_t ub = 0, ck = 0, cv = 0;
   int rv_max = 0;
   for (int h = 0; h < L->n_kv_heads; ++h) {
@@ -157,7 +160,7 @@ lrkv_status lrkv_quantize(const lrkv_layer *L, int32_t which, const float *x, in
   LayerArgs A;
   lrkv_status st = make_layer(L, &A);
   if (st != LRKV_OK) return st;
-  if (L->dtype != LRKV_BF16_Q8) return LRKV_ERR_DTYPE;
+  if (!quantised(L->dtype)) return LRKV_ERR_DTYPE;
   if (which != 0 && which != 1) return LRKV_ERR_SHAPE;
   if (n_tok < 0 || slot0 < 0) return LRKV_ERR_SHAPE;
   if (int64_t(slot0) + n_tok > L->cap) return LRKV_ERR_CAPACITY;

@@ -80,7 +80,8 @@ __device__ __forceinline__ float block_absmax(float x, float *red) {
   return a;
 }
 
-template <typename T, bool Q8>
+// QMAX: 0 for bf16 / f32 codes, 127 for int8 codes, 7 for 4-bit codes
+template <typename T, int QMAX>
 __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, const T *vnew, int pos) {
   __shared__ float rk_row[kD], rv_row[kD];
   __shared__ float red[2];
@@ -116,13 +117,21 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
       for (int k = 0; k < kD; ++k) acck = fmaf(rk_row[k], to_f32(Uk[tid * kD + k]), acck);
     if (tid < hd.rv)
       for (int k = 0; k < kD; ++k) accv = fmaf(rv_row[k], to_f32(Uv[tid * kD + k]), accv);
-    if constexpr (Q8) {
-      int8_t *ck = static_cast<int8_t *>(L.codes_k) + hd.ck + int64_t(b) * L.cap * hd.rk;
-      int8_t *cv = static_cast<int8_t *>(L.codes_v) + hd.cv + int64_t(b) * L.cap * hd.rv;
-      const float sk = q8_scale(block_absmax(tid < hd.rk ? acck : 0.f, red));
-      const float sv = q8_scale(block_absmax(tid < hd.rv ? accv : 0.f, red));
-      if (tid < hd.rk) ck[kslot(code_slot, tid, hd.rk)] = int8_t(q8_value(acck, sk));
-      if (tid < hd.rv) cv[vslot(code_slot, tid, hd.rv)] = int8_t(q8_value(accv, sv));
+    if constexpr (QMAX > 0) {
+      const float sk = qn_scale<QMAX>(block_absmax(tid < hd.rk ? acck : 0.f, red));
+      const float sv = qn_scale<QMAX>(block_absmax(tid < hd.rv ? accv : 0.f, red));
+      const int64_t rgk = hd.ck + int64_t(b) * L.cap * hd.rk, rgv = hd.cv + int64_t(b) * L.cap * hd.rv;
+      if constexpr (QMAX == 127) {
+        int8_t *ck = static_cast<int8_t *>(L.codes_k) + rgk;
+        int8_t *cv = static_cast<int8_t *>(L.codes_v) + rgv;
+        if (tid < hd.rk) ck[kslot(code_slot, tid, hd.rk)] = int8_t(qn_value<QMAX>(acck, sk));
+        if (tid < hd.rv) cv[vslot(code_slot, tid, hd.rv)] = int8_t(qn_value<QMAX>(accv, sv));
+      } else {  // two elements per byte: regions start on even elements
+        uint8_t *ck = static_cast<uint8_t *>(L.codes_k) + rgk / 2;
+        uint8_t *cv = static_cast<uint8_t *>(L.codes_v) + rgv / 2;
+        if (tid < hd.rk) store_q4(ck, kslot(code_slot, tid, hd.rk), qn_value<QMAX>(acck, sk));
+        if (tid < hd.rv) store_q4(cv, vslot(code_slot, tid, hd.rv), qn_value<QMAX>(accv, sv));
+      }
       if (tid == 0) {
         L.scales_k[scale_index(L, h, b, code_slot)] = sk;
         L.scales_v[scale_index(L, h, b, code_slot)] = sv;
@@ -141,9 +150,10 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
 }
 
 // ---------------------------------------------------------------------------
-// Int8 quantisation of given float32 code rows: one wave per (token, row, head),
-// lane l holding columns l and l + 64.
+// Quantisation of given float32 code rows (QMAX 127: int8, 7: 4 bits): one wave
+// per (token, row, head), lane l holding columns l and l + 64.
 // ---------------------------------------------------------------------------
+template <int QMAX>
 __global__ __launch_bounds__(256) void k_quantize(LayerArgs L, int which, const float *x, int64_t sb,
                                                   int64_t sh, int64_t st, int n_tok, int slot0) {
   const int t = blockIdx.x * 4 + int(threadIdx.x >> 6);
@@ -156,12 +166,19 @@ __global__ __launch_bounds__(256) void k_quantize(LayerArgs L, int which, const 
   const float *row = x + b * sb + h * sh + int64_t(t) * st;
   const float v0 = lane < r ? row[lane] : 0.f;
   const float v1 = lane + 64 < r ? row[lane + 64] : 0.f;
-  const float s = q8_scale(wave_max(fmaxf(fabsf(v0), fabsf(v1))));
-  int8_t *codes = static_cast<int8_t *>(which ? L.codes_v : L.codes_k) + (which ? hd.cv : hd.ck) +
-                  int64_t(b) * L.cap * r;
+  const float s = qn_scale<QMAX>(wave_max(fmaxf(fabsf(v0), fabsf(v1))));
+  const int64_t region = (which ? hd.cv : hd.ck) + int64_t(b) * L.cap * r;
   const int j = slot0 + t;
-  if (lane < r) codes[which ? vslot(j, lane, r) : kslot(j, lane, r)] = int8_t(q8_value(v0, s));
-  if (lane + 64 < r) codes[which ? vslot(j, lane + 64, r) : kslot(j, lane + 64, r)] = int8_t(q8_value(v1, s));
+  auto pos = [&](int c) { return which ? vslot(j, c, r) : kslot(j, c, r); };
+  if constexpr (QMAX == 127) {
+    int8_t *codes = static_cast<int8_t *>(which ? L.codes_v : L.codes_k) + region;
+    if (lane < r) codes[pos(lane)] = int8_t(qn_value<QMAX>(v0, s));
+    if (lane + 64 < r) codes[pos(lane + 64)] = int8_t(qn_value<QMAX>(v1, s));
+  } else {
+    uint8_t *codes = static_cast<uint8_t *>(which ? L.codes_v : L.codes_k) + region / 2;
+    if (lane < r) store_q4(codes, pos(lane), qn_value<QMAX>(v0, s));
+    if (lane + 64 < r) store_q4(codes, pos(lane + 64), qn_value<QMAX>(v1, s));
+  }
   if (lane == 0) (which ? L.scales_v : L.scales_k)[scale_index(L, h, b, j)] = s;
 }
 
@@ -171,7 +188,10 @@ __global__ __launch_bounds__(256) void k_quantize(LayerArgs L, int which, const 
 hipError_t launch_quantize(const LayerArgs &L, int which, const float *x, int64_t sb, int64_t sh,
                            int64_t st, int n_tok, int slot0, hipStream_t s) {
   dim3 grid((n_tok + 3) / 4, L.batch * L.n_kv);
-  hipLaunchKernelGGL(k_quantize, grid, dim3(256), 0, s, L, which, x, sb, sh, st, n_tok, slot0);
+  if (L.dtype == LRKV_BF16_Q8)
+    hipLaunchKernelGGL(k_quantize<127>, grid, dim3(256), 0, s, L, which, x, sb, sh, st, n_tok, slot0);
+  else
+    hipLaunchKernelGGL(k_quantize<7>, grid, dim3(256), 0, s, L, which, x, sb, sh, st, n_tok, slot0);
   return hipGetLastError();
 }
 
@@ -198,15 +218,16 @@ hipError_t launch_store_anchors(const LayerArgs &L, const void *k, const void *v
 
 hipError_t launch_append(const LayerArgs &L, const void *k, const void *v, int pos, hipStream_t s) {
   dim3 grid(L.batch * L.n_kv);
+  const bf16_t *kb = static_cast<const bf16_t *>(k), *vb = static_cast<const bf16_t *>(v);
   if (L.dtype == LRKV_F32)
-    hipLaunchKernelGGL((k_append<float, false>), grid, dim3(kD), 0, s, L, static_cast<const float *>(k),
+    hipLaunchKernelGGL((k_append<float, 0>), grid, dim3(kD), 0, s, L, static_cast<const float *>(k),
                        static_cast<const float *>(v), pos);
   else if (L.dtype == LRKV_BF16)
-    hipLaunchKernelGGL((k_append<bf16_t, false>), grid, dim3(kD), 0, s, L, static_cast<const bf16_t *>(k),
-                       static_cast<const bf16_t *>(v), pos);
+    hipLaunchKernelGGL((k_append<bf16_t, 0>), grid, dim3(kD), 0, s, L, kb, vb, pos);
+  else if (L.dtype == LRKV_BF16_Q8)
+    hipLaunchKernelGGL((k_append<bf16_t, 127>), grid, dim3(kD), 0, s, L, kb, vb, pos);
   else
-    hipLaunchKernelGGL((k_append<bf16_t, true>), grid, dim3(kD), 0, s, L, static_cast<const bf16_t *>(k),
-                       static_cast<const bf16_t *>(v), pos);
+    hipLaunchKernelGGL((k_append<bf16_t, 7>), grid, dim3(kD), 0, s, L, kb, vb, pos);
   return hipGetLastError();
 }
 

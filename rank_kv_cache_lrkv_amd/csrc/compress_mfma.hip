@@ -19,8 +19,8 @@
 // The work is bound by reading the 256-byte input rows: 16 MFMAs per 32 tokens
 // and 16 columns keep the matrix cores a small fraction busy.
 //
-// Int8 codes (LRKV_BF16_Q8) take the same products; each token's row is then
-// quantised with its own scale (largest |code| / 127).
+// Quantised codes (LRKV_BF16_Q8, LRKV_BF16_Q4) take the same products; each
+// token's row is then quantised with its own scale (largest |code| / 127 or / 7).
 
 #include "mfma_util.h"
 
@@ -28,17 +28,23 @@ namespace lrkv {
 
 constexpr int kUStride = kD + 8;  // padded LDS row of one basis direction
 
-// 4 int8 values in the bytes of one word, first value in the low byte
-__device__ __forceinline__ uint32_t pack_q8(f32x4 v, float s0, float s1, float s2, float s3) {
-  return (uint32_t(q8_value(v[0], s0)) & 0xffu) | ((uint32_t(q8_value(v[1], s1)) & 0xffu) << 8) |
-         ((uint32_t(q8_value(v[2], s2)) & 0xffu) << 16) | (uint32_t(q8_value(v[3], s3)) << 24);
+// 4 quantised values, first value lowest: int8 in the bytes of a word (QMAX 127)
+// or 4-bit in the nibbles of a half word (QMAX 7)
+template <int QMAX>
+__device__ __forceinline__ uint32_t pack_qn(f32x4 v, float s0, float s1, float s2, float s3) {
+  constexpr int B = QMAX == 127 ? 8 : 4;
+  constexpr uint32_t M = (1u << B) - 1;
+  return (uint32_t(qn_value<QMAX>(v[0], s0)) & M) | ((uint32_t(qn_value<QMAX>(v[1], s1)) & M) << B) |
+         ((uint32_t(qn_value<QMAX>(v[2], s2)) & M) << (2 * B)) |
+         ((uint32_t(qn_value<QMAX>(v[3], s3)) & M) << (3 * B));
 }
 
-// Q8: int8 codes with one float32 scale per token and matrix.  The largest
-// |code| of a token is known only once every column tile is done, so the tiles
-// are swept twice (the products are cheap next to reading the rows): the first
-// sweep takes the maxima and writes the scales, the second quantises.
-template <bool Q8>
+// QMAX > 0: quantised codes (127: int8, 7: 4 bits) with one float32 scale per
+// token and matrix.  The largest |code| of a token is known only once every
+// column tile is done, so the tiles are swept twice (the products are cheap next
+// to reading the rows): the first sweep takes the maxima and writes the scales,
+// the second quantises.
+template <int QMAX>
 __global__ __launch_bounds__(256) void k_compress_mfma(LayerArgs L, int which, const bf16_t *x,
                                                        int64_t sb, int64_t sh, int64_t st,
                                                        int n_tok, int slot0) {
@@ -101,7 +107,7 @@ __global__ __launch_bounds__(256) void k_compress_mfma(LayerArgs L, int which, c
     return acc;
   };
 
-  if constexpr (!Q8) {
+  if constexpr (QMAX == 0) {
     bf16_t *codes = static_cast<bf16_t *>(which ? L.codes_v : L.codes_k) + region;
     for (int nt = 0; nt < r / 16; ++nt) {
       u32x4 uo[4];
@@ -136,7 +142,17 @@ __global__ __launch_bounds__(256) void k_compress_mfma(LayerArgs L, int which, c
       }
     }
   } else {
-    int8_t *codes = static_cast<int8_t *>(which ? L.codes_v : L.codes_k) + region;
+    // int8: one byte per element; 4 bits: regions start on even elements
+    uint8_t *codes = static_cast<uint8_t *>(which ? L.codes_v : L.codes_k) + (QMAX == 127 ? region : region / 2);
+    // 4 consecutive elements from element position p (a multiple of 4)
+    auto store4 = [&](int64_t p, uint32_t packed) {
+      if constexpr (QMAX == 127) *reinterpret_cast<uint32_t *>(codes + p) = packed;
+      else *reinterpret_cast<uint16_t *>(codes + p / 2) = uint16_t(packed);
+    };
+    auto store1 = [&](int64_t p, int q) {
+      if constexpr (QMAX == 127) codes[p] = uint8_t(q);
+      else store_q4(codes, p, q);
+    };
     float *scales = (which ? L.scales_v : L.scales_k) + scale_index(L, h, b, 0);
     // sweep 1: amax[tt][v] = largest |code| of this lane's token(s) (keys: v = 0 only)
     float amax[2][4] = {};
@@ -164,7 +180,7 @@ __global__ __launch_bounds__(256) void k_compress_mfma(LayerArgs L, int which, c
         float a = amax[tt][0];
         a = fmaxf(a, __shfl_xor(a, 16, 64));
         a = fmaxf(a, __shfl_xor(a, 32, 64));
-        sc[tt][0] = sc[tt][1] = sc[tt][2] = sc[tt][3] = q8_scale(a);
+        sc[tt][0] = sc[tt][1] = sc[tt][2] = sc[tt][3] = qn_scale<QMAX>(a);
         const int tok = t_base + 16 * tt + t16;
         if (q4 == 0 && tok < n_tok) scales[slot0 + tok] = sc[tt][0];
       } else {
@@ -173,7 +189,7 @@ __global__ __launch_bounds__(256) void k_compress_mfma(LayerArgs L, int which, c
           float a = amax[tt][v];
 #pragma unroll
           for (int o = 1; o < 16; o <<= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
-          sc[tt][v] = q8_scale(a);
+          sc[tt][v] = qn_scale<QMAX>(a);
           const int tok = t_base + 16 * tt + 4 * q4 + v;
           if (t16 == 0 && tok < n_tok) scales[slot0 + tok] = sc[tt][v];
         }
@@ -189,19 +205,18 @@ __global__ __launch_bounds__(256) void k_compress_mfma(LayerArgs L, int which, c
         if (which == 0) {
           const int tok = t_base + 16 * tt + t16;
           if (tok < n_tok)
-            *reinterpret_cast<uint32_t *>(codes + kslot(slot0 + tok, 16 * nt + 4 * q4, r)) =
-                pack_q8(acc, sc[tt][0], sc[tt][0], sc[tt][0], sc[tt][0]);
+            store4(kslot(slot0 + tok, 16 * nt + 4 * q4, r),
+                   pack_qn<QMAX>(acc, sc[tt][0], sc[tt][0], sc[tt][0], sc[tt][0]));
         } else {
           const int tok0 = t_base + 16 * tt + 4 * q4;
           const int col = 16 * nt + t16;
           const int j0 = slot0 + tok0;
           if (tok0 + 3 < n_tok && (j0 & 3) == 0) {
-            *reinterpret_cast<uint32_t *>(codes + vslot(j0, col, r)) =
-                pack_q8(acc, sc[tt][0], sc[tt][1], sc[tt][2], sc[tt][3]);
+            store4(vslot(j0, col, r), pack_qn<QMAX>(acc, sc[tt][0], sc[tt][1], sc[tt][2], sc[tt][3]));
           } else {
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-              if (tok0 + v < n_tok) codes[vslot(j0 + v, col, r)] = int8_t(q8_value(acc[v], sc[tt][v]));
+              if (tok0 + v < n_tok) store1(vslot(j0 + v, col, r), qn_value<QMAX>(acc[v], sc[tt][v]));
           }
         }
       }
@@ -212,12 +227,13 @@ __global__ __launch_bounds__(256) void k_compress_mfma(LayerArgs L, int which, c
 hipError_t launch_compress_mfma(const LayerArgs &L, int which, const void *x, int64_t sb,
                                 int64_t sh, int64_t st, int n_tok, int slot0, hipStream_t s) {
   dim3 grid((n_tok + 127) / 128, L.batch * L.n_kv);
+  const bf16_t *xb = static_cast<const bf16_t *>(x);
   if (L.dtype == LRKV_BF16_Q8)
-    hipLaunchKernelGGL(k_compress_mfma<true>, grid, dim3(256), 0, s, L, which,
-                       static_cast<const bf16_t *>(x), sb, sh, st, n_tok, slot0);
+    hipLaunchKernelGGL(k_compress_mfma<127>, grid, dim3(256), 0, s, L, which, xb, sb, sh, st, n_tok, slot0);
+  else if (L.dtype == LRKV_BF16_Q4)
+    hipLaunchKernelGGL(k_compress_mfma<7>, grid, dim3(256), 0, s, L, which, xb, sb, sh, st, n_tok, slot0);
   else
-    hipLaunchKernelGGL(k_compress_mfma<false>, grid, dim3(256), 0, s, L, which,
-                       static_cast<const bf16_t *>(x), sb, sh, st, n_tok, slot0);
+    hipLaunchKernelGGL(k_compress_mfma<0>, grid, dim3(256), 0, s, L, which, xb, sb, sh, st, n_tok, slot0);
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
-// Stage 1 of decode attention for bfloat16 caches (and int8 codes with per-token
-// scales, converted to bf16 on the way in) on the gfx950 matrix cores.
+// Stage 1 of decode attention for bfloat16 caches (and int8 or 4-bit codes with
+// per-token scales, converted to bf16 on the way in) on the gfx950 matrix cores.
 //
 // One workgroup of four waves per (split, batch row, KV head).  For one 32-slot
 // code block a wave computes
@@ -69,7 +69,8 @@ struct MfmaSmem {
   float o[4][LRKV_MAX_GROUP][RVMAX];        // per-wave rank-space sums
 };
 
-template <int NKC, int NVC, bool Q8>
+// CB: bits per code element (16 bf16, 8 int8, 4 four-bit)
+template <int NKC, int NVC, int CB>
 struct BlockRegs {
   u32x4 k[2][NKC];
   u32x4 v[NVC];
@@ -79,9 +80,16 @@ struct BlockRegs {
 // 16 ((t16 >> 2) & 1) + 4 q4 + (t16 & 3), so lanes 0 .. 7 of the row hold the
 // row's 8 tokens 16 h2 + 4 q4 + v in the order 4 h2 + v
 template <int NKC, int NVC>
-struct BlockRegs<NKC, NVC, true> {
+struct BlockRegs<NKC, NVC, 8> {
   u32x2 k[2][NKC];
   u32x2 v[NVC];
+  uint32_t sk, sv;
+};
+// 4-bit codes: 4 bytes per lane and operand, scales as for int8
+template <int NKC, int NVC>
+struct BlockRegs<NKC, NVC, 4> {
+  uint32_t k[2][NKC];
+  uint32_t v[NVC];
   uint32_t sk, sv;
 };
 
@@ -116,16 +124,37 @@ __device__ __forceinline__ u32x4 i8x8_to_bf16(u32x2 w) {
   return r;
 }
 
+// 8 four-bit values (lowest nibble first) as 8 bf16 values of 16 times their
+// value: each nibble is moved to the top of a byte and converted with the
+// sign-extending byte select (the factor 16 is taken out of the scales)
+__device__ __forceinline__ u32x4 i4x8_to_bf16_x16(uint32_t w) {
+  auto pair = [](float a, float b) {
+    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+  };
+  const uint32_t ev = (w << 4) & 0xf0f0f0f0u;  // elements 0, 2, 4, 6
+  const uint32_t od = w & 0xf0f0f0f0u;         // elements 1, 3, 5, 7
+  u32x4 r;
+  r[0] = pair(float(int8_t(ev)), float(int8_t(od)));
+  r[1] = pair(float(int8_t(ev >> 8)), float(int8_t(od >> 8)));
+  r[2] = pair(float(int8_t(ev >> 16)), float(int8_t(od >> 16)));
+  r[3] = pair(float(int32_t(ev) >> 24), float(int32_t(od) >> 24));
+  return r;
+}
+
 // EXACT: every head of the layer has rank_k == RKMAX and rank_v == RVMAX, so all
 // rank tests fold at compile time; otherwise ranks are read per head (<= the max).
-// Q8: int8 codes with a float32 scale per token (keys and values): the codes
-// enter the MFMAs converted to bf16 (exact), a score is the product times the
-// key scale, and a token's weight is multiplied by its value scale before it
-// becomes the value MFMA's A operand (the denominator keeps the plain weight).
-template <int RKMAX, int RVMAX, bool EXACT, bool Q8>
+// CB = 8 or 4: quantised codes with a float32 scale per token (keys and values):
+// the codes enter the MFMAs converted to bf16 (exact; 4-bit codes as 16 times
+// their value, the 16 taken out of q~ and of the value sums), a score is the
+// product times the key scale, and a token's weight is multiplied by its value
+// scale before it becomes the value MFMA's A operand (the denominator keeps the
+// plain weight).
+template <int RKMAX, int RVMAX, bool EXACT, int CB>
 __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d) {
   constexpr int NKC = (RKMAX + 31) / 32;  // score MFMAs per 16-token tile (K = 32 each)
   constexpr int NVC = RVMAX / 16;         // value MFMAs per block (16 columns each)
+  constexpr bool QC = CB < 16;            // quantised codes with per-token scales
+  constexpr float kX16 = CB == 4 ? 0.0625f : 1.f;  // undoes the x16 of 4-bit operands
   __shared__ MfmaSmem<RKMAX, RVMAX> sm;
 
   const int S = d.n_splits;
@@ -183,46 +212,51 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   }
 
   // this (row, head)'s key and value code regions (and int8 scales) as buffer
-  // resources; EB = bytes per code element
-  constexpr int EB = Q8 ? 1 : 2;
+  // resources; byte offsets are element offsets * CB / 8 (regions start on even
+  // elements)
   const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
-      static_cast<char *>(L.codes_k) + (hd.ck + int64_t(b) * L.cap * rk) * EB, 0, L.cap * rk * EB,
+      static_cast<char *>(L.codes_k) + (hd.ck + int64_t(b) * L.cap * rk) * CB / 8, 0, L.cap * rk * CB / 8,
       kBufferWord3);
   const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
-      static_cast<char *>(L.codes_v) + (hd.cv + int64_t(b) * L.cap * rv) * EB, 0, L.cap * rv * EB,
+      static_cast<char *>(L.codes_v) + (hd.cv + int64_t(b) * L.cap * rv) * CB / 8, 0, L.cap * rv * CB / 8,
       kBufferWord3);
   __amdgpu_buffer_rsrc_t skres = kres, svres = vres;
-  if constexpr (Q8) {
+  if constexpr (QC) {
     skres = __builtin_amdgcn_make_buffer_rsrc(L.scales_k + scale_index(L, h, b, 0), 0, L.cap * 4, kBufferWord3);
     svres = __builtin_amdgcn_make_buffer_rsrc(L.scales_v + scale_index(L, h, b, 0), 0, L.cap * 4, kBufferWord3);
   }
   const int soff = (16 * ((t16 >> 2) & 1) + 4 * q4 + (t16 & 3)) * 4;  // this lane's scale in a block
-  const int kblk_bytes = kBlock * rk * EB, vblk_bytes = kBlock * rv * EB;
+  const int kblk_bytes = kBlock * rk * CB / 8, vblk_bytes = kBlock * rv * CB / 8;
   int koff[2][NKC];
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       const int kg = min(4 * kc + q4, nkg - 1);  // absent groups re-read a present one, then zero
-      koff[h2][kc] = ((h2 * nkg + kg) * 16 + t16) * 8 * EB;
+      koff[h2][kc] = ((h2 * nkg + kg) * 16 + t16) * CB;
     }
   int voff[NVC];
 #pragma unroll
-  for (int ni = 0; ni < NVC; ++ni) voff[ni] = (q4 * rv + 16 * min(ni, nvt - 1) + t16) * 8 * EB;
+  for (int ni = 0; ni < NVC; ++ni) voff[ni] = (q4 * rv + 16 * min(ni, nvt - 1) + t16) * CB;
 
-  auto load = [&](int blk, BlockRegs<NKC, NVC, Q8> &r) {
+  auto load = [&](int blk, BlockRegs<NKC, NVC, CB> &r) {
     set_priority(blk);
     // the block offsets are wave-uniform: keep them in scalar registers
     const int ks = __builtin_amdgcn_readfirstlane(blk * kblk_bytes);
     const int vs = __builtin_amdgcn_readfirstlane(blk * vblk_bytes);
-    if constexpr (Q8) {
+    if constexpr (QC) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
-          r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b64(kres, koff[h2][kc], ks, 0);
+        for (int kc = 0; kc < NKC; ++kc) {
+          if constexpr (CB == 8) r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b64(kres, koff[h2][kc], ks, 0);
+          else r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b32(kres, koff[h2][kc], ks, 0);
+        }
 #pragma unroll
-      for (int ni = 0; ni < NVC; ++ni) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b64(vres, voff[ni], vs, 0);
+      for (int ni = 0; ni < NVC; ++ni) {
+        if constexpr (CB == 8) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b64(vres, voff[ni], vs, 0);
+        else r.v[ni] = __builtin_amdgcn_raw_buffer_load_b32(vres, voff[ni], vs, 0);
+      }
       const int ss = __builtin_amdgcn_readfirstlane(blk * kBlock * 4);
       r.sk = __builtin_amdgcn_raw_buffer_load_b32(skres, soff, ss, 0);
       r.sv = __builtin_amdgcn_raw_buffer_load_b32(svres, soff, ss, 0);
@@ -264,7 +298,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   __builtin_amdgcn_sched_barrier(0);
   // the wave's first block (clamped to the last block; with no blocks at all
   // block 0 is read and never used, which the region bound makes harmless)
-  BlockRegs<NKC, NVC, Q8> r0, r1;
+  BlockRegs<NKC, NVC, CB> r0, r1;
   {
     const int last = max(nblk - 1, 0);
     load(min(first, last), r0);
@@ -293,7 +327,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int head = 4 * q4 + v;
-        if (head < G) sm.u.qt[head][16 * nt + t16] = acc[v] * d.scale_log2;
+        if (head < G) sm.u.qt[head][16 * nt + t16] = acc[v] * (d.scale_log2 * kX16);
       }
     }
   }
@@ -397,7 +431,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
 #pragma unroll
   for (int ni = 0; ni < NVC; ++ni) o[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto process = [&](int blk, BlockRegs<NKC, NVC, Q8> &r) {
+  auto process = [&](int blk, BlockRegs<NKC, NVC, CB> &r) {
     f32x4 s[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) s[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -408,7 +442,8 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           u32x4 a;
-          if constexpr (Q8) a = i8x8_to_bf16(r.k[h2][kc]);
+          if constexpr (CB == 8) a = i8x8_to_bf16(r.k[h2][kc]);
+          else if constexpr (CB == 4) a = i4x8_to_bf16_x16(r.k[h2][kc]);
           else a = r.k[h2][kc];
           if (4 * kc + q4 >= nkg) a = u32x4{0u, 0u, 0u, 0u};
           s[h2] = mfma16x16x32(a, bh, s[h2]);
@@ -416,7 +451,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
         }
       }
     }
-    if constexpr (Q8) {
+    if constexpr (QC) {
       float ksc[8];
       row_scales(r.sk, ksc);
 #pragma unroll
@@ -433,7 +468,8 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
         for (int v = 0; v < 4; ++v)
           if (tok0 + 16 * h2 + 4 * q4 + v >= c) s[h2][v] = kNegInf;
     }
-    if (!Q8 && tok0 + kBlock > c) {  // bf16 slots past c may hold any bits: zero them
+    if constexpr (!QC) {
+    if (tok0 + kBlock > c) {  // bf16 slots past c may hold any bits: zero them
       uint32_t keep[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -446,6 +482,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
       for (int ni = 0; ni < NVC; ++ni)
 #pragma unroll
         for (int i = 0; i < 4; ++i) r.v[ni][i] &= keep[i];
+    }
     }
     // online softmax of head t16 over its 8 scores in this lane, 32 per block
     float bm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
@@ -473,12 +510,12 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
       }
     }
     // weights as the A operand (k-slot j = 4 h + v), hi and lo parts
-    if constexpr (Q8) {
+    if constexpr (QC) {
       float vsc[8];
       row_scales(r.sv, vsc);
 #pragma unroll
       for (int j = 0; j < 8; ++j) p[j] *= vsc[j];
-      if (ragged) {  // slots past c: weight 0 whatever their scale holds (int8 codes are finite)
+      if (ragged) {  // slots past c: weight 0 whatever their scale holds (quantised codes are finite)
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           if (tok0 + 16 * (j >> 2) + 4 * q4 + (j & 3) >= c) p[j] = 0.f;
@@ -494,7 +531,8 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
     for (int ni = 0; ni < NVC; ++ni) {
       if (ni < nvt) {
         u32x4 bv;
-        if constexpr (Q8) bv = i8x8_to_bf16(r.v[ni]);
+        if constexpr (CB == 8) bv = i8x8_to_bf16(r.v[ni]);
+        else if constexpr (CB == 4) bv = i4x8_to_bf16_x16(r.v[ni]);
         else bv = r.v[ni];
         o[ni] = mfma16x16x32(a_hi, bv, o[ni]);
         o[ni] = mfma16x16x32(a_lo, bv, o[ni]);
@@ -558,7 +596,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
     float acc = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) acc = fmaf(weight(w, hh, M), sm.o[w][hh][cc], acc);
-    split_record(d, q0 + hh, split)[4 + cc] = acc;
+    split_record(d, q0 + hh, split)[4 + cc] = acc * kX16;
   }
   if (na > 0) {  // anchor-free splits leave o_A unwritten; the combine skips it
     for (int i = tid; i < G * kD; i += blockDim.x) {
@@ -578,20 +616,23 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   }
 }
 
+template <int RKMAX, int RVMAX, bool EXACT>
+static void launch_cb(const LayerArgs &L, const DecodeArgs &d, dim3 grid, hipStream_t s) {
+  if (L.dtype == LRKV_BF16_Q8)
+    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, EXACT, 8>), grid, dim3(256), 0, s, L, d);
+  else if (L.dtype == LRKV_BF16_Q4)
+    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, EXACT, 4>), grid, dim3(256), 0, s, L, d);
+  else
+    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, EXACT, 16>), grid, dim3(256), 0, s, L, d);
+}
+
 template <int RKMAX, int RVMAX>
 static hipError_t launch_rv(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
   bool exact = true;
   for (int h = 0; h < L.n_kv; ++h) exact = exact && L.heads[h].rk == RKMAX && L.heads[h].rv == RVMAX;
   dim3 grid(d.n_splits, L.batch * L.n_kv);
-  const bool q8 = L.dtype == LRKV_BF16_Q8;
-  if (exact && q8)
-    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, true, true>), grid, dim3(256), 0, s, L, d);
-  else if (exact)
-    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, true, false>), grid, dim3(256), 0, s, L, d);
-  else if (q8)
-    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, false, true>), grid, dim3(256), 0, s, L, d);
-  else
-    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, false, false>), grid, dim3(256), 0, s, L, d);
+  if (exact) launch_cb<RKMAX, RVMAX, true>(L, d, grid, s);
+  else launch_cb<RKMAX, RVMAX, false>(L, d, grid, s);
   return hipGetLastError();
 }
 

@@ -23,7 +23,7 @@ struct LayerArgs {
   int32_t dtype, batch, n_q, n_kv, group, window, cap, rv_max;
   const void *bases;
   void *codes_k, *codes_v, *anchor_k, *anchor_v;
-  float *scales_k, *scales_v;  // int8 codes: one scale per (head, row, slot)
+  float *scales_k, *scales_v;  // quantised codes: one scale per (head, row, slot)
   HeadInfo heads[LRKV_MAX_KV_HEADS];
 };
 
@@ -84,18 +84,38 @@ __device__ __forceinline__ int anchor_slot(int p, int window) {
   return p == 0 ? 0 : 1 + (p - 1) % window;
 }
 
-// int8 codes: element of the scale of slot j of (KV head h, batch row b)
+// quantised codes: element of the scale of slot j of (KV head h, batch row b)
 __device__ __forceinline__ int64_t scale_index(const LayerArgs &L, int h, int b, int j) {
   return (int64_t(h) * L.batch + b) * L.cap + j;
 }
-// the scale of a code row with largest magnitude a, and one quantised value:
-// x / s rounded to nearest even and clipped to [-127, 127] (float32 divisions,
-// correctly rounded); a zero row (s = 0) quantises to 0
-__device__ __forceinline__ float q8_scale(float absmax) { return absmax / 127.f; }
-__device__ __forceinline__ int q8_value(float x, float s) {
+// QMAX = 127 (int8 codes) or 7 (4-bit codes): the scale of a code row with
+// largest magnitude a, and one quantised value, x / s rounded to nearest even
+// and clipped to [-QMAX, QMAX] (float32 divisions, correctly rounded); a zero
+// row (s = 0) quantises to 0
+template <int QMAX> __device__ __forceinline__ float qn_scale(float absmax) { return absmax / float(QMAX); }
+template <int QMAX> __device__ __forceinline__ int qn_value(float x, float s) {
   if (!(s > 0.f)) return 0;
   const float t = __builtin_rintf(x / s);
-  return int(fminf(fmaxf(t, -127.f), 127.f));
+  return int(fminf(fmaxf(t, -float(QMAX)), float(QMAX)));
+}
+__device__ __forceinline__ float q8_scale(float absmax) { return qn_scale<127>(absmax); }
+__device__ __forceinline__ int q8_value(float x, float s) { return qn_value<127>(x, s); }
+
+// 4-bit codes: store value q of element position p of a region (two per byte,
+// even p in the low half).  Neighbouring elements share bytes, so the update is
+// two word-wide atomics on disjoint bits: any number of threads may store
+// different elements of one word concurrently.
+__device__ __forceinline__ void store_q4(uint8_t *region, int64_t p, int q) {
+  const int64_t byte = p >> 1;
+  uint32_t *word = reinterpret_cast<uint32_t *>(region + (byte & ~int64_t(3)));
+  const int shift = int(byte & 3) * 8 + int(p & 1) * 4;
+  atomicAnd(word, ~(0xfu << shift));
+  atomicOr(word, (uint32_t(q) & 0xfu) << shift);
+}
+
+// bits per code element: 16 (bf16), 32 (f32), 8 or 4 (quantised)
+__device__ __host__ __forceinline__ int code_bits(int dtype) {
+  return dtype == LRKV_F32 ? 32 : dtype == LRKV_BF16 ? 16 : dtype == LRKV_BF16_Q8 ? 8 : 4;
 }
 
 // context length of batch row b

@@ -89,6 +89,24 @@ def pack_codes(codes: np.ndarray, cap: int, which: str) -> np.ndarray:
     return out
 
 
+def pack_nibbles(values: np.ndarray) -> np.ndarray:
+    """Flat element array of 4-bit values in [-8, 7] -> bytes, two per byte, even
+    elements in the low four bits (the 4-bit code layout of lrkv.h)."""
+    v = np.asarray(values).astype(np.int16) & 0xF
+    if v.size % 2:
+        v = np.concatenate([v, np.zeros(1, v.dtype)])
+    return (v[0::2] | (v[1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
+    """Bytes -> flat element array of signed 4-bit values (int8)."""
+    b = np.asarray(packed, np.uint8).astype(np.int16)
+    v = np.empty(b.size * 2, np.int16)
+    v[0::2] = b & 0xF
+    v[1::2] = b >> 4
+    return np.where(v >= 8, v - 16, v).astype(np.int8)
+
+
 def unpack_codes(region: np.ndarray, n: int, r: int, which: str) -> np.ndarray:
     """Flat blocked region -> (n, r) logical codes of slots 0..n-1."""
     return np.asarray(region)[slot_positions(n, r, which)]

@@ -32,10 +32,21 @@ def oracle_q8(exact) -> tuple:
     return oracle.quantize_codes_q8(np.asarray(exact, np.float64).astype(np.float32))
 
 
+def oracle_q4(exact) -> tuple:
+    """4-bit codes and scales of exact code rows: the float32 projection, quantised."""
+    return oracle.quantize_codes_q4(np.asarray(exact, np.float64).astype(np.float32))
+
+
+def oracle_quant(exact, bits: int) -> tuple:
+    return oracle_q8(exact) if bits == 8 else oracle_q4(exact)
+
+
 def code_storage(exact, codes: str) -> np.ndarray:
-    """The code values a cache of kind ``codes`` ("f32", "bf16" or "q8") holds."""
+    """The code values a cache of kind ``codes`` ("f32", "bf16", "q8" or "q4") holds."""
     if codes == "q8":
         return oracle.dequantize_codes_q8(*oracle_q8(exact))
+    if codes == "q4":
+        return oracle.dequantize_codes_q4(*oracle_q4(exact))
     return to_storage(exact, codes)
 
 
@@ -52,11 +63,11 @@ class HostCase:
     v: list
     q: np.ndarray                # (batch, Hq, 128)
     layer: int = 0
-    q8: bool = False             # int8 codes with per-token scales (bf16 everything else)
+    qbits: int = 0               # 8 / 4: quantised codes with per-token scales (bf16 everything else)
 
     @property
     def codes_kind(self) -> str:
-        return "q8" if self.q8 else self.w.dtype
+        return f"q{self.qbits}" if self.qbits else self.w.dtype
 
     @property
     def window(self):
@@ -93,8 +104,10 @@ class HostCase:
 
 
 def host_case(w: synth.Workload, n: Optional[int] = None, layer: int = 0, step: int = 0,
-              q_scale: float = 1.0, lens: Optional[List[int]] = None, q8: bool = False) -> HostCase:
-    assert not (q8 and w.dtype != "bf16"), "int8 codes come with bf16 bases and anchors"
+              q_scale: float = 1.0, lens: Optional[List[int]] = None, q8: bool = False,
+              qbits: int = 0) -> HostCase:
+    qbits = 8 if q8 else qbits
+    assert not (qbits and w.dtype != "bf16"), "quantised codes come with bf16 bases and anchors"
     n = w.n_ctx if n is None else n
     rk, rv = synth.ranks(w, layer)
     u_k = [synth.basis(w, layer, h, "k", int(rk[h])).astype(np.float64) for h in range(w.n_kv_heads)]
@@ -105,7 +118,7 @@ def host_case(w: synth.Workload, n: Optional[int] = None, layer: int = 0, step: 
          for b in range(w.batch)]
     q = np.stack([synth.queries(w, layer, step, b, q_scale) for b in range(w.batch)]).astype(np.float64)
     lens = [n] * w.batch if lens is None else list(lens)
-    return HostCase(w, n, lens, rk, rv, u_k, u_v, k, v, q, layer, q8)
+    return HostCase(w, n, lens, rk, rv, u_k, u_v, k, v, q, layer, qbits)
 
 
 # ---------------------------------------------------------------------------
@@ -130,13 +143,13 @@ def gpu_layer(hc: HostCase, cap: Optional[int] = None, with_codes: bool = True):
     cmax = max(0, hc.n - 1 - W)
     cap = layout.round_cap(cmax) if cap is None else cap
     bases = layout.pack_bases(hc.u_k, hc.u_v)
-    dtype = B.LRKV_BF16_Q8 if hc.q8 else B.LRKV_F32 if w.dtype == "f32" else B.LRKV_BF16
+    dtype = {8: B.LRKV_BF16_Q8, 4: B.LRKV_BF16_Q4}.get(hc.qbits, B.LRKV_F32 if w.dtype == "f32" else B.LRKV_BF16)
     L = B.Layer.allocate(dtype=dtype, batch=w.batch,
                          n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, window=W, cap=cap,
                          rank_k=hc.rk, rank_v=hc.rv, bases=dev(bases, w.dtype))
     if not with_codes:
         return L
-    cdt = np.int8 if hc.q8 else np.float32
+    cdt = np.int8 if hc.qbits else np.float32
     ck = np.zeros(max(1, layout.codes_elems(hc.rk, w.batch, cap)), cdt)
     cv = np.zeros(max(1, layout.codes_elems(hc.rv, w.batch, cap)), cdt)
     sk = np.zeros(max(1, layout.scales_elems(w.n_kv_heads, w.batch, cap)), np.float32)
@@ -150,8 +163,8 @@ def gpu_layer(hc: HostCase, cap: Optional[int] = None, with_codes: bool = True):
         for h in range(w.n_kv_heads):
             for which, flat, off, r, sc in (("k", ck, ok, hc.rk, sk), ("v", cv, ov, hc.rv, sv)):
                 base = off[h] + b * cap * int(r[h])
-                if hc.q8:
-                    q, s = oracle_q8(hc.exact_codes(b, h, which))
+                if hc.qbits:
+                    q, s = oracle_quant(hc.exact_codes(b, h, which), hc.qbits)
                     flat[base:base + cap * int(r[h])] = layout.pack_codes(q, cap, which)
                     s0 = layout.scale_offset(h, b, cap, w.batch)
                     sc[s0:s0 + len(s)] = s
@@ -162,8 +175,10 @@ def gpu_layer(hc: HostCase, cap: Optional[int] = None, with_codes: bool = True):
                 s = layout.anchor_slot(int(p), W)
                 ak[b, h, s] = hc.k[b][h][p]
                 av[b, h, s] = hc.v[b][h][p]
-    if hc.q8:
+    if hc.qbits:
         import torch
+        if hc.qbits == 4:  # element arrays -> bytes, two elements per byte
+            ck, cv = layout.pack_nibbles(ck), layout.pack_nibbles(cv)
         L.codes_k.copy_(torch.from_numpy(ck).cuda())
         L.codes_v.copy_(torch.from_numpy(cv).cuda())
         L.scales_k.copy_(torch.from_numpy(sk).cuda())

@@ -83,6 +83,8 @@ def decode(L, n_ctx=50, q=FAKE, out=FAKE, scale=0.088, S=2, ws=FAKE, ws_bytes=1 
     (dict(dtype=2, scales_k=None), 1),                          # int8 codes need their scales
     (dict(dtype=2, scales_v=FAKE + 4), 5),
     (dict(dtype=2, cap=(1 << 31) // 256 // 32 * 32 + 32), 2),
+    (dict(dtype=3, scales_v=None), 1),                          # 4-bit codes too
+    (dict(dtype=4), 4),
 ])
 def test_layer_validation(kw, status):
     assert decode(layer(**kw)) == status
@@ -184,3 +186,5 @@ def test_quantize_validation():
     assert f(sh=-512) == 2
     assert f(x=FAKE + 2) == 5            # float32 rows need 4-byte alignment only
     assert f(L=layer(dtype=2, scales_v=None)) == 1
+    assert f(L=layer(dtype=3), n=60, slot0=5) == 6     # 4-bit layers take the same checks
+    assert f(L=layer(dtype=3), x=FAKE + 2) == 5

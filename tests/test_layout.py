@@ -65,3 +65,14 @@ def test_pack_bases_rows_are_basis_directions():
             assert np.array_equal(flat[ok[h] + 128 * c: ok[h] + 128 * (c + 1)], uk[h][:, c])
         for c in range(uv[h].shape[1]):
             assert np.array_equal(flat[ov[h] + 128 * c: ov[h] + 128 * (c + 1)], uv[h][:, c])
+
+
+def test_nibble_packing_round_trip_and_order():
+    rng = np.random.default_rng(5)
+    v = rng.integers(-8, 8, 1001).astype(np.int8)
+    p = layout.pack_nibbles(v)
+    assert p.dtype == np.uint8 and p.size == 501
+    assert np.array_equal(layout.unpack_nibbles(p)[:1001], v)
+    # element 0 in the low four bits, element 1 in the high four bits, two's complement
+    assert layout.pack_nibbles(np.array([-1, 2], np.int8)).tolist() == [0x2F]
+    assert layout.pack_nibbles(np.array([7, -8], np.int8)).tolist() == [0x87]
