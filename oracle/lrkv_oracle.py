@@ -28,6 +28,11 @@ Readings where the pages are silent (each also listed in the design doc):
 * query head i of a GQA group reads KV head i // g;
 * codes are ``x @ U`` with U a (128, r) matrix with orthonormal columns.
 
+Online basis adaptation (OjaKV) uses the textbook Oja subspace rule with
+re-orthonormalisation (the page names Oja's algorithm but gives no rule); codes
+made under several basis versions are decoded each with its own version; see
+oja_update and oracle_decode_unit_versions.
+
 Int8 and int4 codes (the first step past the pages: they name quantisation of
 the low-rank cache but no quantiser) follow a stated design, symmetric with one
 float32 scale per code row, decided in float32; see quantize_codes_q8 and
@@ -182,6 +187,67 @@ def oracle_decode_layer(q, bases_k, bases_v, codes_k, codes_v, anchors_k, anchor
                 q[b, rows], bases_k[h], bases_v[h], codes_k[b][h], codes_v[b][h],
                 anchors_k[b][h], anchors_v[b][h], scale)
     return out
+
+
+# ---------------------------------------------------------------------------
+# online subspace adaptation (OjaKV summary and FAQ: Oja's algorithm for online
+# PCA keeps adapting the projection basis, thoroughly during prompt prefill and
+# lightly, now and then, during decoding; older codes stay in the basis they were
+# made with).  The page names the algorithm but prints no update rule, step size
+# or schedule, so the textbook subspace rule is used, with the columns brought
+# back to orthonormal after every step (the decode reads bases as orthonormal).
+# ---------------------------------------------------------------------------
+
+def orthonormalise(a) -> np.ndarray:
+    """The Q of the thin QR factorisation of ``a`` (d, r) whose R has a positive
+    diagonal: the columns Gram-Schmidt gives, in order.  Columns must be
+    linearly independent."""
+    a = np.asarray(a, np.float64)
+    q, r = np.linalg.qr(a)
+    return q * np.sign(np.diag(r))[None, :]
+
+
+def oja_update(u, x, eta: float) -> np.ndarray:
+    """One step of Oja's subspace rule on a batch of rows.
+
+    u (d, r) with orthonormal columns; x (N, d): the rows seen since the last
+    step (keys after RoPE, or values); eta: the step size.  With y = x u (the
+    rows' codes), u' = u + eta (x^T y - u y^T y) / N, i.e. the rule's average
+    over the batch; then u' is orthonormalised.  N = 0 leaves u unchanged."""
+    u = np.asarray(u, np.float64)
+    x = np.asarray(x, np.float64)
+    n = x.shape[0]
+    if n == 0:
+        return u.copy()
+    y = x @ u
+    grad = (x.T @ y - u @ (y.T @ y)) / n
+    return orthonormalise(u + eta * grad)
+
+
+def oracle_decode_unit_versions(q, bases_k, bases_v, versions, c_k, c_v, k_a, v_a,
+                                scale: float) -> np.ndarray:
+    """Decode attention of one GQA group when its code tokens were made under
+    several bases: code token j was compressed with bases_k[versions[j]] and
+    bases_v[versions[j]].  Each token is scored against the query projected
+    with its own key basis and its value sum is up-projected with its own value
+    basis; one softmax covers every code token and the anchors.  Returns out
+    (g, 128)."""
+    q = np.asarray(q, np.float64)
+    versions = np.asarray(versions, np.int64)
+    c_k = np.asarray(c_k, np.float64)
+    c_v = np.asarray(c_v, np.float64)
+    c = len(versions)
+    s_codes = np.zeros((q.shape[0], c))
+    for v in np.unique(versions):
+        sel = versions == v
+        s_codes[:, sel] = code_scores(project_query(q, bases_k[v]), c_k[sel], scale)
+    s = np.concatenate([s_codes, anchor_scores(q, k_a, scale)], axis=1)
+    e, total = softmax_weights(s)
+    out = anchor_values(e[:, c:], v_a)
+    for v in np.unique(versions):
+        sel = versions == v
+        out = out + up_project(rank_space_values(e[:, :c][:, sel], c_v[sel]), bases_v[v])
+    return out / total
 
 
 # ---------------------------------------------------------------------------

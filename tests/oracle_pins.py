@@ -427,4 +427,108 @@ def pin_layer_gqa_sdpa():
     assert rel(got, want) < 1e-12, rel(got, want)
 
 
+# ---------------------------------------------------------------------------
+# online basis adaptation (Oja's subspace rule) and versioned codes
+# ---------------------------------------------------------------------------
+
+def _spectrum_rows(rng, n, sig, rot):
+    """n rows whose second-moment matrix is about rot diag(sig^2) rot^T."""
+    return (rng.standard_normal((n, len(sig))) * sig[None, :]) @ rot.T
+
+
+def pin_oja_fixed_point():
+    """If u spans an invariant subspace of the batch's second-moment matrix C,
+    the rule's step is zero (C u = u u^T C u), for any rotation of that
+    subspace: the update returns u itself."""
+    rng = np.random.default_rng(31)
+    rot = orthonormal(rng, D)
+    sig = np.exp(-np.arange(D) / 16.0)
+    x = np.sqrt(D) * (sig[:, None] * rot.T)        # x^T x / D = rot diag(sig^2) rot^T exactly
+    for r in (1, 16, 64):
+        spin = orthonormal(rng, r)[:r, :r] if r > 1 else np.ones((1, 1))
+        u = rot[:, :r] @ spin
+        u = oracle.orthonormalise(u)               # exact orthonormal columns, same span
+        got = oracle.oja_update(u, x, 0.7)
+        # the step vanishes; the QR sign convention may flip no column of an
+        # already-orthonormal u whose R is the identity
+        assert np.max(np.abs(got - u)) < 1e-10, (r, np.max(np.abs(got - u)))
+
+
+def pin_oja_converges_to_top_subspace():
+    """Repeated steps on one batch with a spectral gap converge to the span of
+    the top-r eigenvectors of x^T x (LAPACK's symmetric eigensolver)."""
+    rng = np.random.default_rng(32)
+    rot = orthonormal(rng, D)
+    sig = np.concatenate([np.linspace(2.0, 1.0, 8), 0.3 * np.exp(-np.arange(D - 8) / 16.0)])
+    x = _spectrum_rows(rng, 3000, sig, rot)
+    w, vecs = np.linalg.eigh(x.T @ x / len(x))
+    top = vecs[:, np.argsort(w)[::-1][:8]]
+    u = orthonormal(rng, 8)
+    # step 0.2: every mode outside the subspace shrinks by 1 - 0.2 (l_in - l_out), in (0, 1)
+    for _ in range(200):
+        u = oracle.oja_update(u, x, 0.2)
+    dist = np.linalg.norm(u @ u.T - top @ top.T)
+    assert dist < 1e-8, dist
+    assert np.max(np.abs(u.T @ u - np.eye(8))) < 1e-12
+
+
+def pin_oja_single_unit_textbook():
+    """r = 1 and one row: Oja's single-neuron rule w + eta y (x - y w), y = x.w,
+    then normalised."""
+    rng = np.random.default_rng(33)
+    w = rng.standard_normal(D)
+    w /= np.linalg.norm(w)
+    x = rng.standard_normal(D)
+    y = float(x @ w)
+    want = w + 0.05 * y * (x - y * w)
+    want /= np.linalg.norm(want)
+    if want @ w < 0:                                # sign convention: R > 0 keeps w's side
+        want = -want
+    got = oracle.oja_update(w[:, None], x[None, :], 0.05)[:, 0]
+    assert np.max(np.abs(got - want)) < 1e-14
+
+
+def pin_oja_batch_is_average_of_rows():
+    """The batch step is the mean of the single-row steps (before
+    orthonormalisation); with r = d the step vanishes (u u^T = I); no rows, no
+    change."""
+    rng = np.random.default_rng(34)
+    u = orthonormal(rng, 24)
+    x = rng.standard_normal((5, D))
+    eta = 0.01
+    mean_step = np.mean([np.outer(xi, xi @ u) - u @ np.outer(xi @ u, xi @ u) for xi in x], axis=0)
+    assert np.max(np.abs(oracle.oja_update(u, x, eta) - oracle.orthonormalise(u + eta * mean_step))) < 1e-14
+    full = orthonormal(rng, D)
+    assert np.max(np.abs(oracle.oja_update(full, x, 0.3) - full)) < 1e-10
+    assert np.array_equal(oracle.oja_update(u, np.zeros((0, D)), 0.3), u)
+
+
+def pin_versions_reduce_and_brute_force():
+    """Codes made under two basis versions: equal versions give the one-basis
+    decode; distinct versions match brute force on the cache reconstructed
+    token by token with each token's own basis, anchors included."""
+    rng = np.random.default_rng(35)
+    n, w, g, rk, rv = 40, 4, 2, 16, 8
+    cpos, apos = oracle.code_positions(n, w), oracle.anchor_positions(n, w)
+    k = rng.standard_normal((n, D))
+    v = rng.standard_normal((n, D))
+    q = rng.standard_normal((g, D)) * 2
+    bk = [orthonormal(rng, rk), orthonormal(rng, rk)]
+    bv = [orthonormal(rng, rv), orthonormal(rng, rv)]
+    ver = (np.arange(len(cpos)) >= 20).astype(int)
+    ck = np.stack([k[j] @ bk[vj] for j, vj in zip(cpos, ver)])
+    cv = np.stack([v[j] @ bv[vj] for j, vj in zip(cpos, ver)])
+    sc = oracle.default_scale()
+    same = oracle.oracle_decode_unit_versions(q, [bk[0], bk[0]], [bv[0], bv[0]], ver,
+                                              k[cpos] @ bk[0], v[cpos] @ bv[0], k[apos], v[apos], sc)
+    ref = oracle.oracle_decode_unit(q, bk[0], bv[0], k[cpos] @ bk[0], v[cpos] @ bv[0], k[apos], v[apos], sc)
+    assert np.max(np.abs(same - ref)) < 1e-12
+    got = oracle.oracle_decode_unit_versions(q, bk, bv, ver, ck, cv, k[apos], v[apos], sc)
+    khat = np.concatenate([np.stack([bk[vj] @ c for c, vj in zip(ck, ver)]), k[apos]])
+    vhat = np.concatenate([np.stack([bv[vj] @ c for c, vj in zip(cv, ver)]), v[apos]])
+    for i in range(g):
+        want, _ = brute_attention(q[i], khat, vhat, sc)
+        assert np.max(np.abs(got[i] - want)) < 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -50,7 +50,39 @@ MUTANTS = {
     "q4_ties_away_from_zero": ("quantize_codes_q4", lambda x: _q8_variant(x, rounding="away", divisor=7, qmax=7)),
     "q4_scale_over_8": ("quantize_codes_q4", lambda x: _q8_variant(x, divisor=8, qmax=7)),
     "q4_clip_at_8": ("quantize_codes_q4", lambda x: _q8_variant(x, divisor=7.5, qmax=8)),
+    "oja_decay_term_sign": ("oja_update", lambda u, x, eta: _oja_variant(u, x, eta, sign=+1)),
+    "oja_not_averaged": ("oja_update", lambda u, x, eta: _oja_variant(u, x, eta, average=False)),
+    "oja_not_orthonormalised": ("oja_update", lambda u, x, eta: _oja_variant(u, x, eta, orth=False)),
+    "oja_gram_schmidt_reversed": ("oja_update", lambda u, x, eta: _oja_variant(u, x, eta, reverse=True)),
+    "versions_one_key_basis": ("oracle_decode_unit_versions", lambda *a: _versions_variant(*a, key_v0=True)),
+    "versions_one_value_basis": ("oracle_decode_unit_versions", lambda *a: _versions_variant(*a, val_v0=True)),
 }
+
+
+def _oja_variant(u, x, eta, sign=-1, average=True, orth=True, reverse=False):
+    u = np.asarray(u, float)
+    x = np.asarray(x, float)
+    if len(x) == 0:
+        return u.copy()
+    y = x @ u
+    step = x.T @ y + sign * (u @ (y.T @ y))
+    if average:
+        step = step / len(x)
+    a = u + eta * step
+    if not orth:
+        return a
+    if reverse:
+        return lo.orthonormalise(a[:, ::-1])[:, ::-1]
+    return lo.orthonormalise(a)
+
+
+def _versions_variant(q, bases_k, bases_v, versions, c_k, c_v, k_a, v_a, scale, key_v0=False, val_v0=False):
+    bk = [bases_k[0]] * len(bases_k) if key_v0 else bases_k
+    bv = [bases_v[0]] * len(bases_v) if val_v0 else bases_v
+    return _ORIG_VERSIONS(q, bk, bv, versions, c_k, c_v, k_a, v_a, scale)
+
+
+_ORIG_VERSIONS = lo.oracle_decode_unit_versions
 
 
 def _q8_variant(x, rounding="even", divisor=127, qmax=127):
