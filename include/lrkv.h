@@ -61,6 +61,7 @@ typedef enum lrkv_dtype {
 #define LRKV_MAX_KV_HEADS 64  /* per layer */
 #define LRKV_MAX_GROUP 16     /* query heads per KV head */
 #define LRKV_MAX_SPLITS 1024
+#define LRKV_MAX_VERSIONS 16  /* basis versions per layer */
 
 /*
  * One layer of compressed cache.  Storage type `dtype` applies to the bases, the
@@ -74,6 +75,9 @@ typedef enum lrkv_dtype {
  *   U_K(h)^T as [rank_k[h]][128], and right after it U_V(h)^T as [rank_v[h]][128];
  *   U_K(h) starts at element 128 * sum_{h' < h} (rank_k[h'] + rank_v[h']).  A code
  *   is x U: column c of a code is the dot product of x with basis row c.
+ *   With basis versions (n_versions > 1, see below) `bases` holds n_versions
+ *   copies of this layout back to back: version v starts at element
+ *   v * 128 * sum_h (rank_k[h] + rank_v[h]).
  *
  * codes_k, codes_v (device): the heads in order; head h owns `batch * cap * r`
  *   elements (r = rank_k[h] resp. rank_v[h]), starting at element
@@ -124,6 +128,13 @@ typedef struct lrkv_layer {
   void *anchor_v;         /* device */
   float *scales_k;        /* device, LRKV_BF16_Q8 and _Q4 only (may be NULL otherwise) */
   float *scales_v;        /* device, LRKV_BF16_Q8 and _Q4 only */
+  int32_t n_versions;     /* basis versions held in `bases`, 1 .. LRKV_MAX_VERSIONS
+                             (0 is read as 1) */
+  const int32_t *version_start; /* device [batch][n_versions] when n_versions > 1 (else
+                             ignored): the first code slot of each version in row b;
+                             version 0 starts at 0, starts are multiples of 32 and
+                             non-decreasing.  Code slot j of row b was made with the
+                             last version whose start is <= j. */
 } lrkv_layer;
 
 /*
@@ -155,6 +166,32 @@ lrkv_status lrkv_compress(const lrkv_layer *L, int32_t which, const void *x,
 lrkv_status lrkv_quantize(const lrkv_layer *L, int32_t which, const float *x,
                           int64_t stride_b, int64_t stride_h, int64_t stride_t,
                           int32_t n_tok, int32_t slot0, lrkv_stream_t stream);
+
+/*
+ * Online basis adaptation (OjaKV summary and FAQ: Oja's algorithm for online PCA
+ * keeps adapting the projection basis, thoroughly during prompt prefill and now
+ * and then during decoding; the page gives no update rule, so this is the
+ * textbook subspace rule).  For every KV head h, with U = U_K(h) (which = 0) or
+ * U_V(h) (which = 1) of basis version `version_in` and the rows x[b, h, t, :] for
+ * b < batch, t < n_tok (N = batch * n_tok rows):
+ *   C  = sum over the rows of x x^T                      (float32)
+ *   U' = U + eta (C U - U (U^T C U)) / N
+ *   U_new = the columns of U' orthonormalised in order (modified Gram-Schmidt,
+ *           float32), stored as bfloat16 U^T rows into version `version_out`
+ *           (which may equal version_in).  The other matrix of version_out is
+ *           left as it is.
+ *   x: device bfloat16, element (b, h, t, i) at x + b*stride_b + h*stride_h + t*stride_t + i.
+ *   workspace: device, >= lrkv_oja_workspace_size(L) bytes, needs no initialisation.
+ * Errors: LRKV_ERR_DTYPE for float32 layers; LRKV_ERR_SHAPE if n_tok < 1, a stride
+ * is negative, eta is not finite or a version is outside [0, n_versions);
+ * LRKV_ERR_ALIGN as lrkv_compress; LRKV_ERR_WORKSPACE if the workspace is short.
+ */
+size_t lrkv_oja_workspace_size(const lrkv_layer *L);
+lrkv_status lrkv_oja_update(const lrkv_layer *L, int32_t which, const void *x,
+                            int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                            int32_t n_tok, float eta, int32_t version_in,
+                            int32_t version_out, void *workspace, size_t workspace_bytes,
+                            lrkv_stream_t stream);
 
 /*
  * Full-rank anchors (OjaKV FAQ: the first token and the most recent tokens are

@@ -48,6 +48,7 @@ class lrkv_layer(ctypes.Structure):
         ("bases", c_void_p), ("codes_k", c_void_p), ("codes_v", c_void_p),
         ("anchor_k", c_void_p), ("anchor_v", c_void_p),
         ("scales_k", c_void_p), ("scales_v", c_void_p),
+        ("n_versions", c_int32), ("version_start", c_void_p),
     ]
 
 
@@ -59,6 +60,9 @@ _P = POINTER(lrkv_layer)
 SIGNATURES = [
     ("lrkv_compress", c_int32, [_P, c_int32, c_void_p, c_int64, c_int64, c_int64, c_int32, c_int32, c_void_p]),
     ("lrkv_quantize", c_int32, [_P, c_int32, c_void_p, c_int64, c_int64, c_int64, c_int32, c_int32, c_void_p]),
+    ("lrkv_oja_workspace_size", c_size_t, [_P]),
+    ("lrkv_oja_update", c_int32, [_P, c_int32, c_void_p, c_int64, c_int64, c_int64, c_int32, c_float,
+                                  c_int32, c_int32, c_void_p, c_size_t, c_void_p]),
     ("lrkv_store_anchors", c_int32, [_P, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int32, c_int32, c_void_p]),
     ("lrkv_append", c_int32, [_P, c_void_p, c_void_p, c_int32, c_void_p]),
     ("lrkv_decode_workspace_size", c_size_t, [_P, c_int32]),
@@ -138,6 +142,8 @@ class Layer:
     anchor_v: "object"
     scales_k: "object" = None  # quantised codes only: float32 [n_kv_heads][batch][cap]
     scales_v: "object" = None
+    n_versions: int = 1
+    version_start: "object" = None  # int32 [batch][n_versions] (device) when n_versions > 1
     _rk: object = field(default=None, repr=False)
     _rv: object = field(default=None, repr=False)
     struct: lrkv_layer = field(default=None, repr=False)
@@ -149,7 +155,8 @@ class Layer:
             self.dtype, self.batch, self.n_q_heads, self.n_kv_heads, self.window, self.cap,
             ctypes.cast(self._rk, POINTER(c_int32)), ctypes.cast(self._rv, POINTER(c_int32)),
             _ptr(self.bases), _ptr(self.codes_k), _ptr(self.codes_v),
-            _ptr(self.anchor_k), _ptr(self.anchor_v), _ptr(self.scales_k), _ptr(self.scales_v))
+            _ptr(self.anchor_k), _ptr(self.anchor_v), _ptr(self.scales_k), _ptr(self.scales_v),
+            int(self.n_versions), _ptr(self.version_start))
 
     @property
     def group(self) -> int:
@@ -172,7 +179,7 @@ class Layer:
     @classmethod
     def allocate(cls, *, dtype: int, batch: int, n_q_heads: int, n_kv_heads: int, window: int,
                  cap: int, rank_k: Sequence[int], rank_v: Sequence[int], device="cuda",
-                 bases=None) -> "Layer":
+                 bases=None, n_versions: int = 1) -> "Layer":
         """Allocate zeroed codes and anchors (and int8 scales) (torch) for the given
         geometry.  ``bases`` (optional) is the flat bases tensor; otherwise zeros."""
         import torch
@@ -182,7 +189,7 @@ class Layer:
         rk = np.asarray(rank_k, np.int32)
         rv = np.asarray(rank_v, np.int32)
         cap = layout.round_cap(cap)
-        nb = layout.bases_elems(rk, rv)
+        nb = layout.bases_elems(rk, rv) * n_versions   # one copy of the layout per version
         if bases is None:
             bases = torch.zeros(nb, dtype=td, device=device)
         assert bases.numel() == nb and bases.dtype == td
@@ -195,7 +202,9 @@ class Layer:
             sk = torch.zeros(max(1, layout.scales_elems(n_kv_heads, batch, cap)), dtype=torch.float32,
                              device=device)
             sv = torch.zeros_like(sk)
-        return cls(dtype, batch, n_q_heads, n_kv_heads, window, cap, rk, rv, bases, ck, cv, ak, av, sk, sv)
+        vs = torch.zeros((batch, n_versions), dtype=torch.int32, device=device) if n_versions > 1 else None
+        return cls(dtype, batch, n_q_heads, n_kv_heads, window, cap, rk, rv, bases, ck, cv, ak, av, sk, sv,
+                   n_versions, vs)
 
 
 # ---------------------------------------------------------------------------
@@ -219,6 +228,25 @@ def lrkv_quantize(layer: Layer, which: int, x, n_tok: int, slot0: int, stream=No
     assert si == 1
     _check(lib().lrkv_quantize(ctypes.byref(layer.struct), which, _ptr(x), sb, sh, st, n_tok, slot0,
                                _stream(stream)), "lrkv_quantize")
+
+
+def lrkv_oja_workspace_size(layer: Layer) -> int:
+    return int(lib().lrkv_oja_workspace_size(ctypes.byref(layer.struct)))
+
+
+def lrkv_oja_update(layer: Layer, which: int, x, n_tok: int, eta: float, version_in: int, version_out: int,
+                    ws=None, stream=None):
+    """x: bf16 device tensor viewed as [batch][n_kv_heads][>= n_tok][128] (last
+    dimension contiguous).  ``ws``: workspace (uint8 device tensor) or None to
+    allocate one."""
+    import torch
+    sb, sh, st, si = x.stride()
+    assert si == 1
+    if ws is None:
+        ws = torch.empty(max(1, lrkv_oja_workspace_size(layer)), dtype=torch.uint8, device=x.device)
+    _check(lib().lrkv_oja_update(ctypes.byref(layer.struct), which, _ptr(x), sb, sh, st, n_tok, eta,
+                                 version_in, version_out, _ptr(ws), ws.numel(), _stream(stream)),
+           "lrkv_oja_update")
 
 
 def lrkv_store_anchors(layer: Layer, k, v, pos0: int, n_tok: int, stream=None):

@@ -34,6 +34,10 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   if (!aligned16(L->bases) || !aligned16(L->codes_k) || !aligned16(L->codes_v) ||
       !aligned16(L->anchor_k) || !aligned16(L->anchor_v))
     return LRKV_ERR_ALIGN;
+  const int32_t nver = L->n_versions == 0 ? 1 : L->n_versions;
+  if (nver < 1 || nver > LRKV_MAX_VERSIONS) return LRKV_ERR_SHAPE;
+  if (nver > 1 && !L->version_start) return LRKV_ERR_NULL;
+  if (nver > 1 && (reinterpret_cast<uintptr_t>(L->version_start) & 3u)) return LRKV_ERR_ALIGN;
   if (quantised(L->dtype)) {
     if (!L->scales_k || !L->scales_v) return LRKV_ERR_NULL;
     if (!aligned16(L->scales_k) || !aligned16(L->scales_v)) return LRKV_ERR_ALIGN;
@@ -71,6 +75,9 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
     rv_max = rv > rv_max ? rv : rv_max;
   }
   A->rv_max = rv_max;
+  A->n_versions = nver;
+  A->vstart = nver > 1 ? L->version_start : nullptr;
+  A->version_elems = ub;
   return LRKV_OK;
 }
 
@@ -170,6 +177,34 @@ lrkv_status lrkv_quantize(const lrkv_layer *L, int32_t which, const float *x, in
   if (reinterpret_cast<uintptr_t>(x) & 3u) return LRKV_ERR_ALIGN;
   return hip_status(launch_quantize(A, which, x, stride_b, stride_h, stride_t, n_tok, slot0,
                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t lrkv_oja_workspace_size(const lrkv_layer *L) {
+  LayerArgs A;
+  if (make_layer(L, &A) != LRKV_OK) return 0;
+  return oja_workspace_bytes(A);
+}
+
+lrkv_status lrkv_oja_update(const lrkv_layer *L, int32_t which, const void *x, int64_t stride_b,
+                            int64_t stride_h, int64_t stride_t, int32_t n_tok, float eta,
+                            int32_t version_in, int32_t version_out, void *workspace,
+                            size_t workspace_bytes, lrkv_stream_t stream) {
+  LayerArgs A;
+  lrkv_status st = make_layer(L, &A);
+  if (st != LRKV_OK) return st;
+  if (L->dtype == LRKV_F32) return LRKV_ERR_DTYPE;
+  if (which != 0 && which != 1) return LRKV_ERR_SHAPE;
+  if (n_tok < 1 || !(eta == eta) || eta > 3.4e38f || eta < -3.4e38f) return LRKV_ERR_SHAPE;
+  if (version_in < 0 || version_in >= A.n_versions || version_out < 0 || version_out >= A.n_versions)
+    return LRKV_ERR_SHAPE;
+  if (!x) return LRKV_ERR_NULL;
+  st = check_strides(L, x, stride_b, stride_h, stride_t);
+  if (st != LRKV_OK) return st;
+  if (!workspace || workspace_bytes < oja_workspace_bytes(A)) return LRKV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LRKV_ERR_ALIGN;
+  return hip_status(launch_oja(A, which, x, stride_b, stride_h, stride_t, n_tok, eta, version_in,
+                               version_out, static_cast<float *>(workspace),
+                               reinterpret_cast<hipStream_t>(stream)));
 }
 
 lrkv_status lrkv_store_anchors(const lrkv_layer *L, const void *k, const void *v, int64_t stride_b,

@@ -24,6 +24,9 @@ struct LayerArgs {
   const void *bases;
   void *codes_k, *codes_v, *anchor_k, *anchor_v;
   float *scales_k, *scales_v;  // quantised codes: one scale per (head, row, slot)
+  int32_t n_versions;          // basis versions (>= 1)
+  const int32_t *vstart;       // [batch][n_versions] first code slot of each version (n_versions > 1)
+  int64_t version_elems;       // elements of one version of the bases
   HeadInfo heads[LRKV_MAX_KV_HEADS];
 };
 
@@ -140,5 +143,8 @@ hipError_t launch_append(const LayerArgs &L, const void *k, const void *v, int p
 hipError_t launch_decode_partials(const LayerArgs &L, const DecodeArgs &d, hipStream_t s);
 hipError_t launch_partials_mfma(const LayerArgs &L, const DecodeArgs &d, hipStream_t s);
 hipError_t launch_decode_combine(const LayerArgs &L, const DecodeArgs &d, float *out, hipStream_t s);
+hipError_t launch_oja(const LayerArgs &L, int which, const void *x, int64_t sb, int64_t sh, int64_t st,
+                      int n_tok, float eta, int vin, int vout, float *ws, hipStream_t s);
+size_t oja_workspace_bytes(const LayerArgs &L);
 
 }  // namespace lrkv

@@ -188,3 +188,35 @@ def test_quantize_validation():
     assert f(L=layer(dtype=2, scales_v=None)) == 1
     assert f(L=layer(dtype=3), n=60, slot0=5) == 6     # 4-bit layers take the same checks
     assert f(L=layer(dtype=3), x=FAKE + 2) == 5
+
+
+def test_versions_validation():
+    # 0 versions is read as 1; more than LRKV_MAX_VERSIONS (16) or a missing or
+    # misaligned start table is rejected
+    assert decode(layer(n_versions=0), q=None) == 1
+    L = layer()
+    L.n_versions = 17
+    assert decode(L) == 2
+    L.n_versions = 2
+    assert decode(L) == 1                   # version_start missing
+    L.version_start = FAKE + 2
+    assert decode(L) == 5
+
+
+def test_oja_validation():
+    lib = B.lib()
+    L = layer()
+    need = lib.lrkv_oja_workspace_size(ctypes.byref(L))
+    assert need == 2 * 64 * 36 * 256 * 4     # 2 KV heads x 64 workgroup partials of 36 tiles
+    f = lambda L=L, **k: lib.lrkv_oja_update(ctypes.byref(L), k.get("which", 0), k.get("x", FAKE), 1024, 512,
+                                             128, k.get("n", 10), k.get("eta", 0.5), k.get("vin", 0),
+                                             k.get("vout", 0), k.get("ws", FAKE), k.get("wsb", need), None)
+    assert f(L=layer(dtype=0)) == 4
+    assert f(which=2) == 2
+    assert f(n=0) == 2
+    assert f(eta=float("nan")) == 2
+    assert f(vout=1) == 2                    # one version only
+    assert f(x=None) == 1
+    assert f(x=FAKE + 2) == 5
+    assert f(wsb=need - 1) == 7
+    assert f(ws=None) == 7
