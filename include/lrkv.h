@@ -129,7 +129,8 @@ typedef struct lrkv_layer {
   float *scales_k;        /* device, LRKV_BF16_Q8 and _Q4 only (may be NULL otherwise) */
   float *scales_v;        /* device, LRKV_BF16_Q8 and _Q4 only */
   int32_t n_versions;     /* basis versions held in `bases`, 1 .. LRKV_MAX_VERSIONS
-                             (0 is read as 1) */
+                             (0 is read as 1; more than 1 needs bf16 bases:
+                             LRKV_ERR_DTYPE for float32 layers) */
   const int32_t *version_start; /* device [batch][n_versions] when n_versions > 1 (else
                              ignored): the first code slot of each version in row b;
                              version 0 starts at 0, starts are multiples of 32 and
@@ -143,7 +144,8 @@ typedef struct lrkv_layer {
  * slot0 + t of `which` (0 = keys with U_K, 1 = values with U_V) receives
  * x[b, h, t, :] U, rounded to the storage type (bf16: round to nearest even of
  * the float32 accumulation; LRKV_BF16_Q8 / _Q4: the float32 accumulation
- * quantised to int8 / 4 bits with its scale, as described above).
+ * quantised to int8 / 4 bits with its scale, as described above).  With basis
+ * versions the latest version (n_versions - 1) is used.
  *   x: device, element (b, h, t, i) at x + b*stride_b + h*stride_h + t*stride_t + i
  *      (strides in elements of the storage type; the 128 features contiguous).
  * Errors: LRKV_ERR_SHAPE if n_tok < 0, slot0 < 0 or a stride is negative;
@@ -182,6 +184,8 @@ lrkv_status lrkv_quantize(const lrkv_layer *L, int32_t which, const float *x,
  *           left as it is.
  *   x: device bfloat16, element (b, h, t, i) at x + b*stride_b + h*stride_h + t*stride_t + i.
  *   workspace: device, >= lrkv_oja_workspace_size(L) bytes, needs no initialisation.
+ * The kernels write into `bases` (version_out) although the layer describes it
+ * as const for every other call.
  * Errors: LRKV_ERR_DTYPE for float32 layers; LRKV_ERR_SHAPE if n_tok < 1, a stride
  * is negative, eta is not finite or a version is outside [0, n_versions);
  * LRKV_ERR_ALIGN as lrkv_compress; LRKV_ERR_WORKSPACE if the workspace is short.
@@ -214,6 +218,8 @@ lrkv_status lrkv_store_anchors(const lrkv_layer *L, const void *k, const void *v
  *    with its scale for LRKV_BF16_Q8 / _Q4), then the new token takes over that slot.
  *  - window == 0 and pos >= 1: the new token is compressed into code slot pos - 1.
  *  - otherwise the new token is stored into its anchor slot.
+ * With basis versions the code is made with the version the code slot belongs
+ * to (version_start of the row).
  * Errors: LRKV_ERR_SHAPE if pos < 0; LRKV_ERR_CAPACITY if the code slot >= cap.
  */
 lrkv_status lrkv_append(const lrkv_layer *L, const void *k_new, const void *v_new,
@@ -233,7 +239,11 @@ lrkv_status lrkv_append(const lrkv_layer *L, const void *k_new, const void *v_ne
  * n_splits: the compressed tokens of each (row, KV head) are cut into this many
  *   contiguous ranges of 32-slot blocks, each scored by its own workgroup
  *   (1 .. LRKV_MAX_SPLITS; 0 = lrkv_decode_auto_splits).  Results agree across
- *   n_splits to rounding; a fixed n_splits is bitwise reproducible.
+ *   n_splits to rounding; a fixed n_splits is bitwise reproducible.  With basis
+ *   versions (OjaKV: codes keep the basis they were made with) every version
+ *   gets its own splits, so n_splits >= n_versions (else LRKV_ERR_SHAPE); a
+ *   code token is scored against the query projected with its version's U_K
+ *   and its value sum is up-projected with its version's U_V.
  * workspace: device, >= lrkv_decode_workspace_size(L, n_splits) bytes, float32
  *   split records; needs no initialisation, and lrkv_decode_partials rewrites
  *   every record lrkv_decode_combine reads.

@@ -36,6 +36,7 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
     return LRKV_ERR_ALIGN;
   const int32_t nver = L->n_versions == 0 ? 1 : L->n_versions;
   if (nver < 1 || nver > LRKV_MAX_VERSIONS) return LRKV_ERR_SHAPE;
+  if (nver > 1 && L->dtype == LRKV_F32) return LRKV_ERR_DTYPE;
   if (nver > 1 && !L->version_start) return LRKV_ERR_NULL;
   if (nver > 1 && (reinterpret_cast<uintptr_t>(L->version_start) & 3u)) return LRKV_ERR_ALIGN;
   if (quantised(L->dtype)) {
@@ -95,6 +96,7 @@ int32_t auto_splits(const LayerArgs &A, int32_t n_ctx) {
   if (s > most) s = most;
   if (s < 1) s = 1;
   if (s > LRKV_MAX_SPLITS) s = LRKV_MAX_SPLITS;
+  if (s < A.n_versions) s = A.n_versions;  // every basis version needs a split
   return int32_t(s);
 }
 
@@ -120,6 +122,7 @@ lrkv_status make_decode(const lrkv_layer *L, const LayerArgs &A, int32_t n_ctx,
   if (n_splits < 0 || n_splits > LRKV_MAX_SPLITS) return LRKV_ERR_SHAPE;
   if (!(sm_scale > 0.f) || sm_scale != sm_scale) return LRKV_ERR_SHAPE;
   const int32_t S = n_splits ? n_splits : auto_splits(A, n_ctx);
+  if (S < A.n_versions) return LRKV_ERR_SHAPE;
   if (!ws) return LRKV_ERR_WORKSPACE;
   if (ws_len < ws_bytes(A, S)) return LRKV_ERR_WORKSPACE;
   if (!aligned16(ws) || (ctx_lens && (reinterpret_cast<uintptr_t>(ctx_lens) & 3u)))

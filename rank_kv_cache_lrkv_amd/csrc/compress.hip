@@ -110,8 +110,12 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
   }
   __syncthreads();
   if (code_slot >= 0) {  // uniform over the workgroup
-    const T *Uk = static_cast<const T *>(L.bases) + hd.u_k;
-    const T *Uv = static_cast<const T *>(L.bases) + hd.u_v;
+    // basis version of the slot: the last one starting at or before it
+    int ver = 0;
+    for (int v = 1; v < L.n_versions; ++v)
+      if (L.vstart[int64_t(b) * L.n_versions + v] <= code_slot) ver = v;
+    const T *Uk = static_cast<const T *>(L.bases) + ver * L.version_elems + hd.u_k;
+    const T *Uv = static_cast<const T *>(L.bases) + ver * L.version_elems + hd.u_v;
     float acck = 0.f, accv = 0.f;
     if (tid < hd.rk)
       for (int k = 0; k < kD; ++k) acck = fmaf(rk_row[k], to_f32(Uk[tid * kD + k]), acck);

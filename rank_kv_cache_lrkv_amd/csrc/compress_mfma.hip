@@ -53,7 +53,9 @@ __global__ __launch_bounds__(256) void k_compress_mfma(LayerArgs L, int which, c
   const int b = unit / L.n_kv, h = unit % L.n_kv;
   const HeadInfo hd = L.heads[h];
   const int r = which ? hd.rv : hd.rk;
-  const bf16_t *ut = static_cast<const bf16_t *>(L.bases) + (which ? hd.u_v : hd.u_k);
+  // the latest basis version (prefill compresses before later versions appear)
+  const bf16_t *ut = static_cast<const bf16_t *>(L.bases) + (L.n_versions - 1) * L.version_elems +
+                     (which ? hd.u_v : hd.u_k);
   const int64_t region = (which ? hd.cv : hd.ck) + int64_t(b) * L.cap * r;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -212,6 +212,61 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, floa
 }
 
 // ---------------------------------------------------------------------------
+// Stage 2 with basis versions (codes made under several bases, OjaKV): each
+// version's rank-space sum is merged from that version's splits and
+// up-projected with that version's U_V; the rest is as in k_combine.  One
+// workgroup of 128 threads per (query head, batch row), thread t = output
+// feature t.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(128) void k_combine_versions(LayerArgs L, DecodeArgs d, float *out) {
+  __shared__ float sot[128];
+  const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int h = i / L.group;
+  const HeadInfo hd = L.heads[h];
+  const int rv = hd.rv;
+  const int S = d.n_splits;
+  const int64_t qi = int64_t(b) * L.n_q + i;
+  const int n = row_ctx(d, b);
+  const int c = max(0, n - 1 - L.window);
+  const int nblk = (c + kBlock - 1) / kBlock;
+  const int a = min(n, 1 + L.window);
+  const int per = anchor_rows_per_split(a, S);
+  const int sa = min(S, (a + per - 1) / per);  // splits 0 .. sa-1 carry anchor sums
+
+  float M = kNegInf;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, split_record(d, qi, s)[0]);  // finite: anchors exist
+  float Ltot = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float *r = split_record(d, qi, s);
+    if (r[0] != kNegInf) Ltot = fmaf(fast_exp2(r[0] - M), r[1], Ltot);
+  }
+  float y = 0.f;
+  for (int v = 0; v < L.n_versions; ++v) {
+    // this version's merged rank-space sum (the splits of a version are consecutive)
+    if (t < rv) {
+      float o = 0.f;
+      for (int s = 0; s < S; ++s) {
+        if (split_segment(L, b, s, S, nblk).v != v) continue;
+        const float *r = split_record(d, qi, s);
+        if (r[0] != kNegInf) o = fmaf(fast_exp2(r[0] - M), r[4 + t], o);
+      }
+      sot[t] = o;
+    }
+    __syncthreads();
+    const T *uvt = static_cast<const T *>(L.bases) + v * L.version_elems + hd.u_v;  // U_V^T rows
+    for (int cc = 0; cc < rv; ++cc) y = fmaf(to_f32(uvt[cc * kD + t]), sot[cc], y);
+    __syncthreads();
+  }
+  float oa = 0.f;
+  for (int s = 0; s < sa; ++s) {
+    const float *r = split_record(d, qi, s);
+    oa = fmaf(fast_exp2(r[0] - M), r[d.oa + t], oa);
+  }
+  out[qi * kD + t] = (y + oa) / Ltot;
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_decode_partials(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
@@ -223,7 +278,9 @@ hipError_t launch_decode_partials(const LayerArgs &L, const DecodeArgs &d, hipSt
 
 hipError_t launch_decode_combine(const LayerArgs &L, const DecodeArgs &d, float *out, hipStream_t s) {
   dim3 grid(L.n_q, L.batch);
-  if (L.dtype == LRKV_F32)
+  if (L.n_versions > 1)  // float32 layers have one version
+    hipLaunchKernelGGL(k_combine_versions<bf16_t>, grid, dim3(kD), 0, s, L, d, out);
+  else if (L.dtype == LRKV_F32)
     hipLaunchKernelGGL(k_combine<float>, grid, dim3(kD), 0, s, L, d, out);
   else
     hipLaunchKernelGGL(k_combine<bf16_t>, grid, dim3(kD), 0, s, L, d, out);

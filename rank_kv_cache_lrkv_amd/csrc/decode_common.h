@@ -53,6 +53,41 @@ __device__ __forceinline__ void anchor_share(int a, int split, int S, int &lo, i
   hi = min(lo + per, a);
 }
 
+// Basis versions: the code blocks of a row form one segment per version
+// (version v owns blocks [B_v, B_v+1), B_v = its first slot / 32, clamped to the
+// row's nblk), and the S splits are shared out so that every version has at
+// least one: version v's splits start at P_v = v + (S - V) B_v / nblk.
+struct SplitSeg {
+  int v;        // basis version
+  int s, ns;    // split index inside the version, splits of the version
+  int lo, hi;   // code blocks [lo, hi) of the version
+};
+__device__ __forceinline__ SplitSeg split_segment(const LayerArgs &L, int b, int split, int S, int nblk) {
+  SplitSeg g{0, split, S, 0, nblk};
+  const int V = L.n_versions;
+  if (V <= 1) return g;
+  const int32_t *vs = L.vstart + int64_t(b) * V;
+  auto blk = [&](int v) {  // B_v, non-decreasing, in [0, nblk]
+    if (v <= 0) return 0;
+    if (v >= V) return nblk;
+    int bv = vs[v] / kBlock;
+    return bv < 0 ? 0 : (bv > nblk ? nblk : bv);
+  };
+  auto first = [&](int v) {
+    if (v >= V) return S;
+    return v + int((int64_t(S - V) * blk(v)) / (nblk > 0 ? nblk : 1));
+  };
+  int v = 0;
+  while (v + 1 < V && first(v + 1) <= split) ++v;
+  const int p0 = first(v), p1 = first(v + 1);
+  g.v = v;
+  g.s = split - p0;
+  g.ns = p1 - p0;
+  g.lo = blk(v);
+  g.hi = max(g.lo, blk(v + 1));
+  return g;
+}
+
 // code blocks [lo, hi) of split s out of nblk (contiguous ranges)
 __device__ __forceinline__ void block_share(int nblk, int split, int S, int &lo, int &hi) {
   lo = int((int64_t(split) * nblk) / S);

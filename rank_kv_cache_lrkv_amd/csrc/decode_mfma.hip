@@ -185,15 +185,18 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   anchor_share(min(n, 1 + W), split, S, alo, ahi);
   const int na = ahi - alo;
   const int64_t q0 = int64_t(b) * L.n_q + h * G;
-  const int first = 4 * split + wave, step = 4 * S;
+  // with basis versions the split sweeps its version's blocks [sg.lo, sg.hi)
+  const SplitSeg sg = split_segment(L, b, split, S, nblk);
+  const int bhi = sg.hi;
+  const int first = sg.lo + 4 * sg.s + wave, step = 4 * sg.ns;
   // When every workgroup is resident at once, the older workgroups on a compute unit
   // get their loads served first and the youngest would stream alone at the end;
   // the waves with the larger share of their blocks still to read get the higher
   // issue priority instead, so all of them finish together.
-  const int total = first < nblk ? (nblk - first + step - 1) / step : 0;  // this wave's blocks
+  const int total = first < bhi ? (bhi - first + step - 1) / step : 0;  // this wave's blocks
   auto set_priority = [&](int blk) {
     if (!d.balance) return;
-    const int left = (4 * ((nblk - blk + step - 1) / step)) / (total + 1);  // 0..3
+    const int left = (4 * ((bhi - blk + step - 1) / step)) / (total + 1);  // 0..3
     if (left >= 3) __builtin_amdgcn_s_setprio(3);
     else if (left == 2) __builtin_amdgcn_s_setprio(2);
     else if (left == 1) __builtin_amdgcn_s_setprio(1);
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   };
   if (d.balance) __builtin_amdgcn_s_setprio(3);
 
-  if (4 * split >= nblk && na == 0) {  // nothing for this split
+  if (4 * sg.s >= bhi - sg.lo && na == 0) {  // nothing for this split
     for (int i = tid; i < G; i += blockDim.x) {
       float *rec = split_record(d, q0 + i, split);
       rec[0] = kNegInf;
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   // complete in order, so waiting for the prologue operands never waits for the
   // code blocks, and the barriers below wait for LDS traffic only.
   const bf16_t *qb = static_cast<const bf16_t *>(d.q) + q0 * kD;
-  const bf16_t *ut = static_cast<const bf16_t *>(L.bases) + hd.u_k;
+  const bf16_t *ut = static_cast<const bf16_t *>(L.bases) + sg.v * L.version_elems + hd.u_k;
   constexpr int NT = RKMAX / 16;
   constexpr int NTW = (NT + 3) / 4;  // column tiles of q~ per wave
   // every load below is unconditional, from a clamped in-bounds address; what is
@@ -544,18 +547,18 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   // ahead of the current block's work: hoisting that work above them would make
   // the wave wait for the current block with nothing else in flight.
   int j = first;
-  if (j < nblk) {
+  if (j < bhi) {
     while (true) {
-      load(j + step < nblk ? j + step : j, r1);
+      load(j + step < bhi ? j + step : j, r1);
       __builtin_amdgcn_sched_barrier(0);
       process(j, r0);
       j += step;
-      if (j >= nblk) break;
-      load(j + step < nblk ? j + step : j, r0);
+      if (j >= bhi) break;
+      load(j + step < bhi ? j + step : j, r0);
       __builtin_amdgcn_sched_barrier(0);
       process(j, r1);
       j += step;
-      if (j >= nblk) break;
+      if (j >= bhi) break;
     }
   }
 
