@@ -2,9 +2,11 @@
 Oja step (oracle.oja_update), on the same bf16 rows and the same bf16 basis.
 
 The GPU works in float32 and stores the new basis in bf16; the oracle's float64
-result rounded to bf16 must match within one bf16 step everywhere and bit for
-bit almost everywhere (a float32 result lying next to a rounding boundary may
-round the other way).
+result rounded to bf16 must match within one bf16 step plus the float32 error
+of the computation (an absolute 4e-6 for entries of unit-norm columns: it
+matters only for entries so small that their bf16 step is finer), and bit for
+bit almost everywhere (a float32 result next to a rounding boundary may round
+the other way).
 """
 
 import numpy as np
@@ -64,10 +66,13 @@ def rows(rng, batch, n_kv, n, tau=16.0):
     return oracle.bf16_round(out).astype(np.float32)
 
 
+F32_ABS = 4e-6   # float32 error of one step on unit-norm columns
+
+
 def check_basis(got, want64, label):
     want = oracle.bf16_round(want64)
     err = np.abs(got - want)
-    worst = float(np.max(err / bf16_ulp(want + 1e-30)))
+    worst = float(np.max(err / (bf16_ulp(want + 1e-30) + F32_ABS)))
     equal = float(np.mean(got == want))
     print(f"[parity] {label}: worst {worst:.2f} bf16 steps, bit-equal {equal:.4f}", flush=True)
     assert worst <= 1.0, (label, worst)
@@ -121,7 +126,7 @@ def test_oja_in_place_and_repeated_steps():
         for step in range(3):
             u = oracle.bf16_round(oracle.oja_update(u, x[:, h].reshape(-1, D).astype(np.float64), 0.5))
         got = read_basis(L2, 0, h, 0)
-        err = np.max(np.abs(got - u) / bf16_ulp(u + 1e-30))
+        err = np.max(np.abs(got - u) / (bf16_ulp(u + 1e-30) + 3 * F32_ABS))
         print(f"[parity] chain h{h}: worst {err:.2f} bf16 steps", flush=True)
         assert err <= 2.0
 
