@@ -28,6 +28,10 @@ Readings where the pages are silent (each also listed in the design doc):
 * query head i of a GQA group reads KV head i // g;
 * codes are ``x @ U`` with U a (128, r) matrix with orthonormal columns.
 
+Group-head latents (Palu's medium-grained decomposition) share one code stream
+among the KV heads of a group, each head reading its own slice of the group
+basis; see oracle_compress_group and oracle_decode_group.
+
 Online basis adaptation (OjaKV) uses the textbook Oja subspace rule with
 re-orthonormalisation (the page names Oja's algorithm but gives no rule); codes
 made under several basis versions are decoded each with its own version; see
@@ -248,6 +252,43 @@ def oracle_decode_unit_versions(q, bases_k, bases_v, versions, c_k, c_v, k_a, v_
         sel = versions == v
         out = out + up_project(rank_space_values(e[:, :c][:, sel], c_v[sel]), bases_v[v])
     return out / total
+
+
+# ---------------------------------------------------------------------------
+# group-head latents (Palu abstract: a medium-grained low-rank decomposition
+# between one latent per head and one for all heads).  Reading: the n_g KV heads
+# of a group share one code per token, the projection of their concatenated
+# keys (values) onto one (n_g * 128, r) basis with orthonormal columns; KV head
+# j of the group reconstructs as its 128-row slice of the basis times the code.
+# ---------------------------------------------------------------------------
+
+def oracle_compress_group(x_heads, u_group) -> np.ndarray:
+    """Shared codes of a head group: x_heads (n_g, t, 128) the group's rows (head
+    by head), u_group (n_g * 128, r).  Returns (t, r): [x_1 ... x_ng] u_group."""
+    x = np.asarray(x_heads, np.float64)
+    joined = np.concatenate(list(x), axis=1)  # (t, n_g * 128), head 0's features first
+    return joined @ np.asarray(u_group, np.float64)
+
+
+def group_slice(u_group, j: int) -> np.ndarray:
+    """KV head j's (128, r) slice of a group basis: rows 128 j .. 128 j + 127."""
+    return np.asarray(u_group, np.float64)[HEAD_DIM * j:HEAD_DIM * (j + 1)]
+
+
+def oracle_decode_group(q, head_of_query, u_k_group, u_v_group, c_k, c_v, k_a, v_a,
+                        scale: float) -> np.ndarray:
+    """Decode attention of the query heads of one head group against its shared
+    codes.  q (m, 128); head_of_query (m,) the group-local KV head j of each
+    query; u_k_group (n_g * 128, r_k), u_v_group (n_g * 128, r_v); c_k (c, r_k),
+    c_v (c, r_v) shared; k_a[j], v_a[j] (a, 128) the anchors of KV head j.
+    Query i is the one-head decode with KV head j's slices of the bases, the
+    shared codes and KV head j's anchors.  Returns out (m, 128)."""
+    q = np.asarray(q, np.float64)
+    out = np.empty((q.shape[0], HEAD_DIM))
+    for i, j in enumerate(head_of_query):
+        out[i] = oracle_decode_unit(q[i:i + 1], group_slice(u_k_group, j), group_slice(u_v_group, j),
+                                    c_k, c_v, k_a[j], v_a[j], scale)[0]
+    return out
 
 
 # ---------------------------------------------------------------------------

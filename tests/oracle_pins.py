@@ -531,4 +531,57 @@ def pin_versions_reduce_and_brute_force():
         assert np.max(np.abs(got[i] - want)) < 1e-12
 
 
+# ---------------------------------------------------------------------------
+# group-head latents
+# ---------------------------------------------------------------------------
+
+def pin_group_compress_is_concatenated_projection():
+    """The shared code is the sum of each head's rows times its slice (block
+    matrix product written out), and a block-diagonal group basis gives each
+    head's own per-head codes side by side."""
+    rng = np.random.default_rng(36)
+    ng, t, r = 3, 7, 24
+    x = rng.standard_normal((ng, t, D))
+    u = np.linalg.qr(rng.standard_normal((ng * D, ng * D)))[0][:, :r]
+    want = sum(x[j] @ u[j * D:(j + 1) * D] for j in range(ng))
+    assert np.max(np.abs(oracle.oracle_compress_group(x, u) - want)) < 1e-12
+    per = [orthonormal(rng, 8) for _ in range(ng)]
+    bd = np.zeros((ng * D, ng * 8))
+    for j in range(ng):
+        bd[j * D:(j + 1) * D, j * 8:(j + 1) * 8] = per[j]
+    got = oracle.oracle_compress_group(x, bd)
+    for j in range(ng):
+        assert np.max(np.abs(got[:, j * 8:(j + 1) * 8] - x[j] @ per[j])) < 1e-12
+
+
+def pin_group_decode_brute_force():
+    """Each query head of a group against brute force on its own KV head's cache,
+    reconstructed token by token from the shared codes with that head's slice;
+    with one head per group it is the one-head decode."""
+    rng = np.random.default_rng(37)
+    ng, g, n, w, rk, rv = 2, 2, 30, 4, 16, 12
+    cpos, apos = oracle.code_positions(n, w), oracle.anchor_positions(n, w)
+    k = rng.standard_normal((ng, n, D))
+    v = rng.standard_normal((ng, n, D))
+    uk = np.linalg.qr(rng.standard_normal((ng * D, ng * D)))[0][:, :rk]
+    uv = np.linalg.qr(rng.standard_normal((ng * D, ng * D)))[0][:, :rv]
+    ck = oracle.oracle_compress_group(k[:, cpos], uk)
+    cv = oracle.oracle_compress_group(v[:, cpos], uv)
+    q = rng.standard_normal((ng * g, D)) * 2
+    heads = np.repeat(np.arange(ng), g)
+    sc = oracle.default_scale()
+    got = oracle.oracle_decode_group(q, heads, uk, uv, ck, cv, [k[j][apos] for j in range(ng)],
+                                     [v[j][apos] for j in range(ng)], sc)
+    for i, j in enumerate(heads):
+        khat = np.concatenate([reconstruct(ck, uk[j * D:(j + 1) * D]), k[j][apos]])
+        vhat = np.concatenate([reconstruct(cv, uv[j * D:(j + 1) * D]), v[j][apos]])
+        want, _ = brute_attention(q[i], khat, vhat, sc)
+        assert np.max(np.abs(got[i] - want)) < 1e-12
+    one = oracle.oracle_decode_group(q[:2], [0, 0], uk[:D], uv[:D], k[0][cpos] @ uk[:D], v[0][cpos] @ uv[:D],
+                                     [k[0][apos]], [v[0][apos]], sc)
+    ref = oracle.oracle_decode_unit(q[:2], uk[:D], uv[:D], k[0][cpos] @ uk[:D], v[0][cpos] @ uv[:D],
+                                    k[0][apos], v[0][apos], sc)
+    assert np.max(np.abs(one - ref)) < 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -56,6 +56,9 @@ MUTANTS = {
     "oja_gram_schmidt_reversed": ("oja_update", lambda u, x, eta: _oja_variant(u, x, eta, reverse=True)),
     "versions_one_key_basis": ("oracle_decode_unit_versions", lambda *a: _versions_variant(*a, key_v0=True)),
     "versions_one_value_basis": ("oracle_decode_unit_versions", lambda *a: _versions_variant(*a, val_v0=True)),
+    "group_heads_reversed": ("oracle_compress_group",
+                             lambda x, u: np.concatenate(list(np.asarray(x, float))[::-1], axis=1) @ np.asarray(u, float)),
+    "group_slice_off_by_one_head": ("group_slice", lambda u, j: np.asarray(u, float)[128 * max(j - 1, 0):128 * max(j, 1)]),
 }
 
 
