@@ -48,20 +48,22 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, n, bits=16):
+def algorithmic_bytes(w, n, bits=16, hg=1):
     """Bytes the method must move for one decode call of one layer, and the part
     the partials kernel moves (codes, anchors, U_K, q).  Quantised codes: r bytes
-    (int8) or r / 2 bytes (4-bit) per code row plus its 4-byte scale."""
+    (int8) or r / 2 bytes (4-bit) per code row plus its 4-byte scale.  Group-head
+    latents (hg KV heads per code stream): one code row per group and token, bases
+    of hg * 128 rows per group, anchors per KV head."""
     import oracle
     s = 4 if w.dtype == "f32" else 2
     c = len(oracle.code_positions(n, w.window))
     a = len(oracle.anchor_positions(n, w.window))
-    units = w.batch * w.n_kv_heads
+    units = w.batch * w.n_kv_heads // hg
     if bits < 16:
         codes = units * c * ((w.rank_k + w.rank_v) * bits // 8 + 8)
     else:
         codes = units * c * (w.rank_k + w.rank_v) * s
-    anchors = units * a * 2 * 128 * s
+    anchors = w.batch * w.n_kv_heads * a * 2 * 128 * s
     u_k = w.n_kv_heads * 128 * w.rank_k * s
     u_v = w.n_kv_heads * 128 * w.rank_v * s
     q = w.batch * w.n_q_heads * 128 * s
@@ -70,7 +72,7 @@ def algorithmic_bytes(w, n, bits=16):
             "codes": codes, "anchors": anchors}
 
 
-def build_cache(w, B, dev, bits=16):
+def build_cache(w, B, dev, bits=16, hg=1):
     """Prefill on the GPU: compress tokens 1..n-W-1, store token 0 and the window."""
     import numpy as np
     import torch
@@ -79,14 +81,20 @@ def build_cache(w, B, dev, bits=16):
     from rank_kv_cache_lrkv_amd import layout
 
     rk, rv = synth.ranks(w, 0)
-    bases = layout.pack_bases([synth.basis(w, 0, h, "k", int(rk[h])) for h in range(w.n_kv_heads)],
-                              [synth.basis(w, 0, h, "v", int(rv[h])) for h in range(w.n_kv_heads)])
+    if hg > 1:  # one basis pair per group of hg KV heads (uniform ranks)
+        n_lat = w.n_kv_heads // hg
+        rk, rv = rk[:n_lat], rv[:n_lat]
+        bases = layout.pack_bases([synth.group_basis(w, 0, g, hg, "k", int(rk[g])) for g in range(n_lat)],
+                                  [synth.group_basis(w, 0, g, hg, "v", int(rv[g])) for g in range(n_lat)])
+    else:
+        bases = layout.pack_bases([synth.basis(w, 0, h, "k", int(rk[h])) for h in range(w.n_kv_heads)],
+                                  [synth.basis(w, 0, h, "v", int(rv[h])) for h in range(w.n_kv_heads)])
     n = w.n_ctx
     c = max(0, n - 1 - w.window)
     dtype = {8: B.LRKV_BF16_Q8, 4: B.LRKV_BF16_Q4}.get(bits, B.LRKV_BF16 if w.dtype == "bf16" else B.LRKV_F32)
     L = B.Layer.allocate(dtype=dtype, batch=w.batch,
                          n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, window=w.window,
-                         cap=layout.round_cap(c), rank_k=rk, rank_v=rv, bases=dev(bases))
+                         cap=layout.round_cap(c), rank_k=rk, rank_v=rv, bases=dev(bases), head_group=hg)
     td = L.torch_dtype
     K = torch.empty((w.batch, w.n_kv_heads, n, 128), dtype=td, device="cuda")
     V = torch.empty_like(K)
@@ -108,11 +116,11 @@ def build_cache(w, B, dev, bits=16):
     ms = ev[0].elapsed_time(ev[1])
     s = 2 if w.dtype == "bf16" else 4
     row = (2 * 128 * s + (w.rank_k + w.rank_v) * bits // 8 + 8) if bits < 16 else (2 * 128 + w.rank_k + w.rank_v) * s
-    moved = w.batch * w.n_kv_heads * c * row
+    moved = w.batch * w.n_kv_heads * c * 2 * 128 * s + w.batch * (w.n_kv_heads // hg) * c * (row - 2 * 128 * s)
     compress = {"ms": round(ms, 4), "tokens": c, "alg_bytes": moved,
                 "gbps": round(moved / (ms * 1e-3) / 1e9, 1)}
     oja = None
-    if bits == 16 and w.dtype == "bf16":
+    if bits == 16 and w.dtype == "bf16" and hg == 1:
         # one Oja step of the key bases over the whole prompt (OjaKV's prefill
         # adaptation), version 0 -> 1 of a two-version copy of the bases
         Lo = B.Layer.allocate(dtype=B.LRKV_BF16, batch=w.batch, n_q_heads=w.n_q_heads,
@@ -138,7 +146,7 @@ def replicate(L, B):
     sc = lambda t: None if t is None else t.clone()
     return B.Layer(L.dtype, L.batch, L.n_q_heads, L.n_kv_heads, L.window, L.cap, L.rank_k, L.rank_v,
                    L.bases.clone(), L.codes_k.clone(), L.codes_v.clone(), L.anchor_k.clone(),
-                   L.anchor_v.clone(), sc(L.scales_k), sc(L.scales_v))
+                   L.anchor_v.clone(), sc(L.scales_k), sc(L.scales_v), head_group=L.head_group)
 
 
 def cpu_baseline(w, seconds):
@@ -191,11 +199,11 @@ def cpu_baseline(w, seconds):
                       f"(code preparation untimed)"}
 
 
-def traffic_from_profile(source_hash, codes="bf16"):
+def traffic_from_profile(source_hash, codes="bf16", hg=1):
     """HBM traffic per launch of the dominant kernel, from the committed counter
     summary, if it was taken on the current kernel source."""
-    name = "decode_partials_llama31_8b_32k_traffic.json" if codes == "bf16" else \
-        f"decode_partials_llama31_8b_32k_{codes}_traffic.json"
+    name = "decode_partials_llama31_8b_32k" + ("" if codes == "bf16" else f"_{codes}") + \
+        ("" if hg == 1 else f"_hg{hg}") + "_traffic.json"
     p = os.path.join(ROOT, "profiles", name)
     try:
         d = json.load(open(p))
@@ -214,6 +222,8 @@ def main():
     ap.add_argument("--workload", default="llama31_8b_32k")
     ap.add_argument("--codes", choices=("bf16", "int8", "int4"), default="bf16",
                     help="code storage (bf16 workloads): bf16, or int8 / int4 with per-token scales")
+    ap.add_argument("--head-group", type=int, default=1,
+                    help="KV heads sharing one code stream (group-head latents; bf16 workloads)")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated (0: >= 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -255,12 +265,14 @@ def main():
     t0 = time.time()
     bits = {"bf16": 16, "int8": 8, "int4": 4}[args.codes]
     assert not (bits < 16 and w.dtype != "bf16"), "quantised codes are for the bf16 workloads"
-    L0, compress, oja = build_cache(w, B, dev, bits)
+    hg = args.head_group
+    assert hg == 1 or (w.dtype == "bf16" and w.n_kv_heads % hg == 0), "head groups need bf16 storage"
+    L0, compress, oja = build_cache(w, B, dev, bits, hg)
     log(f"cache built and compressed on the GPU in {time.time() - t0:.1f} s "
         f"(compress {compress['ms']:.3f} ms, {compress['gbps']} GB/s)")
     if oja:
         log(f"Oja step over the prompt's keys: {oja['ms']:.3f} ms ({oja['gbps']} GB/s of rows)")
-    nb = algorithmic_bytes(w, w.n_ctx, bits)
+    nb = algorithmic_bytes(w, w.n_ctx, bits, hg)
     R = args.replicas or max(1, math.ceil((1 << 30) / nb["call"]))
     layers = [L0] + [replicate(L0, B) for _ in range(R - 1)]
     n = w.n_ctx
@@ -307,10 +319,12 @@ def main():
     kernel = DOMINANT_KERNEL if w.dtype == "bf16" else "k_partials_generic (stage 1)"
     if bits < 16:
         kernel = f"k_partials_mfma, {args.codes} codes (stage 1: code splits + anchors)"
+    if hg > 1:
+        kernel += f", {hg} KV heads per code stream"
     k_bytes = nb["partials"]
     achieved = k_bytes / (k_ms * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    traffic = traffic_from_profile(src_hash, args.codes)
+    traffic = traffic_from_profile(src_hash, args.codes, hg)
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
@@ -333,7 +347,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": 128, "n_ctx": n, "rank_k": w.rank_k,
                    "rank_v": w.rank_v, "window": w.window, "n_splits": S, "cache_replicas": R,
-                   "codes": args.codes},
+                   "codes": args.codes, "head_group": hg},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": k_bytes,

@@ -62,6 +62,7 @@ typedef enum lrkv_dtype {
 #define LRKV_MAX_GROUP 16     /* query heads per KV head */
 #define LRKV_MAX_SPLITS 1024
 #define LRKV_MAX_VERSIONS 16  /* basis versions per layer */
+#define LRKV_MAX_HEAD_GROUP 8 /* KV heads sharing one code stream */
 
 /*
  * One layer of compressed cache.  Storage type `dtype` applies to the bases, the
@@ -102,8 +103,22 @@ typedef enum lrkv_dtype {
  * s = max_c |x_c| / 127, all in float32 (a zero row: s = 0, q = 0); the code it
  * stands for is s q.  codes_k / codes_v keep the blocked positions above with
  * one-byte elements; the scales are float32:
- *   scales_k, scales_v (device): slot j of batch row b, KV head h at element
- *   (h * batch + b) * cap + j.
+ *   scales_k, scales_v (device): slot j of batch row b, KV head h (latent group
+ *   h with head groups) at element (h * batch + b) * cap + j.
+ *
+ * Group-head latents (head_group = n_g > 1; Palu abstract: a medium-grained
+ * decomposition between one latent per head and one for all heads).  The n_g
+ * consecutive KV heads of a group (g = h / n_g) share one code per token: the
+ * projection of their concatenated rows [x_{g n_g}, ..., x_{g n_g + n_g - 1}]
+ * (n_g * 128 features, head by head) onto one basis U(g) of n_g * 128 rows; KV
+ * head h reads its 128-row slice (rows 128 (h % n_g) ..) of U(g).  Everything
+ * "per head" above is then per group: rank_k / rank_v have n_kv_heads / n_g
+ * entries, bases hold per group U_K(g)^T as [rank_k[g]][n_g * 128] then
+ * U_V(g)^T, codes and scales regions are per group.  Anchors stay per KV head.
+ * n_kv_heads must be a multiple of n_g, n_g * (n_q_heads / n_kv_heads) <=
+ * LRKV_MAX_GROUP, n_g <= LRKV_MAX_HEAD_GROUP, and the storage is bf16 (or
+ * quantised codes); lrkv_oja_update needs n_g = 1.  Errors: LRKV_ERR_SHAPE for
+ * a group size that breaks these limits, LRKV_ERR_DTYPE for float32 storage.
  *
  * 4-bit codes (dtype LRKV_BF16_Q4): the same rule with 7 in place of 127
  * (s = max_c |x_c| / 7, q in [-7, 7]), the same scales.  Element position p of
@@ -136,13 +151,16 @@ typedef struct lrkv_layer {
                              version 0 starts at 0, starts are multiples of 32 and
                              non-decreasing.  Code slot j of row b was made with the
                              last version whose start is <= j. */
+  int32_t head_group;     /* KV heads sharing one code stream (Palu's group-head
+                             latents, see below); 0 or 1: one per KV head */
 } lrkv_layer;
 
 /*
  * Prefill compression (blog section 04: one projection per (layer, head), keys
  * after RoPE).  For every (batch row b, KV head h) and t in [0, n_tok): code slot
  * slot0 + t of `which` (0 = keys with U_K, 1 = values with U_V) receives
- * x[b, h, t, :] U, rounded to the storage type (bf16: round to nearest even of
+ * x[b, h, t, :] U, rounded to the storage type (with head groups: group g's slot
+ * receives the concatenated rows of its KV heads times U(g)) (bf16: round to nearest even of
  * the float32 accumulation; LRKV_BF16_Q8 / _Q4: the float32 accumulation
  * quantised to int8 / 4 bits with its scale, as described above).  With basis
  * versions the latest version (n_versions - 1) is used.
@@ -158,8 +176,8 @@ lrkv_status lrkv_compress(const lrkv_layer *L, int32_t which, const void *x,
 
 /*
  * The quantising step of lrkv_compress on given float32 code rows (LRKV_BF16_Q8
- * and LRKV_BF16_Q4 layers only): slot slot0 + t of head h, row b receives the
- * quantisation of
+ * and LRKV_BF16_Q4 layers only): slot slot0 + t of head h (of latent group h
+ * with head groups), row b receives the quantisation of
  * x[b, h, t, 0 .. r-1] (r = the head's rank for `which`) and its scale.
  *   x: device float32, element (b, h, t, c) at x + b*stride_b + h*stride_h + t*stride_t + c.
  * Errors: LRKV_ERR_DTYPE for other layer types; otherwise as lrkv_compress
@@ -219,7 +237,8 @@ lrkv_status lrkv_store_anchors(const lrkv_layer *L, const void *k, const void *v
  *  - window == 0 and pos >= 1: the new token is compressed into code slot pos - 1.
  *  - otherwise the new token is stored into its anchor slot.
  * With basis versions the code is made with the version the code slot belongs
- * to (version_start of the row).
+ * to (version_start of the row).  With head groups the group's code is made from
+ * the leaving rows of all its KV heads, and each KV head's anchor slot is updated.
  * Errors: LRKV_ERR_SHAPE if pos < 0; LRKV_ERR_CAPACITY if the code slot >= cap.
  */
 lrkv_status lrkv_append(const lrkv_layer *L, const void *k_new, const void *v_new,

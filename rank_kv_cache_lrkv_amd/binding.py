@@ -49,6 +49,7 @@ class lrkv_layer(ctypes.Structure):
         ("anchor_k", c_void_p), ("anchor_v", c_void_p),
         ("scales_k", c_void_p), ("scales_v", c_void_p),
         ("n_versions", c_int32), ("version_start", c_void_p),
+        ("head_group", c_int32),
     ]
 
 
@@ -140,27 +141,33 @@ class Layer:
     codes_v: "object"
     anchor_k: "object"
     anchor_v: "object"
-    scales_k: "object" = None  # quantised codes only: float32 [n_kv_heads][batch][cap]
+    scales_k: "object" = None  # quantised codes only: float32 [n_latent][batch][cap]
     scales_v: "object" = None
     n_versions: int = 1
     version_start: "object" = None  # int32 [batch][n_versions] (device) when n_versions > 1
+    head_group: int = 1  # KV heads sharing one code stream; rank_k / rank_v per group
     _rk: object = field(default=None, repr=False)
     _rv: object = field(default=None, repr=False)
     struct: lrkv_layer = field(default=None, repr=False)
 
     def __post_init__(self):
-        self._rk = (c_int32 * self.n_kv_heads)(*[int(x) for x in self.rank_k])
-        self._rv = (c_int32 * self.n_kv_heads)(*[int(x) for x in self.rank_v])
+        self._rk = (c_int32 * max(1, len(self.rank_k)))(*[int(x) for x in self.rank_k])
+        self._rv = (c_int32 * max(1, len(self.rank_v)))(*[int(x) for x in self.rank_v])
         self.struct = lrkv_layer(
             self.dtype, self.batch, self.n_q_heads, self.n_kv_heads, self.window, self.cap,
             ctypes.cast(self._rk, POINTER(c_int32)), ctypes.cast(self._rv, POINTER(c_int32)),
             _ptr(self.bases), _ptr(self.codes_k), _ptr(self.codes_v),
             _ptr(self.anchor_k), _ptr(self.anchor_v), _ptr(self.scales_k), _ptr(self.scales_v),
-            int(self.n_versions), _ptr(self.version_start))
+            int(self.n_versions), _ptr(self.version_start), int(self.head_group))
 
     @property
     def group(self) -> int:
         return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def n_latent(self) -> int:
+        """Code streams per batch row: KV heads, or head groups."""
+        return self.n_kv_heads // max(1, self.head_group)
 
     @property
     def torch_dtype(self):
@@ -179,9 +186,11 @@ class Layer:
     @classmethod
     def allocate(cls, *, dtype: int, batch: int, n_q_heads: int, n_kv_heads: int, window: int,
                  cap: int, rank_k: Sequence[int], rank_v: Sequence[int], device="cuda",
-                 bases=None, n_versions: int = 1) -> "Layer":
+                 bases=None, n_versions: int = 1, head_group: int = 1) -> "Layer":
         """Allocate zeroed codes and anchors (and int8 scales) (torch) for the given
-        geometry.  ``bases`` (optional) is the flat bases tensor; otherwise zeros."""
+        geometry.  ``bases`` (optional) is the flat bases tensor; otherwise zeros.
+        With ``head_group`` > 1, rank_k / rank_v hold one rank per group of
+        ``head_group`` KV heads."""
         import torch
         td = torch.float32 if dtype == LRKV_F32 else torch.bfloat16
         cd = {LRKV_BF16_Q8: torch.int8, LRKV_BF16_Q4: torch.uint8}.get(dtype, td)
@@ -189,7 +198,9 @@ class Layer:
         rk = np.asarray(rank_k, np.int32)
         rv = np.asarray(rank_v, np.int32)
         cap = layout.round_cap(cap)
-        nb = layout.bases_elems(rk, rv) * n_versions   # one copy of the layout per version
+        hg = max(1, int(head_group))
+        n_lat = n_kv_heads // hg
+        nb = layout.bases_elems(rk, rv, hg) * n_versions   # one copy of the layout per version
         if bases is None:
             bases = torch.zeros(nb, dtype=td, device=device)
         assert bases.numel() == nb and bases.dtype == td
@@ -199,12 +210,12 @@ class Layer:
         av = torch.zeros_like(ak)
         sk = sv = None
         if dtype in QUANTISED:
-            sk = torch.zeros(max(1, layout.scales_elems(n_kv_heads, batch, cap)), dtype=torch.float32,
+            sk = torch.zeros(max(1, layout.scales_elems(n_lat, batch, cap)), dtype=torch.float32,
                              device=device)
             sv = torch.zeros_like(sk)
         vs = torch.zeros((batch, n_versions), dtype=torch.int32, device=device) if n_versions > 1 else None
         return cls(dtype, batch, n_q_heads, n_kv_heads, window, cap, rk, rv, bases, ck, cv, ak, av, sk, sv,
-                   n_versions, vs)
+                   n_versions, vs, hg)
 
 
 # ---------------------------------------------------------------------------
@@ -221,7 +232,7 @@ def lrkv_compress(layer: Layer, which: int, x, n_tok: int, slot0: int, stream=No
 
 
 def lrkv_quantize(layer: Layer, which: int, x, n_tok: int, slot0: int, stream=None):
-    """x: float32 device tensor viewed as [batch][n_kv_heads][>= n_tok][>= r]
+    """x: float32 device tensor viewed as [batch][n_latent][>= n_tok][>= r]
     (any strides, last dimension contiguous): code rows to quantise into int8
     slots slot0 .. slot0 + n_tok - 1."""
     sb, sh, st, si = x.stride()

@@ -39,6 +39,10 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   if (nver > 1 && L->dtype == LRKV_F32) return LRKV_ERR_DTYPE;
   if (nver > 1 && !L->version_start) return LRKV_ERR_NULL;
   if (nver > 1 && (reinterpret_cast<uintptr_t>(L->version_start) & 3u)) return LRKV_ERR_ALIGN;
+  const int32_t hg = L->head_group <= 1 ? 1 : L->head_group;
+  if (hg > LRKV_MAX_HEAD_GROUP || L->n_kv_heads % hg) return LRKV_ERR_SHAPE;
+  if (hg > 1 && int64_t(hg) * (L->n_q_heads / L->n_kv_heads) > LRKV_MAX_GROUP) return LRKV_ERR_SHAPE;
+  if (hg > 1 && L->dtype == LRKV_F32) return LRKV_ERR_DTYPE;
   if (quantised(L->dtype)) {
     if (!L->scales_k || !L->scales_v) return LRKV_ERR_NULL;
     if (!aligned16(L->scales_k) || !aligned16(L->scales_v)) return LRKV_ERR_ALIGN;
@@ -49,6 +53,8 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   A->n_q = L->n_q_heads;
   A->n_kv = L->n_kv_heads;
   A->group = L->n_q_heads / L->n_kv_heads;
+  A->hg = hg;
+  A->n_lat = L->n_kv_heads / hg;
   A->window = L->window;
   A->cap = L->cap;
   A->bases = L->bases;
@@ -60,17 +66,17 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   A->scales_v = quantised(L->dtype) ? L->scales_v : nullptr;
   int64_t ub = 0, ck = 0, cv = 0;
   int rv_max = 0;
-  for (int h = 0; h < L->n_kv_heads; ++h) {
+  for (int h = 0; h < A->n_lat; ++h) {
     const int32_t rk = L->rank_k[h], rv = L->rank_v[h];
     if (!valid_rank(rk) || !valid_rank(rv)) return LRKV_ERR_RANK;
     HeadInfo &hd = A->heads[h];
     hd.rk = rk;
     hd.rv = rv;
     hd.u_k = int32_t(ub);
-    hd.u_v = int32_t(ub + int64_t(kD) * rk);
+    hd.u_v = int32_t(ub + int64_t(hg) * kD * rk);
     hd.ck = ck;
     hd.cv = cv;
-    ub += int64_t(kD) * (rk + rv);
+    ub += int64_t(hg) * kD * (rk + rv);
     ck += int64_t(L->batch) * L->cap * rk;
     cv += int64_t(L->batch) * L->cap * rv;
     rv_max = rv > rv_max ? rv : rv_max;
@@ -88,7 +94,7 @@ int32_t rec_floats(const LayerArgs &A) { return 4 + rvp_floats(A) + kD; }
 int32_t auto_splits(const LayerArgs &A, int32_t n_ctx) {
   const int64_t c = n_ctx - 1 - A.window;
   const int64_t nblk = c > 0 ? (c + LRKV_BLOCK - 1) / LRKV_BLOCK : 0;
-  const int64_t units = int64_t(A.batch) * A.n_kv;
+  const int64_t units = int64_t(A.batch) * A.n_lat;
   // about four workgroups of codes per compute unit (256 CUs), at least four
   // 32-slot blocks per split
   int64_t s = (1024 + units - 1) / units;
@@ -196,6 +202,7 @@ lrkv_status lrkv_oja_update(const lrkv_layer *L, int32_t which, const void *x, i
   lrkv_status st = make_layer(L, &A);
   if (st != LRKV_OK) return st;
   if (L->dtype == LRKV_F32) return LRKV_ERR_DTYPE;
+  if (A.hg != 1) return LRKV_ERR_SHAPE;  // the step is per KV head
   if (which != 0 && which != 1) return LRKV_ERR_SHAPE;
   if (n_tok < 1 || !(eta == eta) || eta > 3.4e38f || eta < -3.4e38f) return LRKV_ERR_SHAPE;
   if (version_in < 0 || version_in >= A.n_versions || version_out < 0 || version_out >= A.n_versions)

@@ -12,8 +12,8 @@
 namespace lrkv {
 
 // ---------------------------------------------------------------------------
-// Generic projection (float32 storage; bf16 and int8 codes run on the matrix
-// cores, see compress_mfma.hip).
+// Generic projection (float32 storage, which has no head groups; bf16 and
+// quantised codes run on the matrix cores, see compress_mfma.hip).
 // One workgroup per (64-token tile, batch row, KV head).  The 64x128 input tile
 // is staged in LDS as float32; each thread produces code columns with a float32
 // dot product over the 128 features against a basis row (read through the cache).
@@ -66,9 +66,12 @@ __global__ __launch_bounds__(128) void k_store_anchors(LayerArgs L, const T *k, 
 }
 
 // ---------------------------------------------------------------------------
-// Decode-step maintenance: one workgroup (128 threads) per (row, head).  The row
-// to compress is staged in LDS before the anchor slot is overwritten, so the
-// read of the leaving token and the write of the new one cannot overlap.
+// Decode-step maintenance: one workgroup (128 threads) per (row, latent group),
+// that is per (row, KV head) without head groups.  The rows to compress (one per
+// KV head of the group) are staged in LDS before the anchor slots are
+// overwritten, so the read of a leaving token and the write of the new one
+// cannot overlap.  Thread t makes code column t from the concatenated rows: the
+// sum over the group's KV heads j of row_j . (slice j of basis row t).
 // ---------------------------------------------------------------------------
 // largest |x| over the 128 threads of the workgroup (every thread calls it)
 __device__ __forceinline__ float block_absmax(float x, float *red) {
@@ -83,28 +86,34 @@ __device__ __forceinline__ float block_absmax(float x, float *red) {
 // QMAX: 0 for bf16 / f32 codes, 127 for int8 codes, 7 for 4-bit codes
 template <typename T, int QMAX>
 __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, const T *vnew, int pos) {
-  __shared__ float rk_row[kD], rv_row[kD];
+  __shared__ float rk_row[LRKV_MAX_HEAD_GROUP][kD], rv_row[LRKV_MAX_HEAD_GROUP][kD];
   __shared__ float red[2];
   const int unit = blockIdx.x;
-  const int b = unit / L.n_kv, h = unit % L.n_kv;
+  const int b = unit / L.n_lat, h = unit % L.n_lat;
+  const int hg = L.hg;
   const int W = L.window;
   const int tid = threadIdx.x;
   const HeadInfo hd = L.heads[h];
-  T *ak = static_cast<T *>(L.anchor_k) + int64_t(unit) * (1 + W) * kD;
-  T *av = static_cast<T *>(L.anchor_v) + int64_t(unit) * (1 + W) * kD;
-  const T *kn = knew + int64_t(unit) * kD;
-  const T *vn = vnew + int64_t(unit) * kD;
+  const int64_t kv0 = int64_t(b) * L.n_kv + int64_t(h) * hg;  // the group's first (row, KV head)
+  auto ak = [&](int j) { return static_cast<T *>(L.anchor_k) + (kv0 + j) * (1 + W) * kD; };
+  auto av = [&](int j) { return static_cast<T *>(L.anchor_v) + (kv0 + j) * (1 + W) * kD; };
+  auto kn = [&](int j) { return knew + (kv0 + j) * kD; };
+  auto vn = [&](int j) { return vnew + (kv0 + j) * kD; };
 
   int slot = -1, code_slot = -1;
   if (W >= 1 && pos > W) {
     slot = 1 + (pos - 1) % W;  // holds token pos - W, which now leaves the window
     code_slot = pos - W - 1;
-    rk_row[tid] = to_f32(ak[slot * kD + tid]);
-    rv_row[tid] = to_f32(av[slot * kD + tid]);
+    for (int j = 0; j < hg; ++j) {
+      rk_row[j][tid] = to_f32(ak(j)[slot * kD + tid]);
+      rv_row[j][tid] = to_f32(av(j)[slot * kD + tid]);
+    }
   } else if (W == 0 && pos >= 1) {
     code_slot = pos - 1;
-    rk_row[tid] = to_f32(kn[tid]);
-    rv_row[tid] = to_f32(vn[tid]);
+    for (int j = 0; j < hg; ++j) {
+      rk_row[j][tid] = to_f32(kn(j)[tid]);
+      rv_row[j][tid] = to_f32(vn(j)[tid]);
+    }
   } else {
     slot = anchor_slot(pos, W);
   }
@@ -116,11 +125,14 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
       if (L.vstart[int64_t(b) * L.n_versions + v] <= code_slot) ver = v;
     const T *Uk = static_cast<const T *>(L.bases) + ver * L.version_elems + hd.u_k;
     const T *Uv = static_cast<const T *>(L.bases) + ver * L.version_elems + hd.u_v;
+    const int urow = hg * kD;  // elements of a basis row (U^T row)
     float acck = 0.f, accv = 0.f;
     if (tid < hd.rk)
-      for (int k = 0; k < kD; ++k) acck = fmaf(rk_row[k], to_f32(Uk[tid * kD + k]), acck);
+      for (int j = 0; j < hg; ++j)
+        for (int k = 0; k < kD; ++k) acck = fmaf(rk_row[j][k], to_f32(Uk[tid * urow + j * kD + k]), acck);
     if (tid < hd.rv)
-      for (int k = 0; k < kD; ++k) accv = fmaf(rv_row[k], to_f32(Uv[tid * kD + k]), accv);
+      for (int j = 0; j < hg; ++j)
+        for (int k = 0; k < kD; ++k) accv = fmaf(rv_row[j][k], to_f32(Uv[tid * urow + j * kD + k]), accv);
     if constexpr (QMAX > 0) {
       const float sk = qn_scale<QMAX>(block_absmax(tid < hd.rk ? acck : 0.f, red));
       const float sv = qn_scale<QMAX>(block_absmax(tid < hd.rv ? accv : 0.f, red));
@@ -148,21 +160,23 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
     }
   }
   if (slot >= 0) {
-    ak[slot * kD + tid] = kn[tid];
-    av[slot * kD + tid] = vn[tid];
+    for (int j = 0; j < hg; ++j) {
+      ak(j)[slot * kD + tid] = kn(j)[tid];
+      av(j)[slot * kD + tid] = vn(j)[tid];
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Quantisation of given float32 code rows (QMAX 127: int8, 7: 4 bits): one wave
-// per (token, row, head), lane l holding columns l and l + 64.
+// per (token, row, head or latent group), lane l holding columns l and l + 64.
 // ---------------------------------------------------------------------------
 template <int QMAX>
 __global__ __launch_bounds__(256) void k_quantize(LayerArgs L, int which, const float *x, int64_t sb,
                                                   int64_t sh, int64_t st, int n_tok, int slot0) {
   const int t = blockIdx.x * 4 + int(threadIdx.x >> 6);
   const int unit = blockIdx.y;
-  const int b = unit / L.n_kv, h = unit % L.n_kv;
+  const int b = unit / L.n_lat, h = unit % L.n_lat;
   if (t >= n_tok) return;  // no barrier follows
   const HeadInfo hd = L.heads[h];
   const int r = which ? hd.rv : hd.rk;
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(256) void k_quantize(LayerArgs L, int which, const 
 // ---------------------------------------------------------------------------
 hipError_t launch_quantize(const LayerArgs &L, int which, const float *x, int64_t sb, int64_t sh,
                            int64_t st, int n_tok, int slot0, hipStream_t s) {
-  dim3 grid((n_tok + 3) / 4, L.batch * L.n_kv);
+  dim3 grid((n_tok + 3) / 4, L.batch * L.n_lat);
   if (L.dtype == LRKV_BF16_Q8)
     hipLaunchKernelGGL(k_quantize<127>, grid, dim3(256), 0, s, L, which, x, sb, sh, st, n_tok, slot0);
   else
@@ -221,7 +235,7 @@ hipError_t launch_store_anchors(const LayerArgs &L, const void *k, const void *v
 }
 
 hipError_t launch_append(const LayerArgs &L, const void *k, const void *v, int pos, hipStream_t s) {
-  dim3 grid(L.batch * L.n_kv);
+  dim3 grid(L.batch * L.n_lat);
   const bf16_t *kb = static_cast<const bf16_t *>(k), *vb = static_cast<const bf16_t *>(v);
   if (L.dtype == LRKV_F32)
     hipLaunchKernelGGL((k_append<float, 0>), grid, dim3(kD), 0, s, L, static_cast<const float *>(k),

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void k_compress_mfma(LayerArgs L, int which, c
                                                        int n_tok, int slot0) {
   __shared__ bf16_t su[kD * kUStride];
   const int unit = blockIdx.y;
-  const int b = unit / L.n_kv, h = unit % L.n_kv;
+  const int b = unit / L.n_lat, h = unit % L.n_lat;
   const HeadInfo hd = L.heads[h];
   const int r = which ? hd.rv : hd.rk;
   // the latest basis version (prefill compresses before later versions appear)
@@ -226,11 +226,156 @@ __global__ __launch_bounds__(256) void k_compress_mfma(LayerArgs L, int which, c
   }
 }
 
+// ---------------------------------------------------------------------------
+// Head groups (Palu's group-head latents): one workgroup per (128-token tile,
+// batch row, latent group).  A token's code is the product of its concatenated
+// rows (the group's KV heads one after another) with U(g), so the kernel walks
+// the KV heads j of the group: it loads that head's rows, stages slice j of the
+// U^T rows (columns 128 j .. 128 j + 127) in LDS and adds the products into
+// accumulators that hold every column tile of the wave's 32 tokens.  The codes
+// are stored (or quantised from the accumulators: the row maxima need no second
+// sweep) once all heads are in.
+// ---------------------------------------------------------------------------
+template <int QMAX>
+__global__ __launch_bounds__(256) void k_compress_group(LayerArgs L, int which, const bf16_t *x,
+                                                        int64_t sb, int64_t sh, int64_t st,
+                                                        int n_tok, int slot0) {
+  __shared__ bf16_t su[kD * kUStride];
+  const int unit = blockIdx.y;
+  const int b = unit / L.n_lat, h = unit % L.n_lat;
+  const HeadInfo hd = L.heads[h];
+  const int r = which ? hd.rv : hd.rk;
+  const int ntr = r / 16;
+  const int urow = L.hg * kD;
+  const bf16_t *ut = static_cast<const bf16_t *>(L.bases) + (L.n_versions - 1) * L.version_elems +
+                     (which ? hd.u_v : hd.u_k);
+  const int64_t region = (which ? hd.cv : hd.ck) + int64_t(b) * L.cap * r;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q4 = lane >> 4, t16 = lane & 15;
+  const int t_base = blockIdx.x * 128 + wave * 32;
+
+  f32x4 acc[kD / 16][2];
+#pragma unroll
+  for (int nt = 0; nt < kD / 16; ++nt) acc[nt][0] = acc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < L.hg; ++j) {
+    const bf16_t *xb = x + b * sb + (int64_t(h) * L.hg + j) * sh;
+    u32x4 xo[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tok = min(t_base + 16 * tt + t16, n_tok - 1);
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        xo[tt][kc] = *reinterpret_cast<const u32x4 *>(xb + int64_t(tok) * st + 32 * kc + 8 * q4);
+    }
+    u32x4 uu[kD * 16 / 256];
+#pragma unroll
+    for (int k = 0; k < kD * 16 / 256; ++k) {
+      const int p = min(tid + 256 * k, r * 16 - 1);
+      uu[k] = *reinterpret_cast<const u32x4 *>(ut + (p >> 4) * urow + j * kD + (p & 15) * 8);
+    }
+    if (j > 0) __syncthreads();  // every wave is done with slice j - 1
+#pragma unroll
+    for (int k = 0; k < kD * 16 / 256; ++k) {
+      const int p = tid + 256 * k;
+      if (p < r * 16) *reinterpret_cast<u32x4 *>(&su[(p >> 4) * kUStride + (p & 15) * 8]) = uu[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < kD / 16; ++nt) {
+      if (nt < ntr) {
+        u32x4 uo[4];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+          uo[kc] = *reinterpret_cast<const u32x4 *>(&su[(16 * nt + t16) * kUStride + 32 * kc + 8 * q4]);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          if (which == 0) {
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) acc[nt][tt] = mfma16x16x32(uo[kc], xo[tt][kc], acc[nt][tt]);
+          } else {
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) acc[nt][tt] = mfma16x16x32(xo[tt][kc], uo[kc], acc[nt][tt]);
+          }
+        }
+      }
+    }
+  }
+  if (t_base >= n_tok) return;  // no barrier follows
+
+  // keys: lane (q4, t16) holds columns 16 nt + 4 q4 + v of token t16; values:
+  // tokens 4 q4 + v of column 16 nt + t16 (as in k_compress_mfma)
+  float sc[2][4];
+  if constexpr (QMAX > 0) {
+    float *scales = (which ? L.scales_v : L.scales_k) + scale_index(L, h, b, 0);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float am[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int nt = 0; nt < kD / 16; ++nt)
+        if (nt < ntr)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) am[v] = fmaxf(am[v], fabsf(acc[nt][tt][v]));
+      if (which == 0) {
+        float a = fmaxf(fmaxf(am[0], am[1]), fmaxf(am[2], am[3]));
+        a = fmaxf(a, __shfl_xor(a, 16, 64));
+        a = fmaxf(a, __shfl_xor(a, 32, 64));
+        sc[tt][0] = sc[tt][1] = sc[tt][2] = sc[tt][3] = qn_scale<QMAX>(a);
+        const int tok = t_base + 16 * tt + t16;
+        if (q4 == 0 && tok < n_tok) scales[slot0 + tok] = sc[tt][0];
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float a = am[v];
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+          sc[tt][v] = qn_scale<QMAX>(a);
+          const int tok = t_base + 16 * tt + 4 * q4 + v;
+          if (t16 == 0 && tok < n_tok) scales[slot0 + tok] = sc[tt][v];
+        }
+      }
+    }
+  }
+  // one element of code position p: bf16, int8 or a nibble
+  auto store1 = [&](int64_t p, float val, float s) {
+    if constexpr (QMAX == 0) static_cast<bf16_t *>(which ? L.codes_v : L.codes_k)[region + p] = from_f32<bf16_t>(val);
+    else if constexpr (QMAX == 127)
+      static_cast<int8_t *>(which ? L.codes_v : L.codes_k)[region + p] = int8_t(qn_value<QMAX>(val, s));
+    else store_q4(static_cast<uint8_t *>(which ? L.codes_v : L.codes_k) + region / 2, p, qn_value<QMAX>(val, s));
+  };
+#pragma unroll
+  for (int nt = 0; nt < kD / 16; ++nt) {
+    if (nt < ntr) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        if (which == 0) {
+          const int tok = t_base + 16 * tt + t16;
+          if (tok < n_tok)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) store1(kslot(slot0 + tok, 16 * nt + 4 * q4 + v, r), acc[nt][tt][v], sc[tt][0]);
+        } else {
+          const int tok0 = t_base + 16 * tt + 4 * q4;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (tok0 + v < n_tok) store1(vslot(slot0 + tok0 + v, 16 * nt + t16, r), acc[nt][tt][v], sc[tt][v]);
+        }
+      }
+    }
+  }
+}
+
 hipError_t launch_compress_mfma(const LayerArgs &L, int which, const void *x, int64_t sb,
                                 int64_t sh, int64_t st, int n_tok, int slot0, hipStream_t s) {
-  dim3 grid((n_tok + 127) / 128, L.batch * L.n_kv);
+  dim3 grid((n_tok + 127) / 128, L.batch * L.n_lat);
   const bf16_t *xb = static_cast<const bf16_t *>(x);
-  if (L.dtype == LRKV_BF16_Q8)
+  if (L.hg > 1) {
+    if (L.dtype == LRKV_BF16_Q8)
+      hipLaunchKernelGGL(k_compress_group<127>, grid, dim3(256), 0, s, L, which, xb, sb, sh, st, n_tok, slot0);
+    else if (L.dtype == LRKV_BF16_Q4)
+      hipLaunchKernelGGL(k_compress_group<7>, grid, dim3(256), 0, s, L, which, xb, sb, sh, st, n_tok, slot0);
+    else
+      hipLaunchKernelGGL(k_compress_group<0>, grid, dim3(256), 0, s, L, which, xb, sb, sh, st, n_tok, slot0);
+  } else if (L.dtype == LRKV_BF16_Q8)
     hipLaunchKernelGGL(k_compress_mfma<127>, grid, dim3(256), 0, s, L, which, xb, sb, sh, st, n_tok, slot0);
   else if (L.dtype == LRKV_BF16_Q4)
     hipLaunchKernelGGL(k_compress_mfma<7>, grid, dim3(256), 0, s, L, which, xb, sb, sh, st, n_tok, slot0);

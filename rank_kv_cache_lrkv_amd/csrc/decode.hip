@@ -119,7 +119,8 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, floa
   constexpr int PRE = 16;   // terms per thread loaded up front (the rest, if any, later)
   __shared__ CombineSmem cs;
   const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  const int h = i / L.group;
+  const int kvh = i / L.group;                 // KV head; its latent group and slice
+  const int h = kvh / L.hg, j = kvh % L.hg;
   const HeadInfo hd = L.heads[h];
   const int rv = hd.rv;
   const int S = d.n_splits;
@@ -130,13 +131,15 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, floa
   auto rec = [&](int s, int f) {  // float f of split s's record
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, (s * d.rec + f) * 4, 0, 0));
   };
-  const int a = min(row_ctx(d, b), 1 + L.window);
+  const int a = min(row_ctx(d, b), 1 + L.window) * L.hg;  // the unit's anchor rows
   const int per = anchor_rows_per_split(a, S);
   const int sa = min(S, (a + per - 1) / per);  // splits 0 .. sa-1 carry anchor sums
-  // U_V^T rows: element (c, t) is column c of output feature t
+  // U_V^T rows (hg * 128 elements, this KV head's slice at j * 128): element
+  // (c, t) of the slice is column c of output feature t
+  const int urow = L.hg * kD;
   const __amdgpu_buffer_rsrc_t ur = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T *>(static_cast<const T *>(L.bases) + hd.u_v), 0, rv * kD * int(sizeof(T)), kBufferWord3);
-  auto uv = [&](int c) { return buffer_elem<T>(ur, (c * kD + t) * int(sizeof(T))); };
+      const_cast<T *>(static_cast<const T *>(L.bases) + hd.u_v), 0, rv * urow * int(sizeof(T)), kBufferWord3);
+  auto uv = [&](int c) { return buffer_elem<T>(ur, (c * urow + j * kD + t) * int(sizeof(T))); };
   const int groups = 128 / rv;
   const int col = t % rv, grp = t / rv;
   const int grp_c = min(grp, groups - 1);
@@ -196,12 +199,14 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, floa
       if (cs.m[g] != kNegInf) o = fmaf(fast_exp2(cs.m[g] - M), cs.o[g * rv + t], o);
     cs.ot[t] = o;
   }
-  // anchor sums of output feature t (anchor splits hold at least one row: finite maxima)
+  // anchor sums of output feature t (a split without rows of this head has m = -inf: weight 0)
 #pragma unroll
   for (int k = 0; k < PRE; ++k)
-    if (k < sa) oa = fmaf(fast_exp2(ma[k] - M), av[k], oa);
-  for (int s = PRE; s < sa; ++s)
-    oa = fmaf(fast_exp2(rec(s, 0) - M), rec(s, d.oa + t), oa);
+    if (k < sa && ma[k] != kNegInf) oa = fmaf(fast_exp2(ma[k] - M), av[k], oa);
+  for (int s = PRE; s < sa; ++s) {
+    const float ms = rec(s, 0);
+    if (ms != kNegInf) oa = fmaf(fast_exp2(ms - M), rec(s, d.oa + t), oa);
+  }
   __syncthreads();
 
   float y = 0.f;
@@ -222,7 +227,8 @@ template <typename T>
 __global__ __launch_bounds__(128) void k_combine_versions(LayerArgs L, DecodeArgs d, float *out) {
   __shared__ float sot[128];
   const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  const int h = i / L.group;
+  const int kvh = i / L.group;
+  const int h = kvh / L.hg, j = kvh % L.hg;
   const HeadInfo hd = L.heads[h];
   const int rv = hd.rv;
   const int S = d.n_splits;
@@ -230,12 +236,12 @@ __global__ __launch_bounds__(128) void k_combine_versions(LayerArgs L, DecodeArg
   const int n = row_ctx(d, b);
   const int c = max(0, n - 1 - L.window);
   const int nblk = (c + kBlock - 1) / kBlock;
-  const int a = min(n, 1 + L.window);
+  const int a = min(n, 1 + L.window) * L.hg;
   const int per = anchor_rows_per_split(a, S);
   const int sa = min(S, (a + per - 1) / per);  // splits 0 .. sa-1 carry anchor sums
 
   float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, split_record(d, qi, s)[0]);  // finite: anchors exist
+  for (int s = 0; s < S; ++s) M = fmaxf(M, split_record(d, qi, s)[0]);  // finite: token 0 is an anchor
   float Ltot = 0.f;
   for (int s = 0; s < S; ++s) {
     const float *r = split_record(d, qi, s);
@@ -255,13 +261,13 @@ __global__ __launch_bounds__(128) void k_combine_versions(LayerArgs L, DecodeArg
     }
     __syncthreads();
     const T *uvt = static_cast<const T *>(L.bases) + v * L.version_elems + hd.u_v;  // U_V^T rows
-    for (int cc = 0; cc < rv; ++cc) y = fmaf(to_f32(uvt[cc * kD + t]), sot[cc], y);
+    for (int cc = 0; cc < rv; ++cc) y = fmaf(to_f32(uvt[cc * L.hg * kD + j * kD + t]), sot[cc], y);
     __syncthreads();
   }
   float oa = 0.f;
   for (int s = 0; s < sa; ++s) {
     const float *r = split_record(d, qi, s);
-    oa = fmaf(fast_exp2(r[0] - M), r[d.oa + t], oa);
+    if (r[0] != kNegInf) oa = fmaf(fast_exp2(r[0] - M), r[d.oa + t], oa);
   }
   out[qi * kD + t] = (y + oa) / Ltot;
 }

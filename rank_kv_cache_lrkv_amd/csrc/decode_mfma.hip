@@ -168,8 +168,10 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
     unit = (i & 7) * (gridDim.y >> 3) + k / S;
     split = k % S;
   }
-  const int b = unit / L.n_kv, h = unit % L.n_kv;
-  const int G = L.group;
+  // unit = (batch row b, latent group h); its G query heads are those of the hg
+  // KV heads h hg .. h hg + hg - 1 (GK each), which share the group's codes
+  const int b = unit / L.n_lat, h = unit % L.n_lat;
+  const int GK = L.group, G = GK * L.hg;
   const int W = L.window;
   const HeadInfo hd = L.heads[h];
   const int rk = EXACT ? RKMAX : hd.rk, rv = EXACT ? RVMAX : hd.rv;
@@ -181,9 +183,14 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   const int n = row_ctx(d, b);
   const int c = max(0, n - 1 - W);
   const int nblk = (c + kBlock - 1) / kBlock;
+  // the unit's anchor rows: a1 per KV head, KV head after KV head
+  const int a1 = min(n, 1 + W);
   int alo, ahi;
-  anchor_share(min(n, 1 + W), split, S, alo, ahi);
+  anchor_share(a1 * L.hg, split, S, alo, ahi);
   const int na = ahi - alo;
+  auto anchor_row = [&](int rho) {  // element row of anchor row rho of the unit
+    return (int64_t(b) * L.n_kv + h * L.hg + rho / a1) * (1 + W) + rho % a1;
+  };
   const int64_t q0 = int64_t(b) * L.n_q + h * G;
   // with basis versions the split sweeps its version's blocks [sg.lo, sg.hi)
   const SplitSeg sg = split_segment(L, b, split, S, nblk);
@@ -285,17 +292,21 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   constexpr int NTW = (NT + 3) / 4;  // column tiles of q~ per wave
   // every load below is unconditional, from a clamped in-bounds address; what is
   // absent is zeroed afterwards (no divergent branches around the loads)
-  u32x4 bu[NTW][4];                  // B = rows of U_K^T
+  const int urow = L.hg * kD;        // elements per U^T row (one 128-slice per KV head of the group)
+  u32x4 bu[NTW][4];                  // B = rows of U_K^T, the slice of the group's first KV head
+  auto load_bu = [&](int j) {
 #pragma unroll
-  for (int i = 0; i < NTW; ++i) {
-    const int nt = min(wave + 4 * i, rk / 16 - 1);
+    for (int i = 0; i < NTW; ++i) {
+      const int nt = min(wave + 4 * i, rk / 16 - 1);
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-      bu[i][kc] = *reinterpret_cast<const u32x4 *>(ut + (16 * nt + t16) * kD + 32 * kc + 8 * q4);
-  }
+      for (int kc = 0; kc < 4; ++kc)
+        bu[i][kc] = *reinterpret_cast<const u32x4 *>(ut + (16 * nt + t16) * urow + j * kD + 32 * kc + 8 * q4);
+    }
+  };
+  load_bu(0);
   const int r16 = tid >> 4, piece = tid & 15;  // 16 rows x 16 pieces of 16 bytes
   u32x4 qq = *reinterpret_cast<const u32x4 *>(qb + min(r16, G - 1) * kD + piece * 8);
-  const int64_t arow = int64_t(unit) * (1 + W) + (na > 0 ? alo + min(r16, na - 1) : 0);
+  const int64_t arow = na > 0 ? anchor_row(alo + min(r16, na - 1)) : anchor_row(0);
   u32x4 kk = *reinterpret_cast<const u32x4 *>(static_cast<const bf16_t *>(L.anchor_k) + arow * kD + piece * 8);
   u32x4 vv = *reinterpret_cast<const u32x4 *>(static_cast<const bf16_t *>(L.anchor_v) + arow * kD + piece * 8);
   __builtin_amdgcn_sched_barrier(0);
@@ -319,18 +330,30 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   u32x4 aq[4];
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) aq[kc] = *reinterpret_cast<const u32x4 *>(&sm.sq[t16][16 * kc + 4 * q4]);
-  // D[head][col] = sum_k q[head][k] U_K[k][col]; the waves share the column tiles
+  // D[head][col] = sum_k q[head][k] U_K[k][col], with U_K the slice of the head's
+  // own KV head: one pass per KV head of the group, the other heads' q zeroed;
+  // the waves share the column tiles
+  f32x4 qacc[NTW];
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) qacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < L.hg; ++j) {
+    if (j > 0) load_bu(j);
+    u32x4 aj[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) aj[kc] = t16 / GK == j ? aq[kc] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < NTW; ++i)
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) qacc[i] = mfma16x16x32(aj[kc], bu[i][kc], qacc[i]);
+  }
 #pragma unroll
   for (int i = 0; i < NTW; ++i) {
     const int nt = wave + 4 * i;
     if (nt < rk / 16) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) acc = mfma16x16x32(aq[kc], bu[i][kc], acc);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int head = 4 * q4 + v;
-        if (head < G) sm.u.qt[head][16 * nt + t16] = acc[v] * (d.scale_log2 * kX16);
+        if (head < G) sm.u.qt[head][16 * nt + t16] = qacc[i][v] * (d.scale_log2 * kX16);
       }
     }
   }
@@ -370,7 +393,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int idx = lane + 64 * i, r = idx >> 4, piece = idx & 15;
-          const int64_t row = int64_t(unit) * (1 + W) + alo + r0 + min(r, nr - 1);
+          const int64_t row = anchor_row(alo + r0 + min(r, nr - 1));
           const u32x4 kk = *reinterpret_cast<const u32x4 *>(static_cast<const bf16_t *>(L.anchor_k) + row * kD + piece * 8);
           const u32x4 vv = *reinterpret_cast<const u32x4 *>(static_cast<const bf16_t *>(L.anchor_v) + row * kD + piece * 8);
           *reinterpret_cast<u32x4 *>(&sm.ak[r][piece * 4]) = kk;
@@ -383,16 +406,22 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
       for (int kc = 0; kc < 4; ++kc)
         s = mfma16x16x32(*reinterpret_cast<const u32x4 *>(&sm.ak[t16][16 * kc + 4 * q4]),
                          *reinterpret_cast<const u32x4 *>(&sm.sq[t16][16 * kc + 4 * q4]), s);
+      // row 4 q4 + v (of KV head (alo + r0 + row) / a1) scores only that KV head's query heads
 #pragma unroll
-      for (int v = 0; v < 4; ++v) s[v] = 4 * q4 + v < nr ? s[v] * d.scale_log2 : kNegInf;
+      for (int v = 0; v < 4; ++v) {
+        const int row = 4 * q4 + v;
+        s[v] = row < nr && (alo + r0 + row) / a1 == t16 / GK ? s[v] * d.scale_log2 : kNegInf;
+      }
       float cm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
       cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
       cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-      const float mn = fmaxf(mA, cm);  // finite: nr >= 1
-      const float al = fast_exp2(mA - mn);
+      // a head may have no row in this chunk (rows of another KV head, or an absent head)
+      const float mn = fmaxf(mA, cm);
+      const bool none = mn == kNegInf;
+      const float al = none ? 1.f : fast_exp2(mA - mn);
       float p[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) p[v] = fast_exp2(s[v] - mn);
+      for (int v = 0; v < 4; ++v) p[v] = none ? 0.f : fast_exp2(s[v] - mn);
       float ps = (p[0] + p[1]) + (p[2] + p[3]);
       ps += __shfl_xor(ps, 16, 64);
       ps += __shfl_xor(ps, 32, 64);
@@ -632,8 +661,8 @@ static void launch_cb(const LayerArgs &L, const DecodeArgs &d, dim3 grid, hipStr
 template <int RKMAX, int RVMAX>
 static hipError_t launch_rv(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
   bool exact = true;
-  for (int h = 0; h < L.n_kv; ++h) exact = exact && L.heads[h].rk == RKMAX && L.heads[h].rv == RVMAX;
-  dim3 grid(d.n_splits, L.batch * L.n_kv);
+  for (int h = 0; h < L.n_lat; ++h) exact = exact && L.heads[h].rk == RKMAX && L.heads[h].rv == RVMAX;
+  dim3 grid(d.n_splits, L.batch * L.n_lat);
   if (exact) launch_cb<RKMAX, RVMAX, true>(L, d, grid, s);
   else launch_cb<RKMAX, RVMAX, false>(L, d, grid, s);
   return hipGetLastError();
@@ -663,9 +692,9 @@ static int cu_count() {
 hipError_t launch_partials_mfma(const LayerArgs &L, const DecodeArgs &d0, hipStream_t s) {
   DecodeArgs d = d0;
   // balancing pays when the whole grid is resident at once (four workgroups per CU)
-  d.balance = int64_t(d.n_splits) * L.batch * L.n_kv <= 4 * int64_t(cu_count());
+  d.balance = int64_t(d.n_splits) * L.batch * L.n_lat <= 4 * int64_t(cu_count());
   int rk_max = 0;
-  for (int h = 0; h < L.n_kv; ++h) rk_max = L.heads[h].rk > rk_max ? L.heads[h].rk : rk_max;
+  for (int h = 0; h < L.n_lat; ++h) rk_max = L.heads[h].rk > rk_max ? L.heads[h].rk : rk_max;
   if (rk_max <= 32) return launch_rk<32>(L, d, s);
   if (rk_max <= 64) return launch_rk<64>(L, d, s);
   if (rk_max <= 96) return launch_rk<96>(L, d, s);

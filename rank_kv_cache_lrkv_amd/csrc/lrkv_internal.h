@@ -15,12 +15,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Per-KV-head geometry, element offsets precomputed on the host.
 struct HeadInfo {
   int32_t rk, rv;
-  int32_t u_k, u_v;  // offsets of U_K(h), U_V(h) in the bases buffer
+  int32_t u_k, u_v;  // offsets of U_K(h), U_V(h) in the bases buffer (rows of hg * 128)
   int64_t ck, cv;    // offsets of head h's [batch][cap][r] code region
 };
 
+// With group-head latents (hg > 1) the hg consecutive KV heads of latent group g
+// share one code stream; HeadInfo and the code / scale regions are per latent
+// group (n_lat of them), anchors per KV head.  hg = 1: a group is one KV head.
 struct LayerArgs {
   int32_t dtype, batch, n_q, n_kv, group, window, cap, rv_max;
+  int32_t hg, n_lat;           // KV heads per latent group, latent groups
   const void *bases;
   void *codes_k, *codes_v, *anchor_k, *anchor_v;
   float *scales_k, *scales_v;  // quantised codes: one scale per (head, row, slot)
@@ -87,7 +91,7 @@ __device__ __forceinline__ int anchor_slot(int p, int window) {
   return p == 0 ? 0 : 1 + (p - 1) % window;
 }
 
-// quantised codes: element of the scale of slot j of (KV head h, batch row b)
+// quantised codes: element of the scale of slot j of (latent group h, batch row b)
 __device__ __forceinline__ int64_t scale_index(const LayerArgs &L, int h, int b, int j) {
   return (int64_t(h) * L.batch + b) * L.cap + j;
 }

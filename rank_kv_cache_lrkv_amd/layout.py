@@ -20,23 +20,28 @@ def round_cap(n: int) -> int:
     return (n + BLOCK - 1) // BLOCK * BLOCK
 
 
-def bases_elems(rank_k: Sequence[int], rank_v: Sequence[int]) -> int:
-    return HEAD_DIM * int(np.sum(rank_k) + np.sum(rank_v))
+def bases_elems(rank_k: Sequence[int], rank_v: Sequence[int], head_group: int = 1) -> int:
+    """Elements of one version of the bases: per head (or head group of
+    ``head_group`` KV heads) U_K^T and U_V^T with rows of 128 * head_group."""
+    return HEAD_DIM * int(head_group) * int(np.sum(rank_k) + np.sum(rank_v))
 
 
-def bases_offsets(rank_k: Sequence[int], rank_v: Sequence[int]):
-    """Element offsets of U_K(h) and U_V(h) in the bases buffer."""
+def bases_offsets(rank_k: Sequence[int], rank_v: Sequence[int], head_group: int = 1):
+    """Element offsets of U_K(h) and U_V(h) (h a head, or a head group) in the
+    bases buffer."""
+    row = HEAD_DIM * int(head_group)
     uk, uv, off = [], [], 0
     for rk, rv in zip(rank_k, rank_v):
         uk.append(off)
-        uv.append(off + HEAD_DIM * int(rk))
-        off += HEAD_DIM * (int(rk) + int(rv))
+        uv.append(off + row * int(rk))
+        off += row * (int(rk) + int(rv))
     return np.array(uk), np.array(uv)
 
 
 def pack_bases(u_k: Sequence[np.ndarray], u_v: Sequence[np.ndarray]) -> np.ndarray:
-    """Flat bases buffer from per-head (128, r) matrices: head by head, U_K^T then
-    U_V^T, each basis direction as 128 contiguous elements."""
+    """Flat bases buffer from per-head (128, r) matrices (per head group:
+    (128 * head_group, r)): head by head, U_K^T then U_V^T, each basis direction
+    as its rows' contiguous elements."""
     parts = []
     for uk, uv in zip(u_k, u_v):
         parts += [np.asarray(uk).T.ravel(), np.asarray(uv).T.ravel()]
@@ -54,12 +59,14 @@ def code_offsets(ranks: Sequence[int], batch: int, cap: int) -> np.ndarray:
 
 
 def scales_elems(n_kv_heads: int, batch: int, cap: int) -> int:
-    """Elements of one int8-code scales buffer: float32 [n_kv_heads][batch][cap]."""
+    """Elements of one quantised-code scales buffer: float32 [heads][batch][cap]
+    (heads = KV heads, or latent groups with head groups)."""
     return int(n_kv_heads) * int(batch) * int(cap)
 
 
 def scale_offset(h: int, b: int, cap: int, batch: int) -> int:
-    """Element offset of slot 0 of (KV head h, batch row b) in a scales buffer."""
+    """Element offset of slot 0 of (KV head or latent group h, batch row b) in a
+    scales buffer."""
     return (int(h) * int(batch) + int(b)) * int(cap)
 
 

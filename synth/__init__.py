@@ -13,6 +13,7 @@ from .workloads import (  # noqa: F401
     Workload,
     basis,
     calibration_rows,
+    group_basis,
     haar_orthogonal,
     queries,
     ranks,

@@ -177,6 +177,17 @@ def basis(w: Workload, layer: int, head: int, which: str, rank: int) -> np.ndarr
     return round_to_storage(vt[:rank].T, w.dtype)
 
 
+def group_basis(w: Workload, layer: int, group: int, head_group: int, which: str, rank: int) -> np.ndarray:
+    """Basis of a group of ``head_group`` consecutive KV heads (group-head
+    latents): the top-``rank`` right singular vectors of the group's calibration
+    rows joined feature-wise (head by head), a (128 * head_group, rank) matrix
+    with orthonormal columns, rounded to storage."""
+    heads = range(group * head_group, (group + 1) * head_group)
+    x = np.concatenate([calibration_rows(w, layer, h, which) for h in heads], axis=1)
+    _, _, vt = np.linalg.svd(x, full_matrices=False)
+    return round_to_storage(vt[:rank].T, w.dtype)
+
+
 def unit_kv(w: Workload, layer: int, head: int, b: int, which: str) -> np.ndarray:
     """All ``n_total`` rows of keys (``which='k'``) or values for one
     (layer, KV head, batch row), rounded to storage: shape (n_total, 128)."""

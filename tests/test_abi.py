@@ -220,3 +220,26 @@ def test_oja_validation():
     assert f(x=FAKE + 2) == 5
     assert f(wsb=need - 1) == 7
     assert f(ws=None) == 7
+
+
+def test_head_group_validation():
+    def grouped(hg, **kw):
+        L = layer(**kw)
+        L.head_group = hg
+        return L
+    one = dict(rank_k=[64], rank_v=[32])    # one latent group of both KV heads
+    assert decode(grouped(2, **one), q=None) == 1      # a valid layer: fails on q only
+    assert decode(grouped(0), q=None) == 1             # 0 and 1: one code stream per KV head
+    assert decode(grouped(1), q=None) == 1
+    assert decode(grouped(3, **one)) == 2              # 2 KV heads are not groups of 3
+    assert decode(grouped(16, n_kv_heads=16, n_q_heads=16, rank_k=[64], rank_v=[32])) == 2  # > 8
+    assert decode(grouped(2, n_q_heads=2 * 16, **one)) == 2   # 2 x 16 query heads per group > 16
+    assert decode(grouped(2, dtype=0, **one)) == 4     # float32 storage has no groups
+    assert decode(grouped(2, rank_k=[64], rank_v=[24])) == 3
+    lib = B.lib()
+    L = grouped(2, **one)
+    # the auto split count depends on the code streams (one here), not the KV heads
+    assert lib.lrkv_decode_auto_splits(ctypes.byref(L), 32768) >= \
+        lib.lrkv_decode_auto_splits(ctypes.byref(layer()), 32768)
+    assert lib.lrkv_oja_update(ctypes.byref(L), 0, FAKE, 1024, 512, 128, 10, 0.5, 0, 0, FAKE, 1 << 30,
+                               None) == 2      # the Oja step is per KV head
