@@ -276,7 +276,9 @@ def main():
     R = args.replicas or max(1, math.ceil((1 << 30) / nb["call"]))
     layers = [L0] + [replicate(L0, B) for _ in range(R - 1)]
     n = w.n_ctx
-    S = w.n_splits or B.lrkv_decode_auto_splits(L0, n)
+    # splits per code stream: the workload's count per KV head, times the group size
+    # with head groups (so the grid keeps its size), else the library's choice
+    S = w.n_splits * hg if w.n_splits else B.lrkv_decode_auto_splits(L0, n)
     q = dev(np.stack([synth.queries(w, 0, 0, b) for b in range(w.batch)]))
     out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device="cuda")
     ws = B.workspace(L0, S)

@@ -305,7 +305,7 @@ __global__ __launch_bounds__(256) void k_compress_group(LayerArgs L, int which, 
 
   // keys: lane (q4, t16) holds columns 16 nt + 4 q4 + v of token t16; values:
   // tokens 4 q4 + v of column 16 nt + t16 (as in k_compress_mfma)
-  float sc[2][4];
+  float sc[2][4] = {};
   if constexpr (QMAX > 0) {
     float *scales = (which ? L.scales_v : L.scales_k) + scale_index(L, h, b, 0);
 #pragma unroll
@@ -336,28 +336,45 @@ __global__ __launch_bounds__(256) void k_compress_group(LayerArgs L, int which, 
       }
     }
   }
-  // one element of code position p: bf16, int8 or a nibble
+  // 4 consecutive elements from position p (a multiple of 4), or one element at
+  // p: bf16, int8 or 4-bit, quantised with the scales sc
+  char *base = static_cast<char *>(which ? L.codes_v : L.codes_k);
+  auto store4 = [&](int64_t p, f32x4 v, float s0, float s1, float s2, float s3) {
+    if constexpr (QMAX == 0) {
+      uint2 v2;
+      v2.x = pack_rne(v[0], v[1]);
+      v2.y = pack_rne(v[2], v[3]);
+      *reinterpret_cast<uint2 *>(reinterpret_cast<bf16_t *>(base) + region + p) = v2;
+    } else if constexpr (QMAX == 127) {
+      *reinterpret_cast<uint32_t *>(base + region + p) = pack_qn<QMAX>(v, s0, s1, s2, s3);
+    } else {
+      *reinterpret_cast<uint16_t *>(base + (region + p) / 2) = uint16_t(pack_qn<QMAX>(v, s0, s1, s2, s3));
+    }
+  };
   auto store1 = [&](int64_t p, float val, float s) {
-    if constexpr (QMAX == 0) static_cast<bf16_t *>(which ? L.codes_v : L.codes_k)[region + p] = from_f32<bf16_t>(val);
-    else if constexpr (QMAX == 127)
-      static_cast<int8_t *>(which ? L.codes_v : L.codes_k)[region + p] = int8_t(qn_value<QMAX>(val, s));
-    else store_q4(static_cast<uint8_t *>(which ? L.codes_v : L.codes_k) + region / 2, p, qn_value<QMAX>(val, s));
+    if constexpr (QMAX == 0) reinterpret_cast<bf16_t *>(base)[region + p] = from_f32<bf16_t>(val);
+    else if constexpr (QMAX == 127) reinterpret_cast<int8_t *>(base)[region + p] = int8_t(qn_value<QMAX>(val, s));
+    else store_q4(reinterpret_cast<uint8_t *>(base) + region / 2, p, qn_value<QMAX>(val, s));
   };
 #pragma unroll
   for (int nt = 0; nt < kD / 16; ++nt) {
     if (nt < ntr) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        if (which == 0) {
+        const f32x4 a = acc[nt][tt];
+        if (which == 0) {  // 4 consecutive columns of one token: contiguous
           const int tok = t_base + 16 * tt + t16;
-          if (tok < n_tok)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) store1(kslot(slot0 + tok, 16 * nt + 4 * q4 + v, r), acc[nt][tt][v], sc[tt][0]);
-        } else {
+          if (tok < n_tok) store4(kslot(slot0 + tok, 16 * nt + 4 * q4, r), a, sc[tt][0], sc[tt][0], sc[tt][0], sc[tt][0]);
+        } else {  // 4 tokens of one column: contiguous when 4-aligned and present
           const int tok0 = t_base + 16 * tt + 4 * q4;
+          const int j0 = slot0 + tok0, col = 16 * nt + t16;
+          if (tok0 + 3 < n_tok && (j0 & 3) == 0) {
+            store4(vslot(j0, col, r), a, sc[tt][0], sc[tt][1], sc[tt][2], sc[tt][3]);
+          } else {
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (tok0 + v < n_tok) store1(vslot(slot0 + tok0 + v, 16 * nt + t16, r), acc[nt][tt][v], sc[tt][v]);
+            for (int v = 0; v < 4; ++v)
+              if (tok0 + v < n_tok) store1(vslot(j0 + v, col, r), a[v], sc[tt][v]);
+          }
         }
       }
     }

@@ -131,9 +131,11 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, floa
   auto rec = [&](int s, int f) {  // float f of split s's record
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, (s * d.rec + f) * 4, 0, 0));
   };
-  const int a = min(row_ctx(d, b), 1 + L.window) * L.hg;  // the unit's anchor rows
-  const int per = anchor_rows_per_split(a, S);
-  const int sa = min(S, (a + per - 1) / per);  // splits 0 .. sa-1 carry anchor sums
+  const int a1 = min(row_ctx(d, b), 1 + L.window);  // anchor rows per KV head
+  const int per = anchor_rows_per_split(a1 * L.hg, S);
+  // splits s_a0 .. s_a1 - 1 hold this KV head's anchor rows j a1 .. (j + 1) a1 - 1
+  // (the unit's rows, KV head after KV head, cut into runs of per rows)
+  const int s_a0 = (j * a1) / per, s_a1 = min(S, ((j + 1) * a1 + per - 1) / per);
   // U_V^T rows (hg * 128 elements, this KV head's slice at j * 128): element
   // (c, t) of the slice is column c of output feature t
   const int urow = L.hg * kD;
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, floa
     const int s = min(grp_c + k * groups, S - 1);
     ml[k] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rr, s * d.rec * 4, 0, 0));
     ov[k] = rec(s, 4 + col);
-    const int sk = min(k, sa - 1);
+    const int sk = min(s_a0 + k, s_a1 - 1);
     ma[k] = rec(sk, 0);
     av[k] = rec(sk, d.oa + t);
   }
@@ -202,8 +204,8 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, floa
   // anchor sums of output feature t (a split without rows of this head has m = -inf: weight 0)
 #pragma unroll
   for (int k = 0; k < PRE; ++k)
-    if (k < sa && ma[k] != kNegInf) oa = fmaf(fast_exp2(ma[k] - M), av[k], oa);
-  for (int s = PRE; s < sa; ++s) {
+    if (s_a0 + k < s_a1 && ma[k] != kNegInf) oa = fmaf(fast_exp2(ma[k] - M), av[k], oa);
+  for (int s = s_a0 + PRE; s < s_a1; ++s) {
     const float ms = rec(s, 0);
     if (ms != kNegInf) oa = fmaf(fast_exp2(ms - M), rec(s, d.oa + t), oa);
   }
@@ -236,9 +238,9 @@ __global__ __launch_bounds__(128) void k_combine_versions(LayerArgs L, DecodeArg
   const int n = row_ctx(d, b);
   const int c = max(0, n - 1 - L.window);
   const int nblk = (c + kBlock - 1) / kBlock;
-  const int a = min(n, 1 + L.window) * L.hg;
-  const int per = anchor_rows_per_split(a, S);
-  const int sa = min(S, (a + per - 1) / per);  // splits 0 .. sa-1 carry anchor sums
+  const int a1 = min(n, 1 + L.window);  // anchor rows per KV head
+  const int per = anchor_rows_per_split(a1 * L.hg, S);
+  const int s_a0 = (j * a1) / per, s_a1 = min(S, ((j + 1) * a1 + per - 1) / per);  // as in k_combine
 
   float M = kNegInf;
   for (int s = 0; s < S; ++s) M = fmaxf(M, split_record(d, qi, s)[0]);  // finite: token 0 is an anchor
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(128) void k_combine_versions(LayerArgs L, DecodeArg
     __syncthreads();
   }
   float oa = 0.f;
-  for (int s = 0; s < sa; ++s) {
+  for (int s = s_a0; s < s_a1; ++s) {
     const float *r = split_record(d, qi, s);
     if (r[0] != kNegInf) oa = fmaf(fast_exp2(r[0] - M), r[d.oa + t], oa);
   }

@@ -630,10 +630,14 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
     for (int w = 0; w < 4; ++w) acc = fmaf(weight(w, hh, M), sm.o[w][hh][cc], acc);
     split_record(d, q0 + hh, split)[4 + cc] = acc * kX16;
   }
-  if (na > 0) {  // anchor-free splits leave o_A unwritten; the combine skips it
+  // o_A of the heads whose KV head has anchor rows in this split; the combine
+  // reads it from exactly these splits and skips the others
+  if (na > 0) {
     for (int i = tid; i < G * kD; i += blockDim.x) {
       const int hh = i / kD, cc = i - hh * kD;
-      split_record(d, q0 + hh, split)[d.oa + cc] = weight(4, hh, head_max(hh)) * sm.u.oa[hh][cc];
+      const int jj = hh / GK;
+      if (jj * a1 < ahi && (jj + 1) * a1 > alo)
+        split_record(d, q0 + hh, split)[d.oa + cc] = weight(4, hh, head_max(hh)) * sm.u.oa[hh][cc];
     }
   }
   for (int hh = tid; hh < G; hh += blockDim.x) {
