@@ -37,6 +37,10 @@ re-orthonormalisation (the page names Oja's algorithm but gives no rule); codes
 made under several basis versions are decoded each with its own version; see
 oja_update and oracle_decode_unit_versions.
 
+LowRAM's value amortisation (values predicted from the key codes by a linear
+map fitted on the prompt, residuals kept for each block's worst-predicted tokens)
+follows readings stated with lowram_fit; see oracle_decode_lowram.
+
 Int8 and int4 codes (the first step past the pages: they name quantisation of
 the low-rank cache but no quantiser) follow a stated design, symmetric with one
 float32 scale per code row, decided in float32; see quantize_codes_q8 and
@@ -351,6 +355,81 @@ def dequantize_codes_q4(q, s) -> np.ndarray:
 # blog section 08: the per-request cache shrinks with the code width, plus the
 # shared projection matrices)
 # ---------------------------------------------------------------------------
+
+# ---------------------------------------------------------------------------
+# LowRAM value amortisation (LowRAM abstract: inside one attention head the
+# values are largely predictable from their keys; a light per-head predictor is
+# fitted at test time and residuals are stored only for the tokens it
+# reconstructs worst).  The page fixes neither the predictor nor the selection
+# rule; the readings (also in the design doc):
+#   * the predictor is linear in the stored key codes, V ~ C_K M with M of shape
+#     (r_k, 128), one per (batch row, KV head), fitted on the prompt's compressed
+#     tokens by least squares with a tiny relative ridge for rank-deficient code
+#     matrices: M = (C_K^T C_K + lam I)^-1 C_K^T V, lam = 1e-6 tr(C_K^T C_K) / r_k;
+#   * the residual of a token is e_t = V_t - C_K,t M with M as stored (bf16);
+#     every 32-slot block keeps the residuals of its R tokens with the largest
+#     squared norm (ties: the lower slot), stored in bf16;
+#   * the decode reads value C_K,t M + e_t for a kept token, C_K,t M otherwise.
+# ---------------------------------------------------------------------------
+
+LOWRAM_BLOCK = 32
+LOWRAM_RIDGE = 1e-6
+
+
+def lowram_fit(c_k, v) -> np.ndarray:
+    """Predictor M (r_k, 128) of values from key codes: ridge-stabilised least
+    squares over the rows of c_k (t, r_k) and v (t, 128)."""
+    c = np.asarray(c_k, np.float64)
+    x = np.asarray(v, np.float64)
+    a = c.T @ c
+    lam = LOWRAM_RIDGE * np.trace(a) / a.shape[0] + 1e-30
+    return np.linalg.solve(a + lam * np.eye(a.shape[0]), c.T @ x)
+
+
+def lowram_residuals(c_k, v, m) -> np.ndarray:
+    """e_t = v_t - c_t M for every row."""
+    return np.asarray(v, np.float64) - np.asarray(c_k, np.float64) @ np.asarray(m, np.float64)
+
+
+def lowram_select(sq_norms, r: int) -> np.ndarray:
+    """Slots whose residual is kept: in every block of 32 consecutive slots, the r
+    with the largest squared norm (ties: the lower slot).  Sorted slot indices."""
+    sq = np.asarray(sq_norms, np.float64)
+    kept = []
+    for b0 in range(0, len(sq), LOWRAM_BLOCK):
+        block = list(range(b0, min(b0 + LOWRAM_BLOCK, len(sq))))
+        block.sort(key=lambda j: (-sq[j], j))
+        kept += block[:r]
+    return np.array(sorted(kept), dtype=np.int64)
+
+
+def lowram_prefill(c_k, v, r: int) -> tuple:
+    """What a prompt leaves in the cache: (M as stored (bf16), kept slots, the
+    residual rows of every slot as stored (bf16)); only the kept rows are read."""
+    m = bf16_round(lowram_fit(c_k, v))
+    e = lowram_residuals(c_k, v, m)
+    kept = lowram_select(np.sum(e * e, axis=1), r)
+    return m, kept, bf16_round(e)
+
+
+def lowram_values(c_k, m, kept, e) -> np.ndarray:
+    """The values the decode reads for the compressed tokens: C_K M, plus the
+    residual rows of the kept slots."""
+    vals = np.asarray(c_k, np.float64) @ np.asarray(m, np.float64)
+    kept = np.asarray(kept, np.int64)
+    vals[kept] += np.asarray(e, np.float64)[kept]
+    return vals
+
+
+def oracle_decode_lowram(q, u_k, m, c_k, kept, e, k_a, v_a, scale: float) -> np.ndarray:
+    """Decode attention of the g query heads of one KV head over a LowRAM cache:
+    keys as in oracle_decode_unit (scored against the codes), values of the
+    compressed tokens from lowram_values, anchors at full rank.  q (g, 128),
+    u_k (128, r_k), m (r_k, 128), c_k (c, r_k), kept (slots), e (c, 128),
+    k_a, v_a (a, 128).  Returns out (g, 128)."""
+    vals = lowram_values(c_k, m, kept, e)
+    return oracle_decode_unit(q, u_k, np.eye(HEAD_DIM), c_k, vals, k_a, v_a, scale)
+
 
 def full_kv_bytes(n_layers: int, n_kv_heads: int, n_tokens: int, batch: int,
                   head_dim: int = HEAD_DIM, elem_bytes: int = 2) -> int:

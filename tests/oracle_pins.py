@@ -584,4 +584,81 @@ def pin_group_decode_brute_force():
     assert np.max(np.abs(one - ref)) < 1e-12
 
 
+def pin_lowram_fit_recovers_map_and_matches_lstsq():
+    """Values that are an exact linear map of the codes give that map back; on
+    general rows the fit equals NumPy's least-squares solver on the ridge-augmented
+    system [C; sqrt(lam) I] M = [V; 0] (lam = 1e-6 tr(C^T C) / r)."""
+    rng = np.random.default_rng(40)
+    t, r = 300, 16
+    c = rng.standard_normal((t, r)) * np.exp(-np.arange(r) / 8)
+    a = rng.standard_normal((r, D))
+    got = oracle.lowram_fit(c, c @ a)
+    assert np.max(np.abs(got - a)) < 1e-3 * np.max(np.abs(a)), np.max(np.abs(got - a))
+    v = rng.standard_normal((t, D)) + c @ a
+    lam = 1e-6 * np.sum(c * c) / r
+    aug_c = np.concatenate([c, math.sqrt(lam) * np.eye(r)])
+    aug_v = np.concatenate([v, np.zeros((r, D))])
+    want = np.linalg.lstsq(aug_c, aug_v, rcond=None)[0]
+    assert np.max(np.abs(oracle.lowram_fit(c, v) - want)) < 1e-9 * np.max(np.abs(want))
+    # an all-zero code matrix predicts nothing
+    assert not np.any(oracle.lowram_fit(np.zeros((5, r)), rng.standard_normal((5, D))))
+
+
+def pin_lowram_select_is_blockwise_top_r():
+    """Per block of 32 slots, exactly min(r, block size) slots are kept, and every
+    kept slot's norm beats every dropped slot's (equal norms: the lower slot is
+    kept); the same set comes out of inserting the slots one at a time in slot
+    order into a set of at most r, replacing the smallest only when strictly
+    beaten (the decode-time rule)."""
+    rng = np.random.default_rng(41)
+    for n, r in ((77, 5), (32, 1), (40, 32), (10, 3), (64, 8)):
+        sq = rng.integers(0, 6, n).astype(float)        # many ties
+        kept = set(oracle.lowram_select(sq, r).tolist())
+        for b0 in range(0, n, 32):
+            blk = list(range(b0, min(b0 + 32, n)))
+            k = [j for j in blk if j in kept]
+            d = [j for j in blk if j not in kept]
+            assert len(k) == min(r, len(blk))
+            for i in k:
+                for j in d:
+                    assert sq[i] > sq[j] or (sq[i] == sq[j] and i < j), (n, r, i, j)
+            online = []
+            for j in blk:
+                if len(online) < r:
+                    online.append(j)
+                else:
+                    low = min(online, key=lambda x: (sq[x], -x))
+                    if sq[j] > sq[low]:
+                        online[online.index(low)] = j
+            assert sorted(online) == k, (n, r)
+
+
+def pin_lowram_decode_brute_force():
+    """Brute force over the reconstructed cache: keys U_K c_t, values M^T c_t plus
+    the residual of kept slots, anchors at full rank.  With every residual kept and
+    unrounded the values are the original rows."""
+    rng = np.random.default_rng(42)
+    n, w, rk, g = 45, 4, 16, 3
+    cpos, apos = oracle.code_positions(n, w), oracle.anchor_positions(n, w)
+    k = rng.standard_normal((n, D))
+    v = rng.standard_normal((n, D)) * 0.5 + k @ rng.standard_normal((D, D)) * 0.05
+    uk = orthonormal(rng, rk)
+    ck = k[cpos] @ uk
+    q = rng.standard_normal((g, D)) * 3
+    sc = oracle.default_scale()
+    m, kept, e = oracle.lowram_prefill(ck, v[cpos], 5)
+    got = oracle.oracle_decode_lowram(q, uk, m, ck, kept, e, k[apos], v[apos], sc)
+    keys = np.concatenate([reconstruct(ck, uk), k[apos]])
+    vals = [np.asarray(m, float).T @ ck[t] + (e[t] if t in set(kept.tolist()) else 0) for t in range(len(cpos))]
+    vals = np.concatenate([np.stack(vals), v[apos]])
+    for i in range(g):
+        want, _ = brute_attention(q[i], keys, vals, sc)
+        assert np.max(np.abs(got[i] - want)) < 1e-12
+    exact_e = oracle.lowram_residuals(ck, v[cpos], m)
+    full = oracle.oracle_decode_lowram(q, uk, m, ck, np.arange(len(cpos)), exact_e, k[apos], v[apos], sc)
+    for i in range(g):
+        want, _ = brute_attention(q[i], keys, np.concatenate([v[cpos], v[apos]]), sc)
+        assert np.max(np.abs(full[i] - want)) < 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -58,8 +58,34 @@ MUTANTS = {
     "versions_one_value_basis": ("oracle_decode_unit_versions", lambda *a: _versions_variant(*a, val_v0=True)),
     "group_heads_reversed": ("oracle_compress_group",
                              lambda x, u: np.concatenate(list(np.asarray(x, float))[::-1], axis=1) @ np.asarray(u, float)),
+    "lowram_residual_sign": ("lowram_values", lambda c, m, kept, e: _lowram_values_variant(c, m, kept, e, sign=-1)),
+    "lowram_residual_dropped": ("lowram_values", lambda c, m, kept, e: _lowram_values_variant(c, m, [], e)),
+    "lowram_fit_diagonal": ("lowram_fit", lambda c, v: np.asarray(c, float).T @ np.asarray(v, float)
+                            / np.maximum(np.sum(np.asarray(c, float) ** 2, axis=0), 1e-30)[:, None]),
+    "lowram_fit_no_ridge_scale": ("lowram_fit", lambda c, v: np.linalg.solve(
+        np.asarray(c, float).T @ np.asarray(c, float) + 1e-2 * np.eye(np.asarray(c).shape[1]),
+        np.asarray(c, float).T @ np.asarray(v, float))),
+    "lowram_select_smallest": ("lowram_select", lambda sq, r: _lowram_select_variant(sq, r, sign=-1)),
+    "lowram_select_ties_high_slot": ("lowram_select", lambda sq, r: _lowram_select_variant(sq, r, tie=-1)),
+    "lowram_select_whole_row": ("lowram_select", lambda sq, r: _lowram_select_variant(sq, r, block=10 ** 9)),
     "group_slice_off_by_one_head": ("group_slice", lambda u, j: np.asarray(u, float)[128 * max(j - 1, 0):128 * max(j, 1)]),
 }
+
+
+def _lowram_values_variant(c, m, kept, e, sign=1):
+    vals = np.asarray(c, float) @ np.asarray(m, float)
+    kept = np.asarray(kept, np.int64)
+    vals[kept] += sign * np.asarray(e, float)[kept]
+    return vals
+
+
+def _lowram_select_variant(sq, r, sign=1, tie=1, block=32):
+    sq = np.asarray(sq, float)
+    kept = []
+    for b0 in range(0, len(sq), block):
+        blk = sorted(range(b0, min(b0 + block, len(sq))), key=lambda j: (-sign * sq[j], tie * j))
+        kept += blk[:r]
+    return np.array(sorted(kept), dtype=np.int64)
 
 
 def _oja_variant(u, x, eta, sign=-1, average=True, orth=True, reverse=False):
