@@ -48,12 +48,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, n, bits=16, hg=1):
+def algorithmic_bytes(w, n, bits=16, hg=1, resid=0):
     """Bytes the method must move for one decode call of one layer, and the part
     the partials kernel moves (codes, anchors, U_K, q).  Quantised codes: r bytes
     (int8) or r / 2 bytes (4-bit) per code row plus its 4-byte scale.  Group-head
     latents (hg KV heads per code stream): one code row per group and token, bases
-    of hg * 128 rows per group, anchors per KV head."""
+    of hg * 128 rows per group, anchors per KV head.  LowRAM values (resid = R >
+    0): key codes only, R residual rows (256 bytes and a 4-byte slot) per 32-slot
+    block, and the row's predictor (r_k x 128) in place of U_V."""
     import oracle
     s = 4 if w.dtype == "f32" else 2
     c = len(oracle.code_positions(n, w.window))
@@ -66,13 +68,17 @@ def algorithmic_bytes(w, n, bits=16, hg=1):
     anchors = w.batch * w.n_kv_heads * a * 2 * 128 * s
     u_k = w.n_kv_heads * 128 * w.rank_k * s
     u_v = w.n_kv_heads * 128 * w.rank_v * s
+    if resid:
+        nblk = (c + 31) // 32
+        codes = units * (c * w.rank_k * s + nblk * resid * (128 * s + 4))
+        u_v = units * w.rank_k * 128 * s
     q = w.batch * w.n_q_heads * 128 * s
     out = w.batch * w.n_q_heads * 128 * 4
     return {"call": codes + anchors + u_k + u_v + q + out, "partials": codes + anchors + u_k + q,
             "codes": codes, "anchors": anchors}
 
 
-def build_cache(w, B, dev, bits=16, hg=1):
+def build_cache(w, B, dev, bits=16, hg=1, resid=0):
     """Prefill on the GPU: compress tokens 1..n-W-1, store token 0 and the window."""
     import numpy as np
     import torch
@@ -94,7 +100,8 @@ def build_cache(w, B, dev, bits=16, hg=1):
     dtype = {8: B.LRKV_BF16_Q8, 4: B.LRKV_BF16_Q4}.get(bits, B.LRKV_BF16 if w.dtype == "bf16" else B.LRKV_F32)
     L = B.Layer.allocate(dtype=dtype, batch=w.batch,
                          n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, window=w.window,
-                         cap=layout.round_cap(c), rank_k=rk, rank_v=rv, bases=dev(bases), head_group=hg)
+                         cap=layout.round_cap(c), rank_k=rk, rank_v=rv, bases=dev(bases), head_group=hg,
+                         lowram_resid=resid)
     td = L.torch_dtype
     K = torch.empty((w.batch, w.n_kv_heads, n, 128), dtype=td, device="cuda")
     V = torch.empty_like(K)
@@ -102,12 +109,16 @@ def build_cache(w, B, dev, bits=16, hg=1):
         for h in range(w.n_kv_heads):
             K[b, h] = dev(synth.unit_kv(w, 0, h, b, "k")[:n])
             V[b, h] = dev(synth.unit_kv(w, 0, h, b, "v")[:n])
-    # prefill compression, timed once warm
+    # prefill compression (LowRAM: keys, then the predictor fit and residuals), timed once warm
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    fit_ws = torch.empty(max(1, B.lrkv_lowram_workspace_size(L)), dtype=torch.uint8, device="cuda") if resid else None
     for rep in range(2):
         ev[0].record()
         B.lrkv_compress(L, 0, K[:, :, 1:], c, 0)
-        B.lrkv_compress(L, 1, V[:, :, 1:], c, 0)
+        if resid:
+            B.lrkv_lowram_fit(L, V[:, :, 1:], c, ws=fit_ws)
+        else:
+            B.lrkv_compress(L, 1, V[:, :, 1:], c, 0)
         ev[1].record()
     B.lrkv_store_anchors(L, K[:, :, 0:1], V[:, :, 0:1], 0, 1)
     lo = max(1, n - w.window)
@@ -117,10 +128,12 @@ def build_cache(w, B, dev, bits=16, hg=1):
     s = 2 if w.dtype == "bf16" else 4
     row = (2 * 128 * s + (w.rank_k + w.rank_v) * bits // 8 + 8) if bits < 16 else (2 * 128 + w.rank_k + w.rank_v) * s
     moved = w.batch * w.n_kv_heads * c * 2 * 128 * s + w.batch * (w.n_kv_heads // hg) * c * (row - 2 * 128 * s)
+    if resid:  # keys and values in, key codes and the kept residual rows out (the fit reads both twice)
+        moved = w.batch * w.n_kv_heads * (c * (2 * 128 * s + w.rank_k * s) + ((c + 31) // 32) * resid * (128 * s + 8))
     compress = {"ms": round(ms, 4), "tokens": c, "alg_bytes": moved,
                 "gbps": round(moved / (ms * 1e-3) / 1e9, 1)}
     oja = None
-    if bits == 16 and w.dtype == "bf16" and hg == 1:
+    if bits == 16 and w.dtype == "bf16" and hg == 1 and not resid:
         # one Oja step of the key bases over the whole prompt (OjaKV's prefill
         # adaptation), version 0 -> 1 of a two-version copy of the bases
         Lo = B.Layer.allocate(dtype=B.LRKV_BF16, batch=w.batch, n_q_heads=w.n_q_heads,
@@ -145,8 +158,10 @@ def build_cache(w, B, dev, bits=16, hg=1):
 def replicate(L, B):
     sc = lambda t: None if t is None else t.clone()
     return B.Layer(L.dtype, L.batch, L.n_q_heads, L.n_kv_heads, L.window, L.cap, L.rank_k, L.rank_v,
-                   L.bases.clone(), L.codes_k.clone(), L.codes_v.clone(), L.anchor_k.clone(),
-                   L.anchor_v.clone(), sc(L.scales_k), sc(L.scales_v), head_group=L.head_group)
+                   L.bases.clone(), L.codes_k.clone(), sc(L.codes_v), L.anchor_k.clone(),
+                   L.anchor_v.clone(), sc(L.scales_k), sc(L.scales_v), head_group=L.head_group,
+                   value_mode=L.value_mode, resid_per_block=L.resid_per_block, predictor=sc(L.predictor),
+                   resid=sc(L.resid), resid_slot=sc(L.resid_slot), resid_norm=sc(L.resid_norm))
 
 
 def cpu_baseline(w, seconds):
@@ -224,6 +239,9 @@ def main():
                     help="code storage (bf16 workloads): bf16, or int8 / int4 with per-token scales")
     ap.add_argument("--head-group", type=int, default=1,
                     help="KV heads sharing one code stream (group-head latents; bf16 workloads)")
+    ap.add_argument("--lowram", type=int, default=0, metavar="R",
+                    help="LowRAM values: predicted from the key codes, R residual rows per 32-slot block "
+                         "(bf16 workloads; values partly predictable from keys)")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated (0: >= 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -267,12 +285,16 @@ def main():
     assert not (bits < 16 and w.dtype != "bf16"), "quantised codes are for the bf16 workloads"
     hg = args.head_group
     assert hg == 1 or (w.dtype == "bf16" and w.n_kv_heads % hg == 0), "head groups need bf16 storage"
-    L0, compress, oja = build_cache(w, B, dev, bits, hg)
+    resid = args.lowram
+    assert not resid or (bits == 16 and hg == 1 and w.dtype == "bf16"), "LowRAM values: bf16 codes, no head groups"
+    if resid:
+        w = w.scaled(v_from_k=0.8)
+    L0, compress, oja = build_cache(w, B, dev, bits, hg, resid)
     log(f"cache built and compressed on the GPU in {time.time() - t0:.1f} s "
         f"(compress {compress['ms']:.3f} ms, {compress['gbps']} GB/s)")
     if oja:
         log(f"Oja step over the prompt's keys: {oja['ms']:.3f} ms ({oja['gbps']} GB/s of rows)")
-    nb = algorithmic_bytes(w, w.n_ctx, bits, hg)
+    nb = algorithmic_bytes(w, w.n_ctx, bits, hg, resid)
     R = args.replicas or max(1, math.ceil((1 << 30) / nb["call"]))
     layers = [L0] + [replicate(L0, B) for _ in range(R - 1)]
     n = w.n_ctx
@@ -323,10 +345,12 @@ def main():
         kernel = f"k_partials_mfma, {args.codes} codes (stage 1: code splits + anchors)"
     if hg > 1:
         kernel += f", {hg} KV heads per code stream"
+    if resid:
+        kernel = f"k_partials_mfma, LowRAM values (key codes + {resid} residual rows per block)"
     k_bytes = nb["partials"]
     achieved = k_bytes / (k_ms * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    traffic = traffic_from_profile(src_hash, args.codes, hg)
+    traffic = None if resid else traffic_from_profile(src_hash, args.codes, hg)
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
@@ -349,7 +373,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": 128, "n_ctx": n, "rank_k": w.rank_k,
                    "rank_v": w.rank_v, "window": w.window, "n_splits": S, "cache_replicas": R,
-                   "codes": args.codes, "head_group": hg},
+                   "codes": args.codes, "head_group": hg, "lowram_resid": resid},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": k_bytes,

@@ -63,6 +63,12 @@ typedef enum lrkv_dtype {
 #define LRKV_MAX_SPLITS 1024
 #define LRKV_MAX_VERSIONS 16  /* basis versions per layer */
 #define LRKV_MAX_HEAD_GROUP 8 /* KV heads sharing one code stream */
+#define LRKV_MAX_RESID 8      /* LowRAM residual rows kept per 32-slot block */
+
+typedef enum lrkv_value_mode {
+  LRKV_VALUES_CODES = 0,  /* values stored as codes C_V = V U_V */
+  LRKV_VALUES_LOWRAM = 1  /* values predicted from the key codes, with residuals (see below) */
+} lrkv_value_mode;
 
 /*
  * One layer of compressed cache.  Storage type `dtype` applies to the bases, the
@@ -120,6 +126,29 @@ typedef enum lrkv_dtype {
  * quantised codes); lrkv_oja_update needs n_g = 1.  Errors: LRKV_ERR_SHAPE for
  * a group size that breaks these limits, LRKV_ERR_DTYPE for float32 storage.
  *
+ * LowRAM value amortisation (value_mode = LRKV_VALUES_LOWRAM; LowRAM abstract:
+ * inside a head the values are largely predictable from the keys, a light
+ * per-head predictor is fitted at test time and residuals are kept only for the
+ * worst-predicted tokens).  No value codes are stored.  Per (batch row b, KV
+ * head h) a predictor M(b, h) of rank_k[h] x 128 maps key codes to values; the
+ * value the decode reads for compressed token t is C_K[t] M + e_t, where e_t is
+ * the residual row V_t - C_K[t] M kept for R = resid_per_block tokens of each
+ * 32-slot block (those with the largest squared norm), and 0 for the others.
+ * lrkv_lowram_fit fits M on the prompt and makes the residuals; lrkv_append
+ * keeps them up to date.  codes_v and the U_V rows of `bases` are not read
+ * (codes_v may be NULL; rank_v still lays out `bases`).  Buffers (nb = cap / 32
+ * blocks per row):
+ *   predictor  bf16, M(b, h) row c (128 values) at element
+ *              (batch * P_h + b * rank_k[h] + c) * 128, P_h = sum of rank_k[h'] for h' < h;
+ *   resid      bf16, entry i of block j of (h, b) at row ((h * batch + b) * nb + j) * R + i,
+ *              128 elements per row;
+ *   resid_slot int32, same entry index: the entry's slot inside its block (0 .. 31),
+ *              or -1 for an empty entry;
+ *   resid_norm float32, same entry index: the squared norm of the entry's residual
+ *              (float32), which decides replacements.
+ * Requires dtype LRKV_BF16, one basis version and head_group <= 1
+ * (LRKV_ERR_DTYPE otherwise) and 1 <= R <= LRKV_MAX_RESID (LRKV_ERR_SHAPE).
+ *
  * 4-bit codes (dtype LRKV_BF16_Q4): the same rule with 7 in place of 127
  * (s = max_c |x_c| / 7, q in [-7, 7]), the same scales.  Element position p of
  * the blocked layout above sits in byte p / 2 of the region, in the low four
@@ -153,6 +182,12 @@ typedef struct lrkv_layer {
                              last version whose start is <= j. */
   int32_t head_group;     /* KV heads sharing one code stream (Palu's group-head
                              latents, see below); 0 or 1: one per KV head */
+  int32_t value_mode;     /* lrkv_value_mode (0: value codes) */
+  int32_t resid_per_block;/* LowRAM: R, residual rows kept per 32-slot block */
+  void *predictor;        /* LowRAM, device, see above (NULL otherwise) */
+  void *resid;            /* LowRAM, device */
+  int32_t *resid_slot;    /* LowRAM, device */
+  float *resid_norm;      /* LowRAM, device */
 } lrkv_layer;
 
 /*
@@ -168,7 +203,8 @@ typedef struct lrkv_layer {
  *      (strides in elements of the storage type; the 128 features contiguous).
  * Errors: LRKV_ERR_SHAPE if n_tok < 0, slot0 < 0 or a stride is negative;
  * LRKV_ERR_CAPACITY if slot0 + n_tok > cap; LRKV_ERR_ALIGN if x or a stride is
- * not 16-byte aligned.  n_tok == 0 is a no-op.
+ * not 16-byte aligned; LRKV_ERR_DTYPE for which = 1 on a LowRAM layer (it has no
+ * value codes).  n_tok == 0 is a no-op.
  */
 lrkv_status lrkv_compress(const lrkv_layer *L, int32_t which, const void *x,
                           int64_t stride_b, int64_t stride_h, int64_t stride_t,
@@ -186,6 +222,29 @@ lrkv_status lrkv_compress(const lrkv_layer *L, int32_t which, const void *x,
 lrkv_status lrkv_quantize(const lrkv_layer *L, int32_t which, const float *x,
                           int64_t stride_b, int64_t stride_h, int64_t stride_t,
                           int32_t n_tok, int32_t slot0, lrkv_stream_t stream);
+
+/*
+ * LowRAM prefill (LowRAM abstract: the per-head predictor is fitted at test
+ * time; the page gives neither its form nor the selection rule, so both are
+ * stated here).  For every (b, h), with C the stored key codes of slots
+ * 0 .. n_tok - 1 (made by lrkv_compress) and V the rows v[b, h, t, :] of the
+ * same tokens (row t = the token in code slot t):
+ *   M = (C^T C + lam I)^-1 C^T V, lam = 1e-6 tr(C^T C) / rank_k[h]   (float32,
+ *       Cholesky), stored as bfloat16 into `predictor`;
+ *   e_t = V_t - C[t] M with M as stored (float32), and for each 32-slot block of
+ *       slots below n_tok the R slots with the largest ||e_t||^2 (float32; equal
+ *       norms: the lower slot) keep e_t (bfloat16, in order of decreasing norm)
+ *       with its slot and norm; the block's other entries are made empty.
+ *   v: device bfloat16, element (b, h, t, i) at v + b*stride_b + h*stride_h + t*stride_t + i.
+ * workspace: device, >= lrkv_lowram_workspace_size(L) bytes, no initialisation.
+ * Errors: LRKV_ERR_DTYPE unless value_mode is LRKV_VALUES_LOWRAM; LRKV_ERR_SHAPE if
+ * n_tok < 1 or a stride is negative; LRKV_ERR_CAPACITY if n_tok > cap;
+ * LRKV_ERR_ALIGN; LRKV_ERR_WORKSPACE.
+ */
+size_t lrkv_lowram_workspace_size(const lrkv_layer *L);
+lrkv_status lrkv_lowram_fit(const lrkv_layer *L, const void *v, int64_t stride_b, int64_t stride_h,
+                            int64_t stride_t, int32_t n_tok, void *workspace, size_t workspace_bytes,
+                            lrkv_stream_t stream);
 
 /*
  * Online basis adaptation (OjaKV summary and FAQ: Oja's algorithm for online PCA
@@ -237,7 +296,13 @@ lrkv_status lrkv_store_anchors(const lrkv_layer *L, const void *k, const void *v
  *  - window == 0 and pos >= 1: the new token is compressed into code slot pos - 1.
  *  - otherwise the new token is stored into its anchor slot.
  * With basis versions the code is made with the version the code slot belongs
- * to (version_start of the row).  With head groups the group's code is made from
+ * to (version_start of the row).  LowRAM layers: the key is compressed as usual
+ * and the value's residual e = V - C_K M (float32, C_K the stored code) enters the
+ * slot's block: a slot opening a block (slot % 32 == 0) first empties the block's
+ * entries; the residual takes an empty entry if there is one, else replaces the
+ * entry of smallest norm (among equal ones the highest slot) if its own squared
+ * norm is strictly larger.  The block then keeps the same slots lrkv_lowram_fit
+ * would choose.  With head groups the group's code is made from
  * the leaving rows of all its KV heads, and each KV head's anchor slot is updated.
  * Errors: LRKV_ERR_SHAPE if pos < 0; LRKV_ERR_CAPACITY if the code slot >= cap.
  */

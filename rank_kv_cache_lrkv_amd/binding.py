@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_PKG, "liblrkv.so")
 
 LRKV_F32, LRKV_BF16, LRKV_BF16_Q8, LRKV_BF16_Q4 = 0, 1, 2, 3
 QUANTISED = (LRKV_BF16_Q8, LRKV_BF16_Q4)
+LRKV_VALUES_CODES, LRKV_VALUES_LOWRAM = 0, 1
 HEAD_DIM = 128
 BLOCK = 32
 
@@ -50,6 +51,8 @@ class lrkv_layer(ctypes.Structure):
         ("scales_k", c_void_p), ("scales_v", c_void_p),
         ("n_versions", c_int32), ("version_start", c_void_p),
         ("head_group", c_int32),
+        ("value_mode", c_int32), ("resid_per_block", c_int32),
+        ("predictor", c_void_p), ("resid", c_void_p), ("resid_slot", c_void_p), ("resid_norm", c_void_p),
     ]
 
 
@@ -61,6 +64,9 @@ _P = POINTER(lrkv_layer)
 SIGNATURES = [
     ("lrkv_compress", c_int32, [_P, c_int32, c_void_p, c_int64, c_int64, c_int64, c_int32, c_int32, c_void_p]),
     ("lrkv_quantize", c_int32, [_P, c_int32, c_void_p, c_int64, c_int64, c_int64, c_int32, c_int32, c_void_p]),
+    ("lrkv_lowram_workspace_size", c_size_t, [_P]),
+    ("lrkv_lowram_fit", c_int32, [_P, c_void_p, c_int64, c_int64, c_int64, c_int32, c_void_p, c_size_t,
+                                  c_void_p]),
     ("lrkv_oja_workspace_size", c_size_t, [_P]),
     ("lrkv_oja_update", c_int32, [_P, c_int32, c_void_p, c_int64, c_int64, c_int64, c_int32, c_float,
                                   c_int32, c_int32, c_void_p, c_size_t, c_void_p]),
@@ -146,6 +152,12 @@ class Layer:
     n_versions: int = 1
     version_start: "object" = None  # int32 [batch][n_versions] (device) when n_versions > 1
     head_group: int = 1  # KV heads sharing one code stream; rank_k / rank_v per group
+    value_mode: int = LRKV_VALUES_CODES
+    resid_per_block: int = 0  # LowRAM: residual entries per 32-slot block
+    predictor: "object" = None  # LowRAM: bf16 M(b, h) rows
+    resid: "object" = None      # LowRAM: bf16 [n_kv][batch][cap / 32][R][128]
+    resid_slot: "object" = None  # LowRAM: int32 [n_kv][batch][cap / 32][R]
+    resid_norm: "object" = None  # LowRAM: float32, same shape
     _rk: object = field(default=None, repr=False)
     _rv: object = field(default=None, repr=False)
     struct: lrkv_layer = field(default=None, repr=False)
@@ -158,7 +170,9 @@ class Layer:
             ctypes.cast(self._rk, POINTER(c_int32)), ctypes.cast(self._rv, POINTER(c_int32)),
             _ptr(self.bases), _ptr(self.codes_k), _ptr(self.codes_v),
             _ptr(self.anchor_k), _ptr(self.anchor_v), _ptr(self.scales_k), _ptr(self.scales_v),
-            int(self.n_versions), _ptr(self.version_start), int(self.head_group))
+            int(self.n_versions), _ptr(self.version_start), int(self.head_group),
+            int(self.value_mode), int(self.resid_per_block), _ptr(self.predictor), _ptr(self.resid),
+            _ptr(self.resid_slot), _ptr(self.resid_norm))
 
     @property
     def group(self) -> int:
@@ -186,11 +200,13 @@ class Layer:
     @classmethod
     def allocate(cls, *, dtype: int, batch: int, n_q_heads: int, n_kv_heads: int, window: int,
                  cap: int, rank_k: Sequence[int], rank_v: Sequence[int], device="cuda",
-                 bases=None, n_versions: int = 1, head_group: int = 1) -> "Layer":
+                 bases=None, n_versions: int = 1, head_group: int = 1, lowram_resid: int = 0) -> "Layer":
         """Allocate zeroed codes and anchors (and int8 scales) (torch) for the given
         geometry.  ``bases`` (optional) is the flat bases tensor; otherwise zeros.
         With ``head_group`` > 1, rank_k / rank_v hold one rank per group of
-        ``head_group`` KV heads."""
+        ``head_group`` KV heads.  ``lowram_resid`` = R > 0 makes a LowRAM layer
+        (values predicted from the key codes, R residual rows per block): no value
+        codes, a zeroed predictor and empty residual entries."""
         import torch
         td = torch.float32 if dtype == LRKV_F32 else torch.bfloat16
         cd = {LRKV_BF16_Q8: torch.int8, LRKV_BF16_Q4: torch.uint8}.get(dtype, td)
@@ -214,6 +230,15 @@ class Layer:
                              device=device)
             sv = torch.zeros_like(sk)
         vs = torch.zeros((batch, n_versions), dtype=torch.int32, device=device) if n_versions > 1 else None
+        if lowram_resid > 0:
+            cv = None
+            ne = layout.resid_entries(n_kv_heads, batch, cap, lowram_resid)
+            pred = torch.zeros(max(1, layout.predictor_elems(rk, batch)), dtype=td, device=device)
+            res = torch.zeros((max(1, ne), HEAD_DIM), dtype=td, device=device)
+            rsl = torch.full((max(1, ne),), -1, dtype=torch.int32, device=device)
+            rno = torch.zeros(max(1, ne), dtype=torch.float32, device=device)
+            return cls(dtype, batch, n_q_heads, n_kv_heads, window, cap, rk, rv, bases, ck, cv, ak, av, sk, sv,
+                       n_versions, vs, hg, LRKV_VALUES_LOWRAM, lowram_resid, pred, res, rsl, rno)
         return cls(dtype, batch, n_q_heads, n_kv_heads, window, cap, rk, rv, bases, ck, cv, ak, av, sk, sv,
                    n_versions, vs, hg)
 
@@ -239,6 +264,23 @@ def lrkv_quantize(layer: Layer, which: int, x, n_tok: int, slot0: int, stream=No
     assert si == 1
     _check(lib().lrkv_quantize(ctypes.byref(layer.struct), which, _ptr(x), sb, sh, st, n_tok, slot0,
                                _stream(stream)), "lrkv_quantize")
+
+
+def lrkv_lowram_workspace_size(layer: Layer) -> int:
+    return int(lib().lrkv_lowram_workspace_size(ctypes.byref(layer.struct)))
+
+
+def lrkv_lowram_fit(layer: Layer, v, n_tok: int, ws=None, stream=None):
+    """v: bf16 device tensor viewed as [batch][n_kv_heads][>= n_tok][128], row t the
+    value of the token in code slot t (last dimension contiguous).  ``ws``:
+    workspace (uint8 device tensor) or None to allocate one."""
+    import torch
+    sb, sh, st, si = v.stride()
+    assert si == 1
+    if ws is None:
+        ws = torch.empty(max(1, lrkv_lowram_workspace_size(layer)), dtype=torch.uint8, device=v.device)
+    _check(lib().lrkv_lowram_fit(ctypes.byref(layer.struct), _ptr(v), sb, sh, st, n_tok, _ptr(ws), ws.numel(),
+                                 _stream(stream)), "lrkv_lowram_fit")
 
 
 def lrkv_oja_workspace_size(layer: Layer) -> int:

@@ -28,10 +28,12 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   if (L->window < 0 || L->cap < 0 || L->cap % LRKV_BLOCK) return LRKV_ERR_SHAPE;
   // one (row, head) code region is addressed with 32-bit byte offsets
   if (int64_t(L->cap) * kD * elem_bytes(L->dtype) > INT32_MAX) return LRKV_ERR_SHAPE;
-  if (!L->rank_k || !L->rank_v || !L->bases || !L->codes_k || !L->codes_v || !L->anchor_k ||
+  if (L->value_mode != LRKV_VALUES_CODES && L->value_mode != LRKV_VALUES_LOWRAM) return LRKV_ERR_DTYPE;
+  const bool lr = L->value_mode == LRKV_VALUES_LOWRAM;  // no value codes
+  if (!L->rank_k || !L->rank_v || !L->bases || !L->codes_k || (!lr && !L->codes_v) || !L->anchor_k ||
       !L->anchor_v)
     return LRKV_ERR_NULL;
-  if (!aligned16(L->bases) || !aligned16(L->codes_k) || !aligned16(L->codes_v) ||
+  if (!aligned16(L->bases) || !aligned16(L->codes_k) || (!lr && !aligned16(L->codes_v)) ||
       !aligned16(L->anchor_k) || !aligned16(L->anchor_v))
     return LRKV_ERR_ALIGN;
   const int32_t nver = L->n_versions == 0 ? 1 : L->n_versions;
@@ -46,6 +48,14 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   if (quantised(L->dtype)) {
     if (!L->scales_k || !L->scales_v) return LRKV_ERR_NULL;
     if (!aligned16(L->scales_k) || !aligned16(L->scales_v)) return LRKV_ERR_ALIGN;
+  }
+  if (lr) {
+    if (L->dtype != LRKV_BF16 || nver > 1 || hg > 1) return LRKV_ERR_DTYPE;
+    if (L->resid_per_block < 1 || L->resid_per_block > LRKV_MAX_RESID) return LRKV_ERR_SHAPE;
+    if (!L->predictor || !L->resid || !L->resid_slot || !L->resid_norm) return LRKV_ERR_NULL;
+    if (!aligned16(L->predictor) || !aligned16(L->resid) || !aligned16(L->resid_slot) ||
+        !aligned16(L->resid_norm))
+      return LRKV_ERR_ALIGN;
   }
   std::memset(A, 0, sizeof(*A));
   A->dtype = L->dtype;
@@ -64,14 +74,16 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   A->anchor_v = L->anchor_v;
   A->scales_k = quantised(L->dtype) ? L->scales_k : nullptr;
   A->scales_v = quantised(L->dtype) ? L->scales_v : nullptr;
-  int64_t ub = 0, ck = 0, cv = 0;
+  int64_t ub = 0, ck = 0, cv = 0, pr = 0;
   int rv_max = 0;
   for (int h = 0; h < A->n_lat; ++h) {
     const int32_t rk = L->rank_k[h], rv = L->rank_v[h];
     if (!valid_rank(rk) || !valid_rank(rv)) return LRKV_ERR_RANK;
     HeadInfo &hd = A->heads[h];
     hd.rk = rk;
-    hd.rv = rv;
+    hd.rv = lr ? rk : rv;  // LowRAM value sums run over the key codes
+    hd.pred = pr;
+    pr += int64_t(L->batch) * rk * kD;
     hd.u_k = int32_t(ub);
     hd.u_v = int32_t(ub + int64_t(hg) * kD * rk);
     hd.ck = ck;
@@ -79,12 +91,20 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
     ub += int64_t(hg) * kD * (rk + rv);
     ck += int64_t(L->batch) * L->cap * rk;
     cv += int64_t(L->batch) * L->cap * rv;
-    rv_max = rv > rv_max ? rv : rv_max;
+    rv_max = hd.rv > rv_max ? hd.rv : rv_max;
   }
   A->rv_max = rv_max;
   A->n_versions = nver;
   A->vstart = nver > 1 ? L->version_start : nullptr;
   A->version_elems = ub;
+  if (lr) {
+    A->lowram = 1;
+    A->R = L->resid_per_block;
+    A->pred = L->predictor;
+    A->resid = L->resid;
+    A->rslot = L->resid_slot;
+    A->rnorm = L->resid_norm;
+  }
   return LRKV_OK;
 }
 
@@ -160,6 +180,7 @@ lrkv_status lrkv_compress(const lrkv_layer *L, int32_t which, const void *x, int
   lrkv_status st = make_layer(L, &A);
   if (st != LRKV_OK) return st;
   if (which != 0 && which != 1) return LRKV_ERR_SHAPE;
+  if (which == 1 && A.lowram) return LRKV_ERR_DTYPE;  // no value codes
   if (n_tok < 0 || slot0 < 0) return LRKV_ERR_SHAPE;
   if (int64_t(slot0) + n_tok > L->cap) return LRKV_ERR_CAPACITY;
   if (n_tok == 0) return LRKV_OK;
@@ -215,6 +236,30 @@ lrkv_status lrkv_oja_update(const lrkv_layer *L, int32_t which, const void *x, i
   return hip_status(launch_oja(A, which, x, stride_b, stride_h, stride_t, n_tok, eta, version_in,
                                version_out, static_cast<float *>(workspace),
                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t lrkv_lowram_workspace_size(const lrkv_layer *L) {
+  LayerArgs A;
+  if (make_layer(L, &A) != LRKV_OK || !A.lowram) return 0;
+  return lowram_workspace_bytes(A);
+}
+
+lrkv_status lrkv_lowram_fit(const lrkv_layer *L, const void *v, int64_t stride_b, int64_t stride_h,
+                            int64_t stride_t, int32_t n_tok, void *workspace, size_t workspace_bytes,
+                            lrkv_stream_t stream) {
+  LayerArgs A;
+  lrkv_status st = make_layer(L, &A);
+  if (st != LRKV_OK) return st;
+  if (!A.lowram) return LRKV_ERR_DTYPE;
+  if (n_tok < 1) return LRKV_ERR_SHAPE;
+  if (n_tok > L->cap) return LRKV_ERR_CAPACITY;
+  if (!v) return LRKV_ERR_NULL;
+  st = check_strides(L, v, stride_b, stride_h, stride_t);
+  if (st != LRKV_OK) return st;
+  if (!workspace || workspace_bytes < lowram_workspace_bytes(A)) return LRKV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return LRKV_ERR_ALIGN;
+  return hip_status(launch_lowram_fit(A, static_cast<const bf16_t *>(v), stride_b, stride_h, stride_t, n_tok,
+                                      static_cast<float *>(workspace), reinterpret_cast<hipStream_t>(stream)));
 }
 
 lrkv_status lrkv_store_anchors(const lrkv_layer *L, const void *k, const void *v, int64_t stride_b,

@@ -83,6 +83,68 @@ __device__ __forceinline__ float block_absmax(float x, float *red) {
   return a;
 }
 
+// sum over the 128 threads of the workgroup (every thread calls it)
+__device__ __forceinline__ float block_sum(float x, float *red) {
+  float w = x;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) w += __shfl_xor(w, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
+  __syncthreads();
+  const float a = red[0] + red[1];
+  __syncthreads();
+  return a;
+}
+
+// LowRAM (values from the key codes, residuals kept for the worst-predicted
+// tokens of each block): the value of code slot j enters its block.  Thread t
+// holds column t of the stored key code (0 past rank_k) and feature t of the
+// value.  e = v - code M (float32); a slot opening a block empties the block's
+// entries first; the residual takes an empty entry, else replaces the entry of
+// smallest squared norm (among equal ones the highest slot) if its own norm is
+// strictly larger.  Inserting a block's slots in order this way keeps its R
+// largest norms (equal norms: the lower slots).
+__device__ void lowram_insert(const LayerArgs &L, int h, int b, int j, float code_t, float v_t, float *red) {
+  __shared__ float s_code[kD];
+  __shared__ int s_take;
+  const int tid = threadIdx.x;
+  const HeadInfo hd = L.heads[h];
+  s_code[tid] = code_t;
+  __syncthreads();
+  const bf16_t *m = static_cast<const bf16_t *>(L.pred) + hd.pred + int64_t(b) * hd.rk * kD;
+  float pr = 0.f;
+  for (int c = 0; c < hd.rk; ++c) pr = fmaf(s_code[c], to_f32(m[c * kD + tid]), pr);
+  const float e = v_t - pr;
+  const float sq = block_sum(e * e, red);
+  const int blk = j / kBlock, sl = j % kBlock;
+  const int64_t e0 = resid_entry(L, h, b, blk, 0);
+  if (tid == 0) {
+    if (sl == 0)
+      for (int i = 0; i < L.R; ++i) L.rslot[e0 + i] = -1;
+    int take = -1, low = -1;
+    float lown = 0.f;
+    for (int i = 0; i < L.R; ++i) {
+      const int si = L.rslot[e0 + i];
+      if (si < 0) {
+        if (take < 0) take = i;
+      } else {
+        const float ni = L.rnorm[e0 + i];
+        if (low < 0 || ni < lown || (ni == lown && si > L.rslot[e0 + low])) {
+          low = i;
+          lown = ni;
+        }
+      }
+    }
+    if (take < 0 && low >= 0 && sq > lown) take = low;
+    if (take >= 0) {
+      L.rslot[e0 + take] = sl;
+      L.rnorm[e0 + take] = sq;
+    }
+    s_take = take;
+  }
+  __syncthreads();
+  if (s_take >= 0) static_cast<bf16_t *>(L.resid)[(e0 + s_take) * kD + tid] = from_f32<bf16_t>(e);
+}
+
 // QMAX: 0 for bf16 / f32 codes, 127 for int8 codes, 7 for 4-bit codes
 template <typename T, int QMAX>
 __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, const T *vnew, int pos) {
@@ -130,7 +192,7 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
     if (tid < hd.rk)
       for (int j = 0; j < hg; ++j)
         for (int k = 0; k < kD; ++k) acck = fmaf(rk_row[j][k], to_f32(Uk[tid * urow + j * kD + k]), acck);
-    if (tid < hd.rv)
+    if (tid < hd.rv && !L.lowram)  // LowRAM layers have no value codes
       for (int j = 0; j < hg; ++j)
         for (int k = 0; k < kD; ++k) accv = fmaf(rv_row[j][k], to_f32(Uv[tid * urow + j * kD + k]), accv);
     if constexpr (QMAX > 0) {
@@ -154,9 +216,13 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
       }
     } else {
       T *ck = static_cast<T *>(L.codes_k) + hd.ck + int64_t(b) * L.cap * hd.rk;
-      T *cv = static_cast<T *>(L.codes_v) + hd.cv + int64_t(b) * L.cap * hd.rv;
       if (tid < hd.rk) ck[kslot(code_slot, tid, hd.rk)] = from_f32<T>(acck);
-      if (tid < hd.rv) cv[vslot(code_slot, tid, hd.rv)] = from_f32<T>(accv);
+      if (!L.lowram) {
+        T *cv = static_cast<T *>(L.codes_v) + hd.cv + int64_t(b) * L.cap * hd.rv;
+        if (tid < hd.rv) cv[vslot(code_slot, tid, hd.rv)] = from_f32<T>(accv);
+      } else {
+        lowram_insert(L, h, b, code_slot, tid < hd.rk ? to_f32(from_f32<T>(acck)) : 0.f, rv_row[0][tid], red);
+      }
     }
   }
   if (slot >= 0) {

@@ -134,13 +134,18 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, floa
   const int a1 = min(row_ctx(d, b), 1 + L.window);  // anchor rows per KV head
   const int per = anchor_rows_per_split(a1 * L.hg, S);
   // splits s_a0 .. s_a1 - 1 hold this KV head's anchor rows j a1 .. (j + 1) a1 - 1
-  // (the unit's rows, KV head after KV head, cut into runs of per rows)
-  const int s_a0 = (j * a1) / per, s_a1 = min(S, ((j + 1) * a1 + per - 1) / per);
-  // U_V^T rows (hg * 128 elements, this KV head's slice at j * 128): element
-  // (c, t) of the slice is column c of output feature t
+  // (the unit's rows, KV head after KV head, cut into runs of per rows); LowRAM:
+  // every split holds residual sums there
+  const int s_a0 = L.lowram ? 0 : (j * a1) / per;
+  const int s_a1 = L.lowram ? S : min(S, ((j + 1) * a1 + per - 1) / per);
+  // U_V^T rows (hg * 128 elements, this KV head's slice at j * 128), or for LowRAM
+  // the row's predictor M (rank_k rows of 128): element (c, t) of the slice is
+  // column c of output feature t
   const int urow = L.hg * kD;
-  const __amdgpu_buffer_rsrc_t ur = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T *>(static_cast<const T *>(L.bases) + hd.u_v), 0, rv * urow * int(sizeof(T)), kBufferWord3);
+  const T *ubase = L.lowram ? static_cast<const T *>(L.pred) + hd.pred + int64_t(b) * rv * kD
+                            : static_cast<const T *>(L.bases) + hd.u_v;
+  const __amdgpu_buffer_rsrc_t ur =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(ubase), 0, rv * urow * int(sizeof(T)), kBufferWord3);
   auto uv = [&](int c) { return buffer_elem<T>(ur, (c * urow + j * kD + t) * int(sizeof(T))); };
   const int groups = 128 / rv;
   const int col = t % rv, grp = t / rv;

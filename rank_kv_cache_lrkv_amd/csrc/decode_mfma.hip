@@ -74,6 +74,8 @@ template <int NKC, int NVC, int CB>
 struct BlockRegs {
   u32x4 k[2][NKC];
   u32x4 v[NVC];
+  uint32_t e[LRKV_MAX_RESID];  // LowRAM: features 2 lane, 2 lane + 1 of the block's residual rows
+  uint32_t es;                 // LowRAM: lane i < R holds the in-block slot of entry i
 };
 // int8 codes: 8 bytes per lane and operand, and one key and one value scale per
 // lane: lane (q4, t16) of the 16-lane row q4 holds those of token
@@ -149,7 +151,16 @@ __device__ __forceinline__ u32x4 i4x8_to_bf16_x16(uint32_t w) {
 // product times the key scale, and a token's weight is multiplied by its value
 // scale before it becomes the value MFMA's A operand (the denominator keeps the
 // plain weight).
-template <int RKMAX, int RVMAX, bool EXACT, int CB>
+//
+// LR: LowRAM value amortisation (bf16 codes, RVMAX == RKMAX).  No value codes are
+// read: the value operand of a block is its key codes transposed (8 tokens of one
+// column per lane), made on the matrix cores as the product with a 0/1 selector,
+// which lands the codes exactly in the layout the value MFMA takes; the rank-space
+// sum over the key codes is up-projected by the combine with the row's predictor
+// M.  The block's kept residual rows (R entries: slot, 128 bf16) are loaded with
+// the block and added as p[t][h] e_t into 128-dim sums per head (each lane two
+// features), which leave the split with the anchor sums.
+template <int RKMAX, int RVMAX, bool EXACT, int CB, bool LR = false>
 __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d) {
   constexpr int NKC = (RKMAX + 31) / 32;  // score MFMAs per 16-token tile (K = 32 each)
   constexpr int NVC = RVMAX / 16;         // value MFMAs per block (16 columns each)
@@ -236,6 +247,14 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
     svres = __builtin_amdgcn_make_buffer_rsrc(L.scales_v + scale_index(L, h, b, 0), 0, L.cap * 4, kBufferWord3);
   }
   const int soff = (16 * ((t16 >> 2) & 1) + 4 * q4 + (t16 & 3)) * 4;  // this lane's scale in a block
+  // LowRAM: this (row, head)'s residual entries, R per block
+  __amdgpu_buffer_rsrc_t eres = kres, esres = kres;
+  if constexpr (LR) {
+    const int64_t e0 = resid_entry(L, h, b, 0, 0);
+    eres = __builtin_amdgcn_make_buffer_rsrc(static_cast<bf16_t *>(L.resid) + e0 * kD, 0,
+                                             (L.cap / kBlock) * L.R * kD * 2, kBufferWord3);
+    esres = __builtin_amdgcn_make_buffer_rsrc(L.rslot + e0, 0, (L.cap / kBlock) * L.R * 4, kBufferWord3);
+  }
   const int kblk_bytes = kBlock * rk * CB / 8, vblk_bytes = kBlock * rv * CB / 8;
   int koff[2][NKC];
 #pragma unroll
@@ -276,8 +295,18 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc)
           r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b128(kres, koff[h2][kc], ks, 0);
+      if constexpr (!LR) {
 #pragma unroll
-      for (int ni = 0; ni < NVC; ++ni) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b128(vres, voff[ni], vs, 0);
+        for (int ni = 0; ni < NVC; ++ni) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b128(vres, voff[ni], vs, 0);
+      }
+    }
+    if constexpr (LR) {
+      const int es = __builtin_amdgcn_readfirstlane(blk * L.R * kD * 2);
+#pragma unroll
+      for (int i = 0; i < LRKV_MAX_RESID; ++i)
+        if (i < L.R) r.e[i] = __builtin_amdgcn_raw_buffer_load_b32(eres, lane * 4 + i * kD * 2, es, 0);
+      r.es = __builtin_amdgcn_raw_buffer_load_b32(esres, min(lane, L.R - 1) * 4,
+                                                  __builtin_amdgcn_readfirstlane(blk * L.R * 4), 0);
     }
   };
 
@@ -462,8 +491,33 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   f32x4 o[NVC];
 #pragma unroll
   for (int ni = 0; ni < NVC; ++ni) o[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // LowRAM: residual sums (lane: features 2 lane, 2 lane + 1 of every head), and the
+  // selectors B[k][n] = (k == 16 half + n) that pick 16 of a fragment's 32 columns
+  float res[LRKV_MAX_GROUP][2];
+  u32x4 sel[2];
+  if constexpr (LR) {
+#pragma unroll
+    for (int hh = 0; hh < LRKV_MAX_GROUP; ++hh) res[hh][0] = res[hh][1] = 0.f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int idx = 16 * half + t16 - 8 * q4;  // the element of this lane's 8 that is 1, if any
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sel[half][i] = (idx == 2 * i ? 0x3f80u : 0u) | (idx == 2 * i + 1 ? 0x3f800000u : 0u);
+    }
+  }
 
   auto process = [&](int blk, BlockRegs<NKC, NVC, CB> &r) {
+    if constexpr (LR) {  // slots past c may hold any bits: their codes become 0 (the
+                         // transposes below mix a token's columns; scores are masked anyway)
+      if (blk * kBlock + kBlock > c) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          if (blk * kBlock + 16 * h2 + t16 >= c)
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) r.k[h2][kc] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
     f32x4 s[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) s[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -540,6 +594,42 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
 #pragma unroll
         for (int ni = 0; ni < NVC; ++ni) o[ni][v] *= a;
       }
+      if constexpr (LR) {  // head hh's factor sits in lane hh
+#pragma unroll
+        for (int hh = 0; hh < LRKV_MAX_GROUP; ++hh) {
+          if (hh < G) {
+            const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), hh));
+            res[hh][0] *= a;
+            res[hh][1] *= a;
+          }
+        }
+      }
+    }
+    if constexpr (LR) {
+      // kept residual rows: entry i holds slot t of this block (wave-uniform); head
+      // hh's weight of token t sits in lane 16 ((t % 16) / 4) + hh, register
+      // 4 (t / 16) + t % 4
+#pragma unroll
+      for (int i = 0; i < LRKV_MAX_RESID; ++i) {
+        if (i < L.R) {
+          const int t = __builtin_amdgcn_readlane(int(r.es), i);
+          if (t >= 0 && blk * kBlock + t < c) {
+            const int jsel = 4 * (t >> 4) + (t & 3), lsel = 16 * ((t & 15) >> 2);
+            float pv = p[0];
+#pragma unroll
+            for (int jj = 1; jj < 8; ++jj) pv = jsel == jj ? p[jj] : pv;
+            const float e0 = __uint_as_float(r.e[i] << 16), e1 = __uint_as_float(r.e[i] & 0xffff0000u);
+#pragma unroll
+            for (int hh = 0; hh < LRKV_MAX_GROUP; ++hh) {
+              if (hh < G) {
+                const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), lsel + hh));
+                res[hh][0] = fmaf(w, e0, res[hh][0]);
+                res[hh][1] = fmaf(w, e1, res[hh][1]);
+              }
+            }
+          }
+        }
+      }
     }
     // weights as the A operand (k-slot j = 4 h + v), hi and lo parts
     if constexpr (QC) {
@@ -565,7 +655,15 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
         u32x4 bv;
         if constexpr (CB == 8) bv = i8x8_to_bf16(r.v[ni]);
         else if constexpr (CB == 4) bv = i4x8_to_bf16_x16(r.v[ni]);
-        else bv = r.v[ni];
+        else if constexpr (LR) {
+          // the key codes of columns 16 ni .. 16 ni + 15 as the value operand:
+          // D[token][n] = C[token][32 kc + 16 half + n], lane (q4, t16) gets tokens
+          // 16 h2 + 4 q4 + v of column 16 ni + t16, exact in float32
+          const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+          const f32x4 d0 = mfma16x16x32(r.k[0][ni >> 1], sel[ni & 1], z);
+          const f32x4 d1 = mfma16x16x32(r.k[1][ni >> 1], sel[ni & 1], z);
+          bv = u32x4{pack_hi(d0[0], d0[1]), pack_hi(d0[2], d0[3]), pack_hi(d1[0], d1[1]), pack_hi(d1[2], d1[3])};
+        } else bv = r.v[ni];
         o[ni] = mfma16x16x32(a_hi, bv, o[ni]);
         o[ni] = mfma16x16x32(a_lo, bv, o[ni]);
       }
@@ -632,7 +730,38 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   }
   // o_A of the heads whose KV head has anchor rows in this split; the combine
   // reads it from exactly these splits and skips the others
-  if (na > 0) {
+  if constexpr (LR) {
+    // every split: the waves' residual sums and the anchor sums under the head's
+    // common max, added into sm.u.oa wave by wave (wave 0 first, over its anchors)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (wave == w) {
+#pragma unroll
+        for (int hh = 0; hh < LRKV_MAX_GROUP; ++hh) {
+          if (hh < G) {
+            const float M = head_max(hh);
+            const float f = weight(w, hh, M);
+            float x0 = f * res[hh][0], x1 = f * res[hh][1];
+            if (w > 0) {
+              x0 += sm.u.oa[hh][2 * lane];
+              x1 += sm.u.oa[hh][2 * lane + 1];
+            } else if (na > 0) {
+              const float fa = weight(4, hh, M);
+              x0 = fmaf(fa, sm.u.oa[hh][2 * lane], x0);
+              x1 = fmaf(fa, sm.u.oa[hh][2 * lane + 1], x1);
+            }
+            sm.u.oa[hh][2 * lane] = x0;
+            sm.u.oa[hh][2 * lane + 1] = x1;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    for (int i = tid; i < G * kD; i += blockDim.x) {
+      const int hh = i / kD, cc = i - hh * kD;
+      split_record(d, q0 + hh, split)[d.oa + cc] = sm.u.oa[hh][cc];
+    }
+  } else if (na > 0) {
     for (int i = tid; i < G * kD; i += blockDim.x) {
       const int hh = i / kD, cc = i - hh * kD;
       const int jj = hh / GK;
@@ -693,12 +822,29 @@ static int cu_count() {
   return cached[dev];
 }
 
+// LowRAM layers: value sums over the key codes (RVMAX = RKMAX), bf16 codes
+template <int RKMAX>
+static hipError_t launch_lr(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
+  bool exact = true;
+  for (int h = 0; h < L.n_lat; ++h) exact = exact && L.heads[h].rk == RKMAX;
+  dim3 grid(d.n_splits, L.batch * L.n_lat);
+  if (exact) hipLaunchKernelGGL((k_partials_mfma<RKMAX, RKMAX, true, 16, true>), grid, dim3(256), 0, s, L, d);
+  else hipLaunchKernelGGL((k_partials_mfma<RKMAX, RKMAX, false, 16, true>), grid, dim3(256), 0, s, L, d);
+  return hipGetLastError();
+}
+
 hipError_t launch_partials_mfma(const LayerArgs &L, const DecodeArgs &d0, hipStream_t s) {
   DecodeArgs d = d0;
   // balancing pays when the whole grid is resident at once (four workgroups per CU)
   d.balance = int64_t(d.n_splits) * L.batch * L.n_lat <= 4 * int64_t(cu_count());
   int rk_max = 0;
   for (int h = 0; h < L.n_lat; ++h) rk_max = L.heads[h].rk > rk_max ? L.heads[h].rk : rk_max;
+  if (L.lowram) {
+    if (rk_max <= 32) return launch_lr<32>(L, d, s);
+    if (rk_max <= 64) return launch_lr<64>(L, d, s);
+    if (rk_max <= 96) return launch_lr<96>(L, d, s);
+    return launch_lr<128>(L, d, s);
+  }
   if (rk_max <= 32) return launch_rk<32>(L, d, s);
   if (rk_max <= 64) return launch_rk<64>(L, d, s);
   if (rk_max <= 96) return launch_rk<96>(L, d, s);

@@ -17,6 +17,7 @@ struct HeadInfo {
   int32_t rk, rv;
   int32_t u_k, u_v;  // offsets of U_K(h), U_V(h) in the bases buffer (rows of hg * 128)
   int64_t ck, cv;    // offsets of head h's [batch][cap][r] code region
+  int64_t pred;      // LowRAM: element offset of M(0, h) in the predictor buffer
 };
 
 // With group-head latents (hg > 1) the hg consecutive KV heads of latent group g
@@ -31,8 +32,20 @@ struct LayerArgs {
   int32_t n_versions;          // basis versions (>= 1)
   const int32_t *vstart;       // [batch][n_versions] first code slot of each version (n_versions > 1)
   int64_t version_elems;       // elements of one version of the bases
+  // LowRAM value amortisation: values are C_K M(b, h) plus kept residual rows;
+  // for these layers heads[h].rv == heads[h].rk (the value sums are rank_k wide)
+  int32_t lowram, R;           // the mode, residual entries per 32-slot block
+  void *pred;                  // bf16 M(b, h) rows (rank_k x 128)
+  void *resid;                 // bf16 residual rows, [h][b][cap / 32][R][128]
+  int32_t *rslot;              // in-block slot of each entry, -1 empty
+  float *rnorm;                // squared norm of each entry
   HeadInfo heads[LRKV_MAX_KV_HEADS];
 };
+
+// LowRAM: index of entry i of block j of (head h, row b)
+__host__ __device__ __forceinline__ int64_t resid_entry(const LayerArgs &L, int h, int b, int j, int i) {
+  return ((int64_t(h) * L.batch + b) * (L.cap / kBlock) + j) * L.R + i;
+}
 
 // Split s of a (batch row, KV head) covers a share of its code blocks and a
 // share of its a anchors (runs of at least 16 rows on the first splits); per
@@ -150,5 +163,8 @@ hipError_t launch_decode_combine(const LayerArgs &L, const DecodeArgs &d, float 
 hipError_t launch_oja(const LayerArgs &L, int which, const void *x, int64_t sb, int64_t sh, int64_t st,
                       int n_tok, float eta, int vin, int vout, float *ws, hipStream_t s);
 size_t oja_workspace_bytes(const LayerArgs &L);
+hipError_t launch_lowram_fit(const LayerArgs &L, const bf16_t *v, int64_t sb, int64_t sh, int64_t st, int n_tok,
+                             float *ws, hipStream_t s);
+size_t lowram_workspace_bytes(const LayerArgs &L);
 
 }  // namespace lrkv

@@ -70,6 +70,27 @@ def scale_offset(h: int, b: int, cap: int, batch: int) -> int:
     return (int(h) * int(batch) + int(b)) * int(cap)
 
 
+def predictor_elems(rank_k: Sequence[int], batch: int) -> int:
+    """Elements of a LowRAM predictor buffer: M(b, h), rank_k[h] rows of 128."""
+    return HEAD_DIM * int(batch) * int(np.sum(rank_k))
+
+
+def predictor_offset(rank_k: Sequence[int], batch: int, h: int, b: int) -> int:
+    """Element offset of M(b, h)'s first row."""
+    r = np.asarray(rank_k, np.int64)
+    return int(HEAD_DIM * (int(batch) * int(np.sum(r[:h])) + int(b) * int(r[h])))
+
+
+def resid_entries(n_kv_heads: int, batch: int, cap: int, r: int) -> int:
+    """LowRAM residual entries: R per 32-slot block of every (KV head, row)."""
+    return int(n_kv_heads) * int(batch) * (int(cap) // BLOCK) * int(r)
+
+
+def resid_entry(h: int, b: int, blk: int, i: int, batch: int, cap: int, r: int) -> int:
+    """Index of entry i of block blk of (KV head h, row b)."""
+    return ((int(h) * int(batch) + int(b)) * (int(cap) // BLOCK) + int(blk)) * int(r) + int(i)
+
+
 def block_positions(r: int, which: str) -> np.ndarray:
     """In-block element position of (slot t in 0..31, column c in 0..r-1)."""
     t = np.arange(BLOCK)[:, None]

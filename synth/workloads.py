@@ -34,6 +34,7 @@ _ROLE = {
     "tok_v": 6,
     "query": 7,
     "ranks": 8,
+    "vmap": 9,
 }
 
 
@@ -60,6 +61,7 @@ class Workload:
     mixed_ranks: bool = False
     rank_k_choices: Tuple[int, ...] = (32, 48, 64, 96)
     rank_v_choices: Tuple[int, ...] = (16, 32)
+    v_from_k: float = 0.0         # values = a (keys @ Q) + sqrt(1 - a^2) (independent rows), Q orthogonal
     description: str = field(default="", compare=False)
 
     @property
@@ -188,11 +190,21 @@ def group_basis(w: Workload, layer: int, group: int, head_group: int, which: str
     return round_to_storage(vt[:rank].T, w.dtype)
 
 
+def _raw_rows(w: Workload, layer: int, head: int, b: int, which: str) -> np.ndarray:
+    z = _rng(w, "tok_" + which, layer, head, b).standard_normal((w.n_total, HEAD_DIM))
+    return (z * spectrum(_tau(w, which))[None, :]) @ rotation(w, layer, head, which).T
+
+
 def unit_kv(w: Workload, layer: int, head: int, b: int, which: str) -> np.ndarray:
     """All ``n_total`` rows of keys (``which='k'``) or values for one
-    (layer, KV head, batch row), rounded to storage: shape (n_total, 128)."""
-    z = _rng(w, "tok_" + which, layer, head, b).standard_normal((w.n_total, HEAD_DIM))
-    x = (z * spectrum(_tau(w, which))[None, :]) @ rotation(w, layer, head, which).T
+    (layer, KV head, batch row), rounded to storage: shape (n_total, 128).
+    With ``v_from_k`` = a > 0 the values are partly a fixed orthogonal map of the
+    keys (the structure LowRAM's value amortisation relies on)."""
+    x = _raw_rows(w, layer, head, b, which)
+    if which == "v" and w.v_from_k > 0:
+        a = float(w.v_from_k)
+        q = haar_orthogonal(_rng(w, "vmap", layer, head))
+        x = a * (_raw_rows(w, layer, head, b, "k") @ q) + np.sqrt(max(0.0, 1.0 - a * a)) * x
     return round_to_storage(x, w.dtype)
 
 

@@ -243,3 +243,43 @@ def test_head_group_validation():
         lib.lrkv_decode_auto_splits(ctypes.byref(layer()), 32768)
     assert lib.lrkv_oja_update(ctypes.byref(L), 0, FAKE, 1024, 512, 128, 10, 0.5, 0, 0, FAKE, 1 << 30,
                                None) == 2      # the Oja step is per KV head
+
+
+def test_lowram_validation():
+    def lowram(r=4, **kw):
+        L = layer(**kw)
+        L.value_mode, L.resid_per_block = 1, r
+        L.predictor, L.resid, L.resid_slot, L.resid_norm = FAKE, FAKE, FAKE, FAKE
+        return L
+    assert decode(lowram(), q=None) == 1                # a valid layer: fails on q only
+    assert decode(lowram(codes_v=None), q=None) == 1    # no value codes needed
+    assert decode(layer(codes_v=None)) == 1               # value codes needed otherwise
+    bad = layer()
+    bad.value_mode = 2
+    assert decode(bad) == 4
+    assert decode(lowram(r=0)) == 2
+    assert decode(lowram(r=9)) == 2                     # > LRKV_MAX_RESID
+    assert decode(lowram(dtype=2)) == 4                 # bf16 codes only
+    L = lowram()
+    L.head_group = 2
+    assert decode(L) == 4
+    L = lowram()
+    L.predictor = None
+    assert decode(L) == 1
+    L = lowram()
+    L.resid = FAKE + 8
+    assert decode(L) == 5
+    lib = B.lib()
+    L = lowram()
+    need = lib.lrkv_lowram_workspace_size(ctypes.byref(L))
+    assert need == 4 * 16 * 64 * (64 + 128) * 4      # 4 units x 16 partials x r x (r + 128) floats
+    assert lib.lrkv_lowram_workspace_size(ctypes.byref(layer())) == 0
+    fit = lambda L=L, **k: lib.lrkv_lowram_fit(ctypes.byref(L), k.get("v", FAKE), 1024, 512, 128, k.get("n", 10),
+                                               k.get("ws", FAKE), k.get("wsb", need), None)
+    assert fit(L=layer()) == 4
+    assert fit(n=0) == 2
+    assert fit(n=65) == 6                                # cap 64
+    assert fit(v=None) == 1
+    assert fit(v=FAKE + 2) == 5
+    assert fit(wsb=need - 1) == 7
+    assert lib.lrkv_compress(ctypes.byref(L), 1, FAKE, 1024, 512, 128, 10, 0, None) == 4
