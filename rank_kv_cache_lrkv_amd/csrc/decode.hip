@@ -178,14 +178,26 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, floa
       og = fmaf(w, ov[k], og);
     }
   }
-  for (int s = grp_c + PRE * groups; s < S; s += groups) {  // more splits than loaded up front
-    const float ms = rec(s, 0);
-    if (ms == kNegInf) continue;
-    const float mn = fmaxf(mg, ms);
-    const float a0 = fast_exp2(mg - mn), a1 = fast_exp2(ms - mn);  // mg = -inf gives a0 = 0
-    lg = fmaf(a1, rec(s, 1), lg * a0);
-    og = fmaf(a1, rec(s, 4 + col), og * a0);
-    mg = mn;
+  // more splits than loaded up front: 8 at a time, all loads issued before the merge
+  for (int s0 = grp_c + PRE * groups; s0 < S; s0 += 8 * groups) {
+    float2 mlx[8];
+    float ovx[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + u * groups, S - 1);
+      mlx[u] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rr, s * d.rec * 4, 0, 0));
+      ovx[u] = rec(s, 4 + col);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float ms = mlx[u].x;
+      if (s0 + u * groups >= S || ms == kNegInf) continue;
+      const float mn = fmaxf(mg, ms);
+      const float a0 = fast_exp2(mg - mn), a1 = fast_exp2(ms - mn);  // mg = -inf gives a0 = 0
+      lg = fmaf(a1, mlx[u].y, lg * a0);
+      og = fmaf(a1, ovx[u], og * a0);
+      mg = mn;
+    }
   }
   if (grp < groups) {
     cs.o[t] = og;
@@ -210,9 +222,17 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, floa
 #pragma unroll
   for (int k = 0; k < PRE; ++k)
     if (s_a0 + k < s_a1 && ma[k] != kNegInf) oa = fmaf(fast_exp2(ma[k] - M), av[k], oa);
-  for (int s = s_a0 + PRE; s < s_a1; ++s) {
-    const float ms = rec(s, 0);
-    if (ms != kNegInf) oa = fmaf(fast_exp2(ms - M), rec(s, d.oa + t), oa);
+  for (int s0 = s_a0 + PRE; s0 < s_a1; s0 += 8) {  // 8 at a time, loads first
+    float mx[8], ax[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + u, s_a1 - 1);
+      mx[u] = rec(s, 0);
+      ax[u] = rec(s, d.oa + t);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < s_a1 && mx[u] != kNegInf) oa = fmaf(fast_exp2(mx[u] - M), ax[u], oa);
   }
   __syncthreads();
 

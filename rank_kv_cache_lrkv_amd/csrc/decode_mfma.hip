@@ -160,7 +160,9 @@ __device__ __forceinline__ u32x4 i4x8_to_bf16_x16(uint32_t w) {
 // M.  The block's kept residual rows (R entries: slot, 128 bf16) are loaded with
 // the block and added as p[t][h] e_t into 128-dim sums per head (each lane two
 // features), which leave the split with the anchor sums.
-template <int RKMAX, int RVMAX, bool EXACT, int CB, bool LR = false>
+// LR > 0 is the most query heads per KV head the instance handles (4 or 16), LRR
+// the most residual entries per block (4 or 8): both size register arrays.
+template <int RKMAX, int RVMAX, bool EXACT, int CB, int LR = 0, int LRR = 0>
 __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d) {
   constexpr int NKC = (RKMAX + 31) / 32;  // score MFMAs per 16-token tile (K = 32 each)
   constexpr int NVC = RVMAX / 16;         // value MFMAs per block (16 columns each)
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   const int soff = (16 * ((t16 >> 2) & 1) + 4 * q4 + (t16 & 3)) * 4;  // this lane's scale in a block
   // LowRAM: this (row, head)'s residual entries, R per block
   __amdgpu_buffer_rsrc_t eres = kres, esres = kres;
-  if constexpr (LR) {
+  if constexpr (LR > 0) {
     const int64_t e0 = resid_entry(L, h, b, 0, 0);
     eres = __builtin_amdgcn_make_buffer_rsrc(static_cast<bf16_t *>(L.resid) + e0 * kD, 0,
                                              (L.cap / kBlock) * L.R * kD * 2, kBufferWord3);
@@ -295,15 +297,15 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc)
           r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b128(kres, koff[h2][kc], ks, 0);
-      if constexpr (!LR) {
+      if constexpr (LR == 0) {
 #pragma unroll
         for (int ni = 0; ni < NVC; ++ni) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b128(vres, voff[ni], vs, 0);
       }
     }
-    if constexpr (LR) {
+    if constexpr (LR > 0) {
       const int es = __builtin_amdgcn_readfirstlane(blk * L.R * kD * 2);
 #pragma unroll
-      for (int i = 0; i < LRKV_MAX_RESID; ++i)
+      for (int i = 0; i < LRR; ++i)
         if (i < L.R) r.e[i] = __builtin_amdgcn_raw_buffer_load_b32(eres, lane * 4 + i * kD * 2, es, 0);
       r.es = __builtin_amdgcn_raw_buffer_load_b32(esres, min(lane, L.R - 1) * 4,
                                                   __builtin_amdgcn_readfirstlane(blk * L.R * 4), 0);
@@ -493,22 +495,21 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   for (int ni = 0; ni < NVC; ++ni) o[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
   // LowRAM: residual sums (lane: features 2 lane, 2 lane + 1 of every head), and the
   // selectors B[k][n] = (k == 16 half + n) that pick 16 of a fragment's 32 columns
-  float res[LRKV_MAX_GROUP][2];
-  u32x4 sel[2];
-  if constexpr (LR) {
+  float res[LR > 0 ? LR : 1][2];
+  if constexpr (LR > 0) {
 #pragma unroll
-    for (int hh = 0; hh < LRKV_MAX_GROUP; ++hh) res[hh][0] = res[hh][1] = 0.f;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int idx = 16 * half + t16 - 8 * q4;  // the element of this lane's 8 that is 1, if any
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sel[half][i] = (idx == 2 * i ? 0x3f80u : 0u) | (idx == 2 * i + 1 ? 0x3f800000u : 0u);
-    }
+    for (int hh = 0; hh < LR; ++hh) res[hh][0] = res[hh][1] = 0.f;
   }
+  auto selector = [&](int half) {
+    const int idx = 16 * half + t16 - 8 * q4;  // the element of this lane's 8 that is 1, if any
+    u32x4 sv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = (idx == 2 * i ? 0x3f80u : 0u) | (idx == 2 * i + 1 ? 0x3f800000u : 0u);
+    return sv;
+  };
 
   auto process = [&](int blk, BlockRegs<NKC, NVC, CB> &r) {
-    if constexpr (LR) {  // slots past c may hold any bits: their codes become 0 (the
+    if constexpr (LR > 0) {  // slots past c may hold any bits: their codes become 0 (the
                          // transposes below mix a token's columns; scores are masked anyway)
       if (blk * kBlock + kBlock > c) {
 #pragma unroll
@@ -594,9 +595,9 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
 #pragma unroll
         for (int ni = 0; ni < NVC; ++ni) o[ni][v] *= a;
       }
-      if constexpr (LR) {  // head hh's factor sits in lane hh
+      if constexpr (LR > 0) {  // head hh's factor sits in lane hh
 #pragma unroll
-        for (int hh = 0; hh < LRKV_MAX_GROUP; ++hh) {
+        for (int hh = 0; hh < LR; ++hh) {
           if (hh < G) {
             const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), hh));
             res[hh][0] *= a;
@@ -605,12 +606,12 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
         }
       }
     }
-    if constexpr (LR) {
+    if constexpr (LR > 0) {
       // kept residual rows: entry i holds slot t of this block (wave-uniform); head
       // hh's weight of token t sits in lane 16 ((t % 16) / 4) + hh, register
       // 4 (t / 16) + t % 4
 #pragma unroll
-      for (int i = 0; i < LRKV_MAX_RESID; ++i) {
+      for (int i = 0; i < LRR; ++i) {
         if (i < L.R) {
           const int t = __builtin_amdgcn_readlane(int(r.es), i);
           if (t >= 0 && blk * kBlock + t < c) {
@@ -620,7 +621,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
             for (int jj = 1; jj < 8; ++jj) pv = jsel == jj ? p[jj] : pv;
             const float e0 = __uint_as_float(r.e[i] << 16), e1 = __uint_as_float(r.e[i] & 0xffff0000u);
 #pragma unroll
-            for (int hh = 0; hh < LRKV_MAX_GROUP; ++hh) {
+            for (int hh = 0; hh < LR; ++hh) {
               if (hh < G) {
                 const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), lsel + hh));
                 res[hh][0] = fmaf(w, e0, res[hh][0]);
@@ -655,13 +656,14 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
         u32x4 bv;
         if constexpr (CB == 8) bv = i8x8_to_bf16(r.v[ni]);
         else if constexpr (CB == 4) bv = i4x8_to_bf16_x16(r.v[ni]);
-        else if constexpr (LR) {
+        else if constexpr (LR > 0) {
           // the key codes of columns 16 ni .. 16 ni + 15 as the value operand:
           // D[token][n] = C[token][32 kc + 16 half + n], lane (q4, t16) gets tokens
           // 16 h2 + 4 q4 + v of column 16 ni + t16, exact in float32
           const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-          const f32x4 d0 = mfma16x16x32(r.k[0][ni >> 1], sel[ni & 1], z);
-          const f32x4 d1 = mfma16x16x32(r.k[1][ni >> 1], sel[ni & 1], z);
+          const u32x4 sl = selector(ni & 1);
+          const f32x4 d0 = mfma16x16x32(r.k[0][ni >> 1], sl, z);
+          const f32x4 d1 = mfma16x16x32(r.k[1][ni >> 1], sl, z);
           bv = u32x4{pack_hi(d0[0], d0[1]), pack_hi(d0[2], d0[3]), pack_hi(d1[0], d1[1]), pack_hi(d1[2], d1[3])};
         } else bv = r.v[ni];
         o[ni] = mfma16x16x32(a_hi, bv, o[ni]);
@@ -730,14 +732,14 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   }
   // o_A of the heads whose KV head has anchor rows in this split; the combine
   // reads it from exactly these splits and skips the others
-  if constexpr (LR) {
+  if constexpr (LR > 0) {
     // every split: the waves' residual sums and the anchor sums under the head's
     // common max, added into sm.u.oa wave by wave (wave 0 first, over its anchors)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       if (wave == w) {
 #pragma unroll
-        for (int hh = 0; hh < LRKV_MAX_GROUP; ++hh) {
+        for (int hh = 0; hh < LR; ++hh) {
           if (hh < G) {
             const float M = head_max(hh);
             const float f = weight(w, hh, M);
@@ -825,11 +827,14 @@ static int cu_count() {
 // LowRAM layers: value sums over the key codes (RVMAX = RKMAX), bf16 codes
 template <int RKMAX>
 static hipError_t launch_lr(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
-  bool exact = true;
-  for (int h = 0; h < L.n_lat; ++h) exact = exact && L.heads[h].rk == RKMAX;
   dim3 grid(d.n_splits, L.batch * L.n_lat);
-  if (exact) hipLaunchKernelGGL((k_partials_mfma<RKMAX, RKMAX, true, 16, true>), grid, dim3(256), 0, s, L, d);
-  else hipLaunchKernelGGL((k_partials_mfma<RKMAX, RKMAX, false, 16, true>), grid, dim3(256), 0, s, L, d);
+  // ranks are read per head (no exact-rank instances); register arrays sized for
+  // at most 4 query heads per KV head and 4 residual entries where that suffices
+  const bool g4 = L.group <= 4, r4 = L.R <= 4;
+  if (g4 && r4) hipLaunchKernelGGL((k_partials_mfma<RKMAX, RKMAX, false, 16, 4, 4>), grid, dim3(256), 0, s, L, d);
+  else if (g4) hipLaunchKernelGGL((k_partials_mfma<RKMAX, RKMAX, false, 16, 4, 8>), grid, dim3(256), 0, s, L, d);
+  else if (r4) hipLaunchKernelGGL((k_partials_mfma<RKMAX, RKMAX, false, 16, 16, 4>), grid, dim3(256), 0, s, L, d);
+  else hipLaunchKernelGGL((k_partials_mfma<RKMAX, RKMAX, false, 16, 16, 8>), grid, dim3(256), 0, s, L, d);
   return hipGetLastError();
 }
 
