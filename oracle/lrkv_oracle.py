@@ -37,6 +37,9 @@ re-orthonormalisation (the page names Oja's algorithm but gives no rule); codes
 made under several basis versions are decoded each with its own version; see
 oja_update and oracle_decode_unit_versions.
 
+Keys compressed before RoPE (Palu) are reconstructed and rotated per token
+before scoring (standard rotate-half RoPE); see oracle_decode_unit_prerope.
+
 LowRAM's value amortisation (values predicted from the key codes by a linear
 map fitted on the prompt, residuals kept for each block's worst-predicted tokens)
 follows readings stated with lowram_fit; see oracle_decode_lowram.
@@ -429,6 +432,42 @@ def oracle_decode_lowram(q, u_k, m, c_k, kept, e, k_a, v_a, scale: float) -> np.
     k_a, v_a (a, 128).  Returns out (g, 128)."""
     vals = lowram_values(c_k, m, kept, e)
     return oracle_decode_unit(q, u_k, np.eye(HEAD_DIM), c_k, vals, k_a, v_a, scale)
+
+
+# ---------------------------------------------------------------------------
+# Keys compressed before RoPE (Palu abstract: the full keys and values are
+# reconstructed on the fly; a decomposition of the key projection keeps the
+# latents before the rotary position embedding, so the keys cannot be scored in
+# code space any more).  The rotation is the standard rotate-half RoPE (the pages
+# name RoPE but print no formula): feature pair (i, i + 64), i < 64, of a key or
+# query at position p turns by the angle p * base^(-2 i / 128).  Codes hold the
+# pre-RoPE keys' projections; anchors and the query are post-RoPE, as attention
+# uses them; values are never rotated.
+# ---------------------------------------------------------------------------
+
+def rope(x, positions, base: float) -> np.ndarray:
+    """Rotate-half RoPE of rows x (t, 128) at the given positions (t,)."""
+    x = np.asarray(x, np.float64)
+    half = HEAD_DIM // 2
+    theta = float(base) ** (-2.0 * np.arange(half) / HEAD_DIM)
+    ang = np.asarray(positions, np.float64)[:, None] * theta[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[:, :half], x[:, half:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=1)
+
+
+def oracle_decode_unit_prerope(q, u_k, u_v, c_k, c_v, code_pos, k_a, v_a, scale: float,
+                               base: float) -> np.ndarray:
+    """Decode attention over codes of pre-RoPE keys: each compressed key is
+    reconstructed (U_K c_t) and rotated to its position code_pos[t], then scored
+    with the post-RoPE query q (g, 128); anchors k_a are post-RoPE; values stay
+    in code space (one up-projection).  Returns out (g, 128)."""
+    c = np.asarray(c_k).shape[0]
+    keys = rope(np.asarray(c_k, np.float64) @ np.asarray(u_k, np.float64).T, code_pos, base)
+    q = np.asarray(q, np.float64)
+    s = np.concatenate([scale * (q @ keys.T), anchor_scores(q, k_a, scale)], axis=1)
+    e, total = softmax_weights(s)
+    return (up_project(rank_space_values(e[:, :c], c_v), u_v) + anchor_values(e[:, c:], v_a)) / total
 
 
 def full_kv_bytes(n_layers: int, n_kv_heads: int, n_tokens: int, batch: int,

@@ -661,4 +661,61 @@ def pin_lowram_decode_brute_force():
         assert np.max(np.abs(full[i] - want)) < 1e-12
 
 
+def pin_rope_is_the_complex_rotation():
+    """RoPE against its complex form, (x_i + i x_(i+64)) e^(i p theta_i) with
+    theta_i = base^(-i/64) written out per pair; identity at position 0; norms
+    kept; dot products depend only on the position difference; p then -p is the
+    identity."""
+    rng = np.random.default_rng(50)
+    base = 10000.0
+    x = rng.standard_normal((5, D))
+    pos = np.array([0, 1, 7, 1000, 32767])
+    got = oracle.rope(x, pos, base)
+    for r in range(5):
+        for i in range(D // 2):
+            z = complex(x[r, i], x[r, i + 64]) * complex(math.cos(pos[r] * base ** (-i / 64)),
+                                                          math.sin(pos[r] * base ** (-i / 64)))
+            assert abs(got[r, i] - z.real) < 1e-9 and abs(got[r, i + 64] - z.imag) < 1e-9, (r, i)
+    assert np.array_equal(oracle.rope(x[:1], [0], base), x[:1])
+    assert np.allclose(np.linalg.norm(got, axis=1), np.linalg.norm(x, axis=1), rtol=1e-12)
+    q, k = rng.standard_normal((1, D)), rng.standard_normal((1, D))
+    d1 = float((oracle.rope(q, [100], base) @ oracle.rope(k, [40], base).T)[0, 0])
+    d2 = float((oracle.rope(q, [5060], base) @ oracle.rope(k, [5000], base).T)[0, 0])
+    assert abs(d1 - d2) < 1e-9
+    assert np.allclose(oracle.rope(oracle.rope(x, pos, base), -pos, base), x, atol=1e-9)
+
+
+def pin_prerope_decode_brute_force():
+    """Brute force: every compressed key reconstructed token by token from its
+    code, rotated to its position as a complex number per pair, then softmax
+    attention with loops; at position 0 everywhere it is the code-space decode."""
+    rng = np.random.default_rng(51)
+    n, w, rk, rv, g, base = 40, 4, 16, 16, 2, 500000.0
+    cpos, apos = oracle.code_positions(n, w), oracle.anchor_positions(n, w)
+    k_pre = rng.standard_normal((n, D))
+    v = rng.standard_normal((n, D))
+    uk, uv = orthonormal(rng, rk), orthonormal(rng, rv)
+    ck, cv = k_pre[cpos] @ uk, v[cpos] @ uv
+    q = rng.standard_normal((g, D)) * 2
+    k_a = oracle.rope(k_pre[apos], apos, base)
+    sc = oracle.default_scale()
+    got = oracle.oracle_decode_unit_prerope(q, uk, uv, ck, cv, cpos, k_a, v[apos], sc, base)
+    keys = []
+    for t, p in enumerate(cpos):
+        kh = uk @ ck[t]
+        rot = np.empty(D)
+        for i in range(D // 2):
+            z = complex(kh[i], kh[i + 64]) * complex(math.cos(p * base ** (-i / 64)), math.sin(p * base ** (-i / 64)))
+            rot[i], rot[i + 64] = z.real, z.imag
+        keys.append(rot)
+    keys = np.concatenate([np.stack(keys), k_a])
+    vals = np.concatenate([reconstruct(cv, uv), v[apos]])
+    for i in range(g):
+        want, _ = brute_attention(q[i], keys, vals, sc)
+        assert np.max(np.abs(got[i] - want)) < 1e-12
+    zero = oracle.oracle_decode_unit_prerope(q, uk, uv, ck, cv, np.zeros(len(cpos)), k_pre[apos], v[apos], sc, base)
+    ref = oracle.oracle_decode_unit(q, uk, uv, ck, cv, k_pre[apos], v[apos], sc)
+    assert np.max(np.abs(zero - ref)) < 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -68,8 +68,31 @@ MUTANTS = {
     "lowram_select_smallest": ("lowram_select", lambda sq, r: _lowram_select_variant(sq, r, sign=-1)),
     "lowram_select_ties_high_slot": ("lowram_select", lambda sq, r: _lowram_select_variant(sq, r, tie=-1)),
     "lowram_select_whole_row": ("lowram_select", lambda sq, r: _lowram_select_variant(sq, r, block=10 ** 9)),
+    "rope_interleaved_pairs": ("rope", lambda x, pos, base: _rope_variant(x, pos, base, interleaved=True)),
+    "rope_sin_sign": ("rope", lambda x, pos, base: _rope_variant(x, pos, base, sign=-1)),
+    "rope_theta_exponent": ("rope", lambda x, pos, base: _rope_variant(x, pos, base, expo=1.0)),
+    "prerope_positions_off_by_one": ("oracle_decode_unit_prerope",
+                                     lambda q, uk, uv, ck, cv, pos, ka, va, sc, base:
+                                     _ORIG_PREROPE(q, uk, uv, ck, cv, np.asarray(pos) + 1, ka, va, sc, base)),
     "group_slice_off_by_one_head": ("group_slice", lambda u, j: np.asarray(u, float)[128 * max(j - 1, 0):128 * max(j, 1)]),
 }
+
+
+def _rope_variant(x, pos, base, interleaved=False, sign=1, expo=2.0):
+    x = np.asarray(x, float)
+    theta = float(base) ** (-expo * np.arange(64) / 128)
+    ang = np.asarray(pos, float)[:, None] * theta[None, :]
+    c, s = np.cos(ang), sign * np.sin(ang)
+    if interleaved:
+        a, b = x[:, 0::2], x[:, 1::2]
+        out = np.empty_like(x)
+        out[:, 0::2], out[:, 1::2] = a * c - b * s, a * s + b * c
+        return out
+    a, b = x[:, :64], x[:, 64:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=1)
+
+
+_ORIG_PREROPE = lo.oracle_decode_unit_prerope
 
 
 def _lowram_values_variant(c, m, kept, e, sign=1):
