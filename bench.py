@@ -78,7 +78,22 @@ def algorithmic_bytes(w, n, bits=16, hg=1, resid=0):
             "codes": codes, "anchors": anchors}
 
 
-def build_cache(w, B, dev, bits=16, hg=1, resid=0):
+def rotate_rows(x, positions, base):
+    """Rotate-half RoPE of rows x (..., t, 128) at positions (t,) on the GPU in
+    float64 (input preparation for caches whose key codes are pre-RoPE: the
+    anchors the caller stores are post-RoPE keys)."""
+    import torch
+    half = 64
+    theta = torch.tensor([float(base) ** (-2.0 * i / 128) for i in range(half)], dtype=torch.float64,
+                         device=x.device)
+    ang = positions.to(torch.float64)[:, None] * theta[None, :]
+    c, s = torch.cos(ang), torch.sin(ang)
+    xf = x.to(torch.float64)
+    a, b = xf[..., :half], xf[..., half:]
+    return torch.cat([a * c - b * s, a * s + b * c], dim=-1).to(x.dtype)
+
+
+def build_cache(w, B, dev, bits=16, hg=1, resid=0, rope_base=0.0):
     """Prefill on the GPU: compress tokens 1..n-W-1, store token 0 and the window."""
     import numpy as np
     import torch
@@ -101,7 +116,7 @@ def build_cache(w, B, dev, bits=16, hg=1, resid=0):
     L = B.Layer.allocate(dtype=dtype, batch=w.batch,
                          n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, window=w.window,
                          cap=layout.round_cap(c), rank_k=rk, rank_v=rv, bases=dev(bases), head_group=hg,
-                         lowram_resid=resid)
+                         lowram_resid=resid, rope_base=rope_base)
     td = L.torch_dtype
     K = torch.empty((w.batch, w.n_kv_heads, n, 128), dtype=td, device="cuda")
     V = torch.empty_like(K)
@@ -120,9 +135,13 @@ def build_cache(w, B, dev, bits=16, hg=1, resid=0):
         else:
             B.lrkv_compress(L, 1, V[:, :, 1:], c, 0)
         ev[1].record()
-    B.lrkv_store_anchors(L, K[:, :, 0:1], V[:, :, 0:1], 0, 1)
+    KA = K
+    if rope_base:  # the codes took the pre-RoPE keys; anchors hold the keys rotated to their positions
+        KA = rotate_rows(K, torch.arange(n, device="cuda"), rope_base)
+    B.lrkv_store_anchors(L, KA[:, :, 0:1], V[:, :, 0:1], 0, 1)
     lo = max(1, n - w.window)
-    B.lrkv_store_anchors(L, K[:, :, lo:n], V[:, :, lo:n], lo, n - lo)
+    B.lrkv_store_anchors(L, KA[:, :, lo:n], V[:, :, lo:n], lo, n - lo)
+    del KA
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[1])
     s = 2 if w.dtype == "bf16" else 4
@@ -133,7 +152,7 @@ def build_cache(w, B, dev, bits=16, hg=1, resid=0):
     compress = {"ms": round(ms, 4), "tokens": c, "alg_bytes": moved,
                 "gbps": round(moved / (ms * 1e-3) / 1e9, 1)}
     oja = None
-    if bits == 16 and w.dtype == "bf16" and hg == 1 and not resid:
+    if bits == 16 and w.dtype == "bf16" and hg == 1 and not resid and not rope_base:
         # one Oja step of the key bases over the whole prompt (OjaKV's prefill
         # adaptation), version 0 -> 1 of a two-version copy of the bases
         Lo = B.Layer.allocate(dtype=B.LRKV_BF16, batch=w.batch, n_q_heads=w.n_q_heads,
@@ -161,7 +180,8 @@ def replicate(L, B):
                    L.bases.clone(), L.codes_k.clone(), sc(L.codes_v), L.anchor_k.clone(),
                    L.anchor_v.clone(), sc(L.scales_k), sc(L.scales_v), head_group=L.head_group,
                    value_mode=L.value_mode, resid_per_block=L.resid_per_block, predictor=sc(L.predictor),
-                   resid=sc(L.resid), resid_slot=sc(L.resid_slot), resid_norm=sc(L.resid_norm))
+                   resid=sc(L.resid), resid_slot=sc(L.resid_slot), resid_norm=sc(L.resid_norm),
+                   rope_base=L.rope_base)
 
 
 def cpu_baseline(w, seconds):
@@ -242,6 +262,9 @@ def main():
     ap.add_argument("--lowram", type=int, default=0, metavar="R",
                     help="LowRAM values: predicted from the key codes, R residual rows per 32-slot block "
                          "(bf16 workloads; values partly predictable from keys)")
+    ap.add_argument("--rope-base", type=float, default=0.0,
+                    help="> 1: key codes of pre-RoPE keys, reconstructed and rotated in the decode "
+                         "(rotate-half RoPE with this base; bf16 codes)")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated (0: >= 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -289,7 +312,10 @@ def main():
     assert not resid or (bits == 16 and hg == 1 and w.dtype == "bf16"), "LowRAM values: bf16 codes, no head groups"
     if resid:
         w = w.scaled(v_from_k=0.8)
-    L0, compress, oja = build_cache(w, B, dev, bits, hg, resid)
+    rope_base = args.rope_base
+    assert not rope_base or (bits == 16 and hg == 1 and not resid and w.dtype == "bf16"), \
+        "pre-RoPE key codes: bf16 codes, no head groups, value codes"
+    L0, compress, oja = build_cache(w, B, dev, bits, hg, resid, rope_base)
     log(f"cache built and compressed on the GPU in {time.time() - t0:.1f} s "
         f"(compress {compress['ms']:.3f} ms, {compress['gbps']} GB/s)")
     if oja:
@@ -347,10 +373,12 @@ def main():
         kernel += f", {hg} KV heads per code stream"
     if resid:
         kernel = f"k_partials_mfma, LowRAM values (key codes + {resid} residual rows per block)"
+    if rope_base:
+        kernel = "k_partials_mfma, pre-RoPE key codes (keys reconstructed and rotated per block)"
     k_bytes = nb["partials"]
     achieved = k_bytes / (k_ms * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    traffic = None if resid else traffic_from_profile(src_hash, args.codes, hg)
+    traffic = None if (resid or rope_base) else traffic_from_profile(src_hash, args.codes, hg)
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
@@ -373,7 +401,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": 128, "n_ctx": n, "rank_k": w.rank_k,
                    "rank_v": w.rank_v, "window": w.window, "n_splits": S, "cache_replicas": R,
-                   "codes": args.codes, "head_group": hg, "lowram_resid": resid},
+                   "codes": args.codes, "head_group": hg, "lowram_resid": resid, "rope_base": rope_base},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": k_bytes,

@@ -149,6 +149,18 @@ typedef enum lrkv_value_mode {
  * Requires dtype LRKV_BF16, one basis version and head_group <= 1
  * (LRKV_ERR_DTYPE otherwise) and 1 <= R <= LRKV_MAX_RESID (LRKV_ERR_SHAPE).
  *
+ * Keys compressed before RoPE (rope_base > 1; Palu abstract: the full keys are
+ * reconstructed on the fly).  The key codes hold projections of the keys before
+ * the rotary position embedding, so they cannot be scored in code space: the
+ * decode reconstructs every compressed key (U_K c), rotates it to its position
+ * (code slot j holds token j + 1) with rotate-half RoPE -- feature pair
+ * (i, i + 64), i < 64, turned by position * rope_base^(-2 i / 128) -- and scores
+ * it against q.  q, the anchors and the keys given to lrkv_store_anchors and
+ * lrkv_append are post-RoPE (as attention uses them); lrkv_compress takes
+ * pre-RoPE keys; values are never rotated.  Requires dtype LRKV_BF16, one basis
+ * version, head_group <= 1 and value codes (LRKV_ERR_DTYPE otherwise); rope_base
+ * must be finite and > 1 (LRKV_ERR_SHAPE).
+ *
  * 4-bit codes (dtype LRKV_BF16_Q4): the same rule with 7 in place of 127
  * (s = max_c |x_c| / 7, q in [-7, 7]), the same scales.  Element position p of
  * the blocked layout above sits in byte p / 2 of the region, in the low four
@@ -188,6 +200,8 @@ typedef struct lrkv_layer {
   void *resid;            /* LowRAM, device */
   int32_t *resid_slot;    /* LowRAM, device */
   float *resid_norm;      /* LowRAM, device */
+  float rope_base;        /* 0: keys compressed after RoPE (scored in code space);
+                             > 1: keys compressed before RoPE, see below */
 } lrkv_layer;
 
 /*
@@ -296,7 +310,9 @@ lrkv_status lrkv_store_anchors(const lrkv_layer *L, const void *k, const void *v
  *  - window == 0 and pos >= 1: the new token is compressed into code slot pos - 1.
  *  - otherwise the new token is stored into its anchor slot.
  * With basis versions the code is made with the version the code slot belongs
- * to (version_start of the row).  LowRAM layers: the key is compressed as usual
+ * to (version_start of the row).  Keys compressed before RoPE: the leaving key
+ * (post-RoPE, from its anchor slot, or k_new when window = 0) is turned back to
+ * its pre-RoPE form at its position before projection.  LowRAM layers: the key is compressed as usual
  * and the value's residual e = V - C_K M (float32, C_K the stored code) enters the
  * slot's block: a slot opening a block (slot % 32 == 0) first empties the block's
  * entries; the residual takes an empty entry if there is one, else replaces the

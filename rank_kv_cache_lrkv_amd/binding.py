@@ -53,6 +53,7 @@ class lrkv_layer(ctypes.Structure):
         ("head_group", c_int32),
         ("value_mode", c_int32), ("resid_per_block", c_int32),
         ("predictor", c_void_p), ("resid", c_void_p), ("resid_slot", c_void_p), ("resid_norm", c_void_p),
+        ("rope_base", c_float),
     ]
 
 
@@ -158,6 +159,7 @@ class Layer:
     resid: "object" = None      # LowRAM: bf16 [n_kv][batch][cap / 32][R][128]
     resid_slot: "object" = None  # LowRAM: int32 [n_kv][batch][cap / 32][R]
     resid_norm: "object" = None  # LowRAM: float32, same shape
+    rope_base: float = 0.0  # > 1: key codes are of pre-RoPE keys (rotate-half RoPE with this base)
     _rk: object = field(default=None, repr=False)
     _rv: object = field(default=None, repr=False)
     struct: lrkv_layer = field(default=None, repr=False)
@@ -172,7 +174,7 @@ class Layer:
             _ptr(self.anchor_k), _ptr(self.anchor_v), _ptr(self.scales_k), _ptr(self.scales_v),
             int(self.n_versions), _ptr(self.version_start), int(self.head_group),
             int(self.value_mode), int(self.resid_per_block), _ptr(self.predictor), _ptr(self.resid),
-            _ptr(self.resid_slot), _ptr(self.resid_norm))
+            _ptr(self.resid_slot), _ptr(self.resid_norm), float(self.rope_base))
 
     @property
     def group(self) -> int:
@@ -200,7 +202,8 @@ class Layer:
     @classmethod
     def allocate(cls, *, dtype: int, batch: int, n_q_heads: int, n_kv_heads: int, window: int,
                  cap: int, rank_k: Sequence[int], rank_v: Sequence[int], device="cuda",
-                 bases=None, n_versions: int = 1, head_group: int = 1, lowram_resid: int = 0) -> "Layer":
+                 bases=None, n_versions: int = 1, head_group: int = 1, lowram_resid: int = 0,
+                 rope_base: float = 0.0) -> "Layer":
         """Allocate zeroed codes and anchors (and int8 scales) (torch) for the given
         geometry.  ``bases`` (optional) is the flat bases tensor; otherwise zeros.
         With ``head_group`` > 1, rank_k / rank_v hold one rank per group of
@@ -240,7 +243,7 @@ class Layer:
             return cls(dtype, batch, n_q_heads, n_kv_heads, window, cap, rk, rv, bases, ck, cv, ak, av, sk, sv,
                        n_versions, vs, hg, LRKV_VALUES_LOWRAM, lowram_resid, pred, res, rsl, rno)
         return cls(dtype, batch, n_q_heads, n_kv_heads, window, cap, rk, rv, bases, ck, cv, ak, av, sk, sv,
-                   n_versions, vs, hg)
+                   n_versions, vs, hg, rope_base=float(rope_base))
 
 
 # ---------------------------------------------------------------------------

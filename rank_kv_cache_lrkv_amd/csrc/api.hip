@@ -1,6 +1,7 @@
 // C entry points: argument checks on the host (before any HIP call), layout
 // offsets, then the launches.  No device memory is allocated here.
 
+#include <cmath>
 #include <cstring>
 
 #include "lrkv_internal.h"
@@ -48,6 +49,10 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   if (quantised(L->dtype)) {
     if (!L->scales_k || !L->scales_v) return LRKV_ERR_NULL;
     if (!aligned16(L->scales_k) || !aligned16(L->scales_v)) return LRKV_ERR_ALIGN;
+  }
+  if (L->rope_base != 0.f) {
+    if (!(L->rope_base > 1.f) || !(L->rope_base < 3.0e38f)) return LRKV_ERR_SHAPE;
+    if (L->dtype != LRKV_BF16 || nver > 1 || hg > 1 || lr) return LRKV_ERR_DTYPE;
   }
   if (lr) {
     if (L->dtype != LRKV_BF16 || nver > 1 || hg > 1) return LRKV_ERR_DTYPE;
@@ -97,6 +102,14 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
   A->n_versions = nver;
   A->vstart = nver > 1 ? L->version_start : nullptr;
   A->version_elems = ub;
+  if (L->rope_base != 0.f) {
+    A->rope = 1;
+    for (int i = 0; i < kD / 2; ++i) {
+      const double a = std::pow(double(L->rope_base), -2.0 * i / kD) / (2.0 * 3.14159265358979323846);
+      A->rope_a[i][0] = float(a);
+      A->rope_a[i][1] = float(a - double(float(a)));
+    }
+  }
   if (lr) {
     A->lowram = 1;
     A->R = L->resid_per_block;

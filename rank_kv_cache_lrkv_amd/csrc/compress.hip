@@ -180,6 +180,18 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
     slot = anchor_slot(pos, W);
   }
   __syncthreads();
+  if (L.rope && code_slot >= 0) {  // keys compressed before RoPE: the leaving (post-RoPE)
+                                   // key turned back by its position's angle
+    if (tid < kD / 2) {
+      const float p = float(W >= 1 ? pos - W : pos);
+      const float rev = rope_rev(L.rope_a[tid][0], L.rope_a[tid][1], p);
+      const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+      const float x = rk_row[0][tid], y = rk_row[0][tid + kD / 2];
+      rk_row[0][tid] = fmaf(x, cs, y * sn);
+      rk_row[0][tid + kD / 2] = fmaf(y, cs, -(x * sn));
+    }
+    __syncthreads();
+  }
   if (code_slot >= 0) {  // uniform over the workgroup
     // basis version of the slot: the last one starting at or before it
     int ver = 0;

@@ -162,13 +162,28 @@ __device__ __forceinline__ u32x4 i4x8_to_bf16_x16(uint32_t w) {
 // features), which leave the split with the anchor sums.
 // LR > 0 is the most query heads per KV head the instance handles (4 or 16), LRR
 // the most residual entries per block (4 or 8): both size register arrays.
-template <int RKMAX, int RVMAX, bool EXACT, int CB, int LR = 0, int LRR = 0>
+//
+// RP: keys compressed before RoPE (Palu's on-the-fly reconstruction; bf16 codes).
+// Codes cannot be scored in code space: per block the wave reconstructs its 32
+// keys on the matrix cores, D[f][t] = sum_c U_K[f][c] C[t][c] (A = U_K staged in
+// LDS feature by feature, B = the key fragments as loaded), which leaves lane
+// (q4, t16) features 16 ft + 4 q4 + v of token 16 h2 + t16 -- so the pair
+// (f, f + 64) of a rotation sits in the same lane (tiles ft and ft + 4).  Each
+// pair is turned by its position's angle (hardware sin/cos of the angle in
+// revolutions, reduced exactly), and the rotated keys, split into bf16 hi + lo,
+// are scored against q whose features are permuted to the order the lanes hold
+// (k = 8 q4 + i <-> feature 32 kc + 16 (i / 4) + 4 q4 + i % 4).
+template <int RKMAX, int RVMAX, bool EXACT, int CB, int LR = 0, int LRR = 0, bool RP = false>
 __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d) {
   constexpr int NKC = (RKMAX + 31) / 32;  // score MFMAs per 16-token tile (K = 32 each)
   constexpr int NVC = RVMAX / 16;         // value MFMAs per block (16 columns each)
   constexpr bool QC = CB < 16;            // quantised codes with per-token scales
   constexpr float kX16 = CB == 4 ? 0.0625f : 1.f;  // undoes the x16 of 4-bit operands
+  constexpr int RS = RKMAX + 8;           // RP: LDS row of U_K (one feature, RKMAX + 8 bf16)
   __shared__ MfmaSmem<RKMAX, RVMAX> sm;
+  __shared__ bf16_t su[RP ? kD * RS : 1];       // RP: U_K, feature-major
+  __shared__ u32x4 rq[RP ? 4 : 1][2][64];        // RP: score B operands (q, permuted, hi / lo)
+  __shared__ float sra[RP ? kD / 2 : 1][2];      // RP: angle per position of each pair (revolutions)
 
   const int S = d.n_splits;
   // Workgroup i of the launch runs on XCD i % 8, and each XCD has its own L2:
@@ -334,7 +349,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
         bu[i][kc] = *reinterpret_cast<const u32x4 *>(ut + (16 * nt + t16) * urow + j * kD + 32 * kc + 8 * q4);
     }
   };
-  load_bu(0);
+  if constexpr (!RP) load_bu(0);
   const int r16 = tid >> 4, piece = tid & 15;  // 16 rows x 16 pieces of 16 bytes
   u32x4 qq = *reinterpret_cast<const u32x4 *>(qb + min(r16, G - 1) * kD + piece * 8);
   const int64_t arow = na > 0 ? anchor_row(alo + min(r16, na - 1)) : anchor_row(0);
@@ -357,6 +372,40 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   *reinterpret_cast<u32x4 *>(&sm.ak[r16][piece * 4]) = kk;
   *reinterpret_cast<u32x4 *>(&sm.av[r16][piece * 4]) = vv;
   lds_barrier();
+  if constexpr (RP) {
+    // U_K feature-major (columns past rk zero), the pair angles, and q's score
+    // operands in the permuted feature order, hi and lo parts (zero past G)
+    for (int e = tid; e < kD * RS; e += blockDim.x) {
+      const int f = e % kD, c = e / kD;
+      su[f * RS + c] = c < rk ? ut[c * kD + f] : bf16_t(0);
+    }
+    if (tid < kD / 2) {
+      sra[tid][0] = L.rope_a[tid][0];
+      sra[tid][1] = L.rope_a[tid][1];
+    }
+    if (wave == 0) {
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int f = 32 * kc + 16 * (i >> 2) + 4 * q4 + (i & 3);
+          const uint32_t wd = sm.sq[t16][f >> 1];
+          const float qv = __uint_as_float((f & 1) ? (wd & 0xffff0000u) : (wd << 16));
+          x[i] = t16 < G ? qv * d.scale_log2 : 0.f;
+        }
+        u32x4 hi, lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hi[i] = pack_hi(x[2 * i], x[2 * i + 1]);
+          lo[i] = pack_rne(x[2 * i] - bf16_trunc(x[2 * i]), x[2 * i + 1] - bf16_trunc(x[2 * i + 1]));
+        }
+        rq[kc][0][lane] = hi;
+        rq[kc][1][lane] = lo;
+      }
+    }
+    lds_barrier();
+  } else {
   // A = q from LDS: lane (q4, t16) holds head t16, features 32 kc + 8 q4 .. (zero past G)
   u32x4 aq[4];
 #pragma unroll
@@ -409,6 +458,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
     }
   }
   lds_barrier();
+  }
 
   // ---- the split's anchor rows (wave 0, before its code blocks, while the other
   // waves already stream): scores on the matrix cores against q; the 128-dim
@@ -522,6 +572,70 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
     f32x4 s[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) s[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (RP) {
+      // feature tiles {2 hf, 2 hf + 1} and their rotation partners {2 hf + 4, 2 hf + 5}
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        f32x4 kr[4][2];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int ft = 2 * hf + (tt & 1) + 4 * (tt >> 1);
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) kr[tt][h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < NKC; ++kc) {
+            if (4 * kc < nkg) {
+              const u32x4 a = *reinterpret_cast<const u32x4 *>(&su[(16 * ft + t16) * RS + 32 * kc + 8 * q4]);
+#pragma unroll
+              for (int h2 = 0; h2 < 2; ++h2) kr[tt][h2] = mfma16x16x32(a, r.k[h2][kc], kr[tt][h2]);
+            }
+          }
+        }
+        // rotate pair (f, f + 64), f = 16 ft + 4 q4 + v, at the token's position
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int ft = 2 * hf + tt;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int f = 16 * ft + 4 * q4 + v;
+            const float ahi = sra[f][0], alo = sra[f][1];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const float pos = float(blk * kBlock + 16 * h2 + t16 + 1);  // code slot j holds token j + 1
+              const float rev = rope_rev(ahi, alo, pos);
+              const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+              const float x = kr[tt][h2][v], y = kr[tt + 2][h2][v];
+              kr[tt][h2][v] = x * cs - y * sn;
+              kr[tt + 2][h2][v] = fmaf(x, sn, y * cs);
+            }
+          }
+        }
+        // score chunks hf (tiles 2 hf, 2 hf + 1) and hf + 2 (tiles 2 hf + 4, 2 hf + 5)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const int kcq = hf + 2 * cc;
+          const u32x4 bh = rq[kcq][0][lane], bl = rq[kcq][1][lane];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              x[i] = kr[2 * cc][h2][i];
+              x[4 + i] = kr[2 * cc + 1][h2][i];
+            }
+            u32x4 ah, al;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              ah[i] = pack_hi(x[2 * i], x[2 * i + 1]);
+              al[i] = pack_rne(x[2 * i] - bf16_trunc(x[2 * i]), x[2 * i + 1] - bf16_trunc(x[2 * i + 1]));
+            }
+            s[h2] = mfma16x16x32(ah, bh, s[h2]);
+            s[h2] = mfma16x16x32(ah, bl, s[h2]);
+            s[h2] = mfma16x16x32(al, bh, s[h2]);
+          }
+        }
+      }
+    } else {
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       if (4 * kc < nkg) {
@@ -537,6 +651,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
           s[h2] = mfma16x16x32(a, bl, s[h2]);
         }
       }
+    }
     }
     if constexpr (QC) {
       float ksc[8];
@@ -838,12 +953,29 @@ static hipError_t launch_lr(const LayerArgs &L, const DecodeArgs &d, hipStream_t
   return hipGetLastError();
 }
 
+// keys compressed before RoPE (bf16 codes, per-head ranks read at run time)
+template <int RKMAX>
+static hipError_t launch_rp(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
+  dim3 grid(d.n_splits, L.batch * L.n_lat);
+  if (L.rv_max <= 16) hipLaunchKernelGGL((k_partials_mfma<RKMAX, 16, false, 16, 0, 0, true>), grid, dim3(256), 0, s, L, d);
+  else if (L.rv_max <= 32) hipLaunchKernelGGL((k_partials_mfma<RKMAX, 32, false, 16, 0, 0, true>), grid, dim3(256), 0, s, L, d);
+  else if (L.rv_max <= 64) hipLaunchKernelGGL((k_partials_mfma<RKMAX, 64, false, 16, 0, 0, true>), grid, dim3(256), 0, s, L, d);
+  else hipLaunchKernelGGL((k_partials_mfma<RKMAX, 128, false, 16, 0, 0, true>), grid, dim3(256), 0, s, L, d);
+  return hipGetLastError();
+}
+
 hipError_t launch_partials_mfma(const LayerArgs &L, const DecodeArgs &d0, hipStream_t s) {
   DecodeArgs d = d0;
   // balancing pays when the whole grid is resident at once (four workgroups per CU)
   d.balance = int64_t(d.n_splits) * L.batch * L.n_lat <= 4 * int64_t(cu_count());
   int rk_max = 0;
   for (int h = 0; h < L.n_lat; ++h) rk_max = L.heads[h].rk > rk_max ? L.heads[h].rk : rk_max;
+  if (L.rope) {
+    if (rk_max <= 32) return launch_rp<32>(L, d, s);
+    if (rk_max <= 64) return launch_rp<64>(L, d, s);
+    if (rk_max <= 96) return launch_rp<96>(L, d, s);
+    return launch_rp<128>(L, d, s);
+  }
   if (L.lowram) {
     if (rk_max <= 32) return launch_lr<32>(L, d, s);
     if (rk_max <= 64) return launch_lr<64>(L, d, s);

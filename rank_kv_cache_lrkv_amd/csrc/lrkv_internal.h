@@ -39,8 +39,21 @@ struct LayerArgs {
   void *resid;                 // bf16 residual rows, [h][b][cap / 32][R][128]
   int32_t *rslot;              // in-block slot of each entry, -1 empty
   float *rnorm;                // squared norm of each entry
+  // keys compressed before RoPE: rope_a[i] = theta_i / (2 pi) as a float32 pair
+  // (hi, lo), theta_i = base^(-2 i / 128), so angles in revolutions come out
+  // exact to float32 at any position
+  int32_t rope;
+  float rope_a[kD / 2][2];
   HeadInfo heads[LRKV_MAX_KV_HEADS];
 };
+
+// the RoPE angle of pair i at position pos, in revolutions reduced to about
+// [-0.5, 0.5]: pos * (hi + lo) with the product's rounding error recovered by an FMA
+__device__ __forceinline__ float rope_rev(float hi, float lo, float pos) {
+  const float p = pos * hi;
+  const float e = fmaf(pos, hi, -p);
+  return (p - __builtin_rintf(p)) + fmaf(pos, lo, e);
+}
 
 // LowRAM: index of entry i of block j of (head h, row b)
 __host__ __device__ __forceinline__ int64_t resid_entry(const LayerArgs &L, int h, int b, int j, int i) {

@@ -283,3 +283,26 @@ def test_lowram_validation():
     assert fit(v=FAKE + 2) == 5
     assert fit(wsb=need - 1) == 7
     assert lib.lrkv_compress(ctypes.byref(L), 1, FAKE, 1024, 512, 128, 10, 0, None) == 4
+
+
+def test_rope_validation():
+    def roped(base, **kw):
+        L = layer(**kw)
+        L.rope_base = base
+        return L
+    assert decode(roped(10000.0), q=None) == 1          # a valid layer: fails on q only
+    assert decode(roped(0.5)) == 2
+    assert decode(roped(float("inf"))) == 2
+    assert decode(roped(float("nan"))) == 2
+    assert decode(roped(10000.0, dtype=2)) == 4          # bf16 codes only
+    L = roped(10000.0)
+    L.head_group = 2
+    L.rank_k = L.rank_k                                  # (one rank per KV head stays valid)
+    assert decode(L) in (2, 4)
+    L = roped(10000.0)
+    L.n_versions, L.version_start = 2, FAKE
+    assert decode(L) == 4
+    L = roped(10000.0)
+    L.value_mode, L.resid_per_block = 1, 4
+    L.predictor, L.resid, L.resid_slot, L.resid_norm = FAKE, FAKE, FAKE, FAKE
+    assert decode(L) == 4
