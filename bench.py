@@ -325,8 +325,9 @@ def main():
     layers = [L0] + [replicate(L0, B) for _ in range(R - 1)]
     n = w.n_ctx
     # splits per code stream: the workload's count per KV head, times the group size
-    # with head groups (so the grid keeps its size), else the library's choice
-    S = w.n_splits * hg if w.n_splits else B.lrkv_decode_auto_splits(L0, n)
+    # with head groups (so the grid keeps its size); the library's choice for the
+    # LowRAM and pre-RoPE kernels (three workgroups per CU resident, not four)
+    S = w.n_splits * hg if (w.n_splits and not resid and not rope_base) else B.lrkv_decode_auto_splits(L0, n)
     q = dev(np.stack([synth.queries(w, 0, 0, b) for b in range(w.batch)]))
     out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device="cuda")
     ws = B.workspace(L0, S)

@@ -128,9 +128,11 @@ int32_t auto_splits(const LayerArgs &A, int32_t n_ctx) {
   const int64_t c = n_ctx - 1 - A.window;
   const int64_t nblk = c > 0 ? (c + LRKV_BLOCK - 1) / LRKV_BLOCK : 0;
   const int64_t units = int64_t(A.batch) * A.n_lat;
-  // about four workgroups of codes per compute unit (256 CUs), at least four
-  // 32-slot blocks per split
-  int64_t s = (1024 + units - 1) / units;
+  // about as many workgroups as are resident at once on the 256 compute units
+  // (four per unit; three for the pre-RoPE and LowRAM kernels, whose LDS or
+  // registers allow three), at least four 32-slot blocks per split
+  const int64_t target = (A.rope || A.lowram) ? 768 : 1024;
+  int64_t s = (target + units - 1) / units;
   const int64_t most = nblk / 4 > 1 ? nblk / 4 : 1;
   if (s > most) s = most;
   if (s < 1) s = 1;

@@ -54,7 +54,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 constexpr int kAnchorChunk = kMinAnchorRows;  // anchor rows staged in LDS at a time
 
-template <int RKMAX, int RVMAX>
+template <int RKMAX, int RVMAX, bool RP = false>
 struct MfmaSmem {
   union {
     float qt[LRKV_MAX_GROUP][RKMAX];  // prologue: projected queries (log2 units)
@@ -66,7 +66,13 @@ struct MfmaSmem {
   uint32_t sq[LRKV_MAX_GROUP][kD / 2];      // the group's queries (bf16 pairs), zero rows past G
   float m[5][LRKV_MAX_GROUP];               // per wave; [4] = the anchors
   float l[5][LRKV_MAX_GROUP];
-  float o[4][LRKV_MAX_GROUP][RVMAX];        // per-wave rank-space sums
+  union {
+    float o[4][LRKV_MAX_GROUP][RVMAX];      // epilogue: per-wave rank-space sums
+    struct {                                // pre-RoPE codes, during the block loop:
+      bf16_t su[RP ? kD * (RKMAX + 8) : 1]; //   U_K feature-major (rows of RKMAX + 8)
+      u32x4 rq[RP ? 4 : 1][2][64];          //   score B operands (q permuted, hi / lo)
+    } r;
+  } w;
 };
 
 // CB: bits per code element (16 bf16, 8 int8, 4 four-bit)
@@ -174,16 +180,16 @@ __device__ __forceinline__ u32x4 i4x8_to_bf16_x16(uint32_t w) {
 // are scored against q whose features are permuted to the order the lanes hold
 // (k = 8 q4 + i <-> feature 32 kc + 16 (i / 4) + 4 q4 + i % 4).
 template <int RKMAX, int RVMAX, bool EXACT, int CB, int LR = 0, int LRR = 0, bool RP = false>
-__global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d) {
+__device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeArgs &d) {
   constexpr int NKC = (RKMAX + 31) / 32;  // score MFMAs per 16-token tile (K = 32 each)
   constexpr int NVC = RVMAX / 16;         // value MFMAs per block (16 columns each)
   constexpr bool QC = CB < 16;            // quantised codes with per-token scales
   constexpr float kX16 = CB == 4 ? 0.0625f : 1.f;  // undoes the x16 of 4-bit operands
   constexpr int RS = RKMAX + 8;           // RP: LDS row of U_K (one feature, RKMAX + 8 bf16)
-  __shared__ MfmaSmem<RKMAX, RVMAX> sm;
-  __shared__ bf16_t su[RP ? kD * RS : 1];       // RP: U_K, feature-major
-  __shared__ u32x4 rq[RP ? 4 : 1][2][64];        // RP: score B operands (q, permuted, hi / lo)
+  __shared__ MfmaSmem<RKMAX, RVMAX, RP> sm;
   __shared__ float sra[RP ? kD / 2 : 1][2];      // RP: angle per position of each pair (revolutions)
+  bf16_t *const su = sm.w.r.su;
+  auto &rq = sm.w.r.rq;
 
   const int S = d.n_splits;
   // Workgroup i of the launch runs on XCD i % 8, and each XCD has its own L2:
@@ -349,7 +355,19 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
         bu[i][kc] = *reinterpret_cast<const u32x4 *>(ut + (16 * nt + t16) * urow + j * kD + 32 * kc + 8 * q4);
     }
   };
-  if constexpr (!RP) load_bu(0);
+  // pre-RoPE codes: U_K^T rows in 16-byte pieces (row c, features 8 p .. 8 p + 7),
+  // all requested now and written to LDS feature-major below
+  constexpr int NUP = RP ? (RKMAX * 16 + 255) / 256 : 1;
+  u32x4 upc[NUP];
+  if constexpr (RP) {
+#pragma unroll
+    for (int i = 0; i < NUP; ++i) {
+      const int pc = min(tid + 256 * i, rk * 16 - 1);
+      upc[i] = *reinterpret_cast<const u32x4 *>(ut + (pc >> 4) * kD + (pc & 15) * 8);
+    }
+  } else {
+    load_bu(0);
+  }
   const int r16 = tid >> 4, piece = tid & 15;  // 16 rows x 16 pieces of 16 bytes
   u32x4 qq = *reinterpret_cast<const u32x4 *>(qb + min(r16, G - 1) * kD + piece * 8);
   const int64_t arow = na > 0 ? anchor_row(alo + min(r16, na - 1)) : anchor_row(0);
@@ -375,10 +393,20 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
   if constexpr (RP) {
     // U_K feature-major (columns past rk zero), the pair angles, and q's score
     // operands in the permuted feature order, hi and lo parts (zero past G)
-    for (int e = tid; e < kD * RS; e += blockDim.x) {
-      const int f = e % kD, c = e / kD;
-      su[f * RS + c] = c < rk ? ut[c * kD + f] : bf16_t(0);
+#pragma unroll
+    for (int i = 0; i < NUP; ++i) {
+      const int pc = tid + 256 * i;
+      if (pc < rk * 16) {
+        const int c = pc >> 4, f0 = (pc & 15) * 8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          su[(f0 + 2 * e) * RS + c] = bf16_t(upc[i][e] & 0xffffu);
+          su[(f0 + 2 * e + 1) * RS + c] = bf16_t(upc[i][e] >> 16);
+        }
+      }
     }
+    for (int e = tid; e < kD * (RS - rk); e += blockDim.x)  // columns past rk: zero
+      su[(e % kD) * RS + rk + e / kD] = bf16_t(0);
     if (tid < kD / 2) {
       sra[tid][0] = L.rope_a[tid][0];
       sra[tid][1] = L.rope_a[tid][1];
@@ -806,7 +834,9 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
     }
   }
 
-  // ---- per-wave state to LDS
+  // ---- per-wave state to LDS (pre-RoPE codes: U_K and q's operands share the
+  // space of the rank-space sums, so every wave must be done with its blocks)
+  if constexpr (RP) __syncthreads();
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   if (q4 == 0 && t16 < G) {
@@ -819,7 +849,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int head = 4 * q4 + v;
-        if (head < G) sm.o[wave][head][16 * ni + t16] = o[ni][v];
+        if (head < G) sm.w.o[wave][head][16 * ni + t16] = o[ni][v];
       }
     }
   }
@@ -842,7 +872,7 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
     const float M = head_max(hh);
     float acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) acc = fmaf(weight(w, hh, M), sm.o[w][hh][cc], acc);
+    for (int w = 0; w < 4; ++w) acc = fmaf(weight(w, hh, M), sm.w.o[w][hh][cc], acc);
     split_record(d, q0 + hh, split)[4 + cc] = acc * kX16;
   }
   // o_A of the heads whose KV head has anchor rows in this split; the combine
@@ -896,6 +926,17 @@ __global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d
     rec[1] = l;
     rec[2] = rec[3] = 0.f;
   }
+}
+
+// The kernels: the code-space instances at up to four workgroups per compute
+// unit; the pre-RoPE instances asked to fit three (their LDS is sized for it).
+template <int RKMAX, int RVMAX, bool EXACT, int CB, int LR = 0, int LRR = 0>
+__global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d) {
+  partials_body<RKMAX, RVMAX, EXACT, CB, LR, LRR, false>(L, d);
+}
+template <int RKMAX, int RVMAX>
+__global__ __launch_bounds__(256, 3) void k_partials_rope(LayerArgs L, DecodeArgs d) {
+  partials_body<RKMAX, RVMAX, false, 16, 0, 0, true>(L, d);
 }
 
 template <int RKMAX, int RVMAX, bool EXACT>
@@ -957,10 +998,10 @@ static hipError_t launch_lr(const LayerArgs &L, const DecodeArgs &d, hipStream_t
 template <int RKMAX>
 static hipError_t launch_rp(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
   dim3 grid(d.n_splits, L.batch * L.n_lat);
-  if (L.rv_max <= 16) hipLaunchKernelGGL((k_partials_mfma<RKMAX, 16, false, 16, 0, 0, true>), grid, dim3(256), 0, s, L, d);
-  else if (L.rv_max <= 32) hipLaunchKernelGGL((k_partials_mfma<RKMAX, 32, false, 16, 0, 0, true>), grid, dim3(256), 0, s, L, d);
-  else if (L.rv_max <= 64) hipLaunchKernelGGL((k_partials_mfma<RKMAX, 64, false, 16, 0, 0, true>), grid, dim3(256), 0, s, L, d);
-  else hipLaunchKernelGGL((k_partials_mfma<RKMAX, 128, false, 16, 0, 0, true>), grid, dim3(256), 0, s, L, d);
+  if (L.rv_max <= 16) hipLaunchKernelGGL((k_partials_rope<RKMAX, 16>), grid, dim3(256), 0, s, L, d);
+  else if (L.rv_max <= 32) hipLaunchKernelGGL((k_partials_rope<RKMAX, 32>), grid, dim3(256), 0, s, L, d);
+  else if (L.rv_max <= 64) hipLaunchKernelGGL((k_partials_rope<RKMAX, 64>), grid, dim3(256), 0, s, L, d);
+  else hipLaunchKernelGGL((k_partials_rope<RKMAX, 128>), grid, dim3(256), 0, s, L, d);
   return hipGetLastError();
 }
 

@@ -123,6 +123,9 @@ def test_auto_splits():
     assert lib.lrkv_decode_auto_splits(ctypes.byref(L), 32768) == 32
     assert lib.lrkv_decode_auto_splits(ctypes.byref(L), 100) == 1
     assert lib.lrkv_decode_auto_splits(ctypes.byref(L), 0) == 0
+    # the pre-RoPE and LowRAM kernels fit three workgroups per compute unit: 768 / 32 = 24
+    L.rope_base = 500000.0
+    assert lib.lrkv_decode_auto_splits(ctypes.byref(L), 32768) == 24
 
 
 def test_compress_validation():
