@@ -176,7 +176,11 @@ __device__ __forceinline__ u32x4 i4x8_to_bf16_x16(uint32_t w) {
 // (q4, t16) features 16 ft + 4 q4 + v of token 16 h2 + t16 -- so the pair
 // (f, f + 64) of a rotation sits in the same lane (tiles ft and ft + 4).  Each
 // pair is turned by its position's angle (hardware sin/cos of the angle in
-// revolutions, reduced exactly), and the rotated keys, split into bf16 hi + lo,
+// revolutions).  A lane keeps the angles of its 16 pairs at its first token,
+// reduced exactly from the position on the wave's first block and every 16th
+// after, and in between advanced by the angle of the wave's block stride (one
+// add and a fraction, error a few units of 2^-24 revolutions); its second
+// token adds the angle of 16 positions.  The rotated keys, split into bf16 hi + lo,
 // are scored against q whose features are permuted to the order the lanes hold
 // (k = 8 q4 + i <-> feature 32 kc + 16 (i / 4) + 4 q4 + i % 4).
 template <int RKMAX, int RVMAX, bool EXACT, int CB, int LR = 0, int LRR = 0, bool RP = false>
@@ -188,6 +192,7 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
   constexpr int RS = RKMAX + 8;           // RP: LDS row of U_K (one feature, RKMAX + 8 bf16)
   __shared__ MfmaSmem<RKMAX, RVMAX, RP> sm;
   __shared__ float sra[RP ? kD / 2 : 1][2];      // RP: angle per position of each pair (revolutions)
+  __shared__ float srd[RP ? kD / 2 : 1][2];      // RP: the same over a wave's block stride, over 16 positions
   bf16_t *const su = sm.w.r.su;
   auto &rq = sm.w.r.rq;
 
@@ -408,8 +413,11 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
     for (int e = tid; e < kD * (RS - rk); e += blockDim.x)  // columns past rk: zero
       su[(e % kD) * RS + rk + e / kD] = bf16_t(0);
     if (tid < kD / 2) {
-      sra[tid][0] = L.rope_a[tid][0];
-      sra[tid][1] = L.rope_a[tid][1];
+      const float ahi = L.rope_a[tid][0], alo = L.rope_a[tid][1];
+      sra[tid][0] = ahi;
+      sra[tid][1] = alo;
+      srd[tid][0] = rope_rev(ahi, alo, float(kBlock * step));  // exact: kBlock * step < 2^24
+      srd[tid][1] = rope_rev(ahi, alo, 16.f);
     }
     if (wave == 0) {
 #pragma unroll
@@ -586,6 +594,14 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
     return sv;
   };
 
+  // RP: the lane's pair angles (revolutions) at its first token of the block being
+  // processed, and the blocks left before they are reduced from the position again
+  // (ranks up to 64 + 32 only: wider ones have no registers to spare for them and
+  // reduce every angle from its position)
+  constexpr bool kLean = RKMAX + RVMAX <= 96;
+  constexpr int kReseed = 16;
+  float rang[RP && kLean ? 4 : 1][4];
+  int rseed = 0;
   auto process = [&](int blk, BlockRegs<NKC, NVC, CB> &r) {
     if constexpr (LR > 0) {  // slots past c may hold any bits: their codes become 0 (the
                          // transposes below mix a token's columns; scores are masked anyway)
@@ -600,6 +616,28 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
     f32x4 s[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) s[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (RP && kLean) {
+      // angles of the lane's pairs at its first token, position blk * 32 + t16 + 1
+      // (code slot j holds token j + 1)
+      if (rseed == 0) {
+        const float pos = float(blk * kBlock + t16 + 1);
+#pragma unroll
+        for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int f = 16 * ft + 4 * q4 + v;
+            rang[ft][v] = rope_rev(sra[f][0], sra[f][1], pos);
+          }
+        rseed = kReseed;
+      } else {
+#pragma unroll
+        for (int ft = 0; ft < 4; ++ft)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            rang[ft][v] = __builtin_amdgcn_fractf(rang[ft][v] + srd[16 * ft + 4 * q4 + v][0]);
+      }
+      --rseed;
+    }
     if constexpr (RP) {
       // feature tiles {2 hf, 2 hf + 1} and their rotation partners {2 hf + 4, 2 hf + 5}
 #pragma unroll
@@ -611,8 +649,11 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) kr[tt][h2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
+          // U_K columns past rk are zero in LDS, so chunks past a head's rank add
+          // nothing (their code lanes re-read a present group): for narrow ranks
+          // they run unconditionally, sparing the branches
           for (int kc = 0; kc < NKC; ++kc) {
-            if (4 * kc < nkg) {
+            if (kLean || 4 * kc < nkg) {
               const u32x4 a = *reinterpret_cast<const u32x4 *>(&su[(16 * ft + t16) * RS + 32 * kc + 8 * q4]);
 #pragma unroll
               for (int h2 = 0; h2 < 2; ++h2) kr[tt][h2] = mfma16x16x32(a, r.k[h2][kc], kr[tt][h2]);
@@ -626,11 +667,18 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int f = 16 * ft + 4 * q4 + v;
-            const float ahi = sra[f][0], alo = sra[f][1];
+            float rev0, rev1;
+            if constexpr (kLean) {
+              rev0 = rang[ft][v];
+              rev1 = rev0 + srd[f][1];
+            } else {
+              const float pos = float(blk * kBlock + t16 + 1);
+              rev0 = rope_rev(sra[f][0], sra[f][1], pos);
+              rev1 = rope_rev(sra[f][0], sra[f][1], pos + 16.f);
+            }
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
-              const float pos = float(blk * kBlock + 16 * h2 + t16 + 1);  // code slot j holds token j + 1
-              const float rev = rope_rev(ahi, alo, pos);
+              const float rev = h2 ? rev1 : rev0;
               const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
               const float x = kr[tt][h2][v], y = kr[tt + 2][h2][v];
               kr[tt][h2][v] = x * cs - y * sn;

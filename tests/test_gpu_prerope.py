@@ -96,6 +96,10 @@ BASE = W["qwen3_1p7b_4k"].scaled(batch=2, n_q_heads=8, n_kv_heads=2, window=16)
 DECODE = [
     # label, workload, rope base, n_splits, ragged lengths
     ("llama_n3000_s32", W["llama31_8b_32k"].scaled(batch=1, n_ctx=3000), 500000.0, 32, None),
+    # one and three splits: 40+ blocks per wave, so the angles carried from block
+    # to block are reduced from the position again along the way
+    ("llama_n6000_s1", W["llama31_8b_32k"].scaled(batch=1, n_ctx=6000), 500000.0, 1, None),
+    ("llama_n5000_s3_b2", W["llama31_8b_32k"].scaled(batch=2, n_ctx=5000), 500000.0, 3, None),
     ("qwen_n1000", W["qwen3_1p7b_4k"].scaled(batch=2, n_ctx=1000), 1000000.0, 0, None),
     ("hc_n777_base1e4", W["llama31_8b_hc_8k"].scaled(batch=3, n_ctx=777), 10000.0, 0, None),
     ("mixed_ranks_n2000", W["llama31_8b_32layer"].scaled(batch=2, n_ctx=2000, n_steps=0), 500000.0, 0, None),
