@@ -23,9 +23,12 @@ __device__ __forceinline__ float bf16_trunc(float x) {
 __device__ __forceinline__ uint32_t pack_hi(float a, float b) {
   return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
 }
+// round-to-nearest-even of both, as one two-source conversion (element by
+// element, two conversions, a shift and an or come out of the scalar form)
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_rne(float a, float b) {
-  return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)a)) |
-         (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)b)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 }  // namespace lrkv
