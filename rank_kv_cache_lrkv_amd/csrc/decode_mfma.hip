@@ -180,7 +180,8 @@ __device__ __forceinline__ u32x4 i4x8_to_bf16_x16(uint32_t w) {
 // reduced exactly from the position on the wave's first block and every 16th
 // after, and in between advanced by the angle of the wave's block stride (one
 // add and a fraction, error a few units of 2^-24 revolutions); its second
-// token adds the angle of 16 positions.  The rotated keys, split into bf16 hi + lo,
+// token, 16 positions on, is turned by the angle-addition formula from the
+// first one's sin and cos.  The rotated keys, split into bf16 hi + lo,
 // are scored against q whose features are permuted to the order the lanes hold
 // (k = 8 q4 + i <-> feature 32 kc + 16 (i / 4) + 4 q4 + i % 4).
 template <int RKMAX, int RVMAX, bool EXACT, int CB, int LR = 0, int LRR = 0, bool RP = false>
@@ -192,7 +193,7 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
   constexpr int RS = RKMAX + 8;           // RP: LDS row of U_K (one feature, RKMAX + 8 bf16)
   __shared__ MfmaSmem<RKMAX, RVMAX, RP> sm;
   __shared__ float sra[RP ? kD / 2 : 1][2];      // RP: angle per position of each pair (revolutions)
-  __shared__ float srd[RP ? kD / 2 : 1][2];      // RP: the same over a wave's block stride, over 16 positions
+  __shared__ float srd[RP ? kD / 2 : 1][3];      // RP: the angle over a wave's block stride; cos, sin over 16 positions
   bf16_t *const su = sm.w.r.su;
   auto &rq = sm.w.r.rq;
 
@@ -417,7 +418,9 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
       sra[tid][0] = ahi;
       sra[tid][1] = alo;
       srd[tid][0] = rope_rev(ahi, alo, float(kBlock * step));  // exact: kBlock * step < 2^24
-      srd[tid][1] = rope_rev(ahi, alo, 16.f);
+      const float r16 = rope_rev(ahi, alo, 16.f);
+      srd[tid][1] = __builtin_amdgcn_cosf(r16);
+      srd[tid][2] = __builtin_amdgcn_sinf(r16);
     }
     if (wave == 0) {
 #pragma unroll
@@ -667,19 +670,27 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int f = 16 * ft + 4 * q4 + v;
-            float rev0, rev1;
+            float sn2[2], cs2[2];
             if constexpr (kLean) {
-              rev0 = rang[ft][v];
-              rev1 = rev0 + srd[f][1];
+              // the second token (16 positions on) by the angle-addition formula
+              const float rev0 = rang[ft][v];
+              sn2[0] = __builtin_amdgcn_sinf(rev0);
+              cs2[0] = __builtin_amdgcn_cosf(rev0);
+              const float c16 = srd[f][1], s16 = srd[f][2];
+              cs2[1] = fmaf(cs2[0], c16, -sn2[0] * s16);
+              sn2[1] = fmaf(sn2[0], c16, cs2[0] * s16);
             } else {
               const float pos = float(blk * kBlock + t16 + 1);
-              rev0 = rope_rev(sra[f][0], sra[f][1], pos);
-              rev1 = rope_rev(sra[f][0], sra[f][1], pos + 16.f);
+#pragma unroll
+              for (int h2 = 0; h2 < 2; ++h2) {
+                const float rev = rope_rev(sra[f][0], sra[f][1], pos + 16.f * h2);
+                sn2[h2] = __builtin_amdgcn_sinf(rev);
+                cs2[h2] = __builtin_amdgcn_cosf(rev);
+              }
             }
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
-              const float rev = h2 ? rev1 : rev0;
-              const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+              const float sn = sn2[h2], cs = cs2[h2];
               const float x = kr[tt][h2][v], y = kr[tt + 2][h2][v];
               kr[tt][h2][v] = x * cs - y * sn;
               kr[tt + 2][h2][v] = fmaf(x, sn, y * cs);
