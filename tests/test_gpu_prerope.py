@@ -187,3 +187,16 @@ def test_prerope_full_size_llama_32k_sampled():
     assert np.all(np.isfinite(got))
     units = [(0, 0), (w.batch // 2, w.n_kv_heads // 2), (w.batch - 1, w.n_kv_heads - 1)]
     check_decode(got, expected(hc, base, units), "bf16", "prerope_full_llama31_8b_32k")
+
+
+@pytest.mark.parametrize("base,S", [(500000.0, 2), (10000.0, 3)])
+def test_prerope_long_positions(base, S):
+    """Positions up to 131,071 on one KV head with two or three splits: each wave
+    carries its pair angles over ~500 blocks at a stride of 8 or 12 blocks,
+    reducing them from the position again every 16 blocks."""
+    w = W["llama31_8b_32k"].scaled(batch=1, n_q_heads=4, n_kv_heads=1, n_ctx=131072)
+    hc = host_case(w)
+    announce(f"pre-RoPE long positions: base {base} n {w.n_ctx} S {S}")
+    L = gpu_prerope_layer(hc, base)
+    got = run_decode(L, w, w.n_ctx, hc.q, S)
+    check_decode(got, expected(hc, base), "bf16", f"prerope_long_{int(base)}_s{S}")
