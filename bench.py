@@ -48,14 +48,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, n, bits=16, hg=1, resid=0):
+def algorithmic_bytes(w, n, bits=16, hg=1, resid=0, versions=1):
     """Bytes the method must move for one decode call of one layer, and the part
     the partials kernel moves (codes, anchors, U_K, q).  Quantised codes: r bytes
     (int8) or r / 2 bytes (4-bit) per code row plus its 4-byte scale.  Group-head
     latents (hg KV heads per code stream): one code row per group and token, bases
     of hg * 128 rows per group, anchors per KV head.  LowRAM values (resid = R >
     0): key codes only, R residual rows (256 bytes and a 4-byte slot) per 32-slot
-    block, and the row's predictor (r_k x 128) in place of U_V."""
+    block, and the row's predictor (r_k x 128) in place of U_V.  Basis versions
+    (codes made under several bases): every version's U_K and U_V rows."""
     import oracle
     s = 4 if w.dtype == "f32" else 2
     c = len(oracle.code_positions(n, w.window))
@@ -66,8 +67,8 @@ def algorithmic_bytes(w, n, bits=16, hg=1, resid=0):
     else:
         codes = units * c * (w.rank_k + w.rank_v) * s
     anchors = w.batch * w.n_kv_heads * a * 2 * 128 * s
-    u_k = w.n_kv_heads * 128 * w.rank_k * s
-    u_v = w.n_kv_heads * 128 * w.rank_v * s
+    u_k = versions * w.n_kv_heads * 128 * w.rank_k * s
+    u_v = versions * w.n_kv_heads * 128 * w.rank_v * s
     if resid:
         nblk = (c + 31) // 32
         codes = units * (c * w.rank_k * s + nblk * resid * (128 * s + 4))
@@ -174,11 +175,26 @@ def build_cache(w, B, dev, bits=16, hg=1, resid=0, rope_base=0.0):
     return L, compress, oja
 
 
+def with_versions(L, B, nver, n):
+    """The same cache read as codes made under nver basis versions: bases holds nver
+    copies of the layer's bases, and row b's code slots are cut into nver runs of
+    whole 32-slot blocks (version v from slot 32 * floor(v * blocks / nver))."""
+    import torch
+    c = max(0, n - 1 - L.window)
+    nblk = (c + 31) // 32
+    starts = [32 * (v * nblk // nver) for v in range(nver)]
+    vs = torch.tensor([starts] * L.batch, dtype=torch.int32, device="cuda")
+    return B.Layer(L.dtype, L.batch, L.n_q_heads, L.n_kv_heads, L.window, L.cap, L.rank_k, L.rank_v,
+                   torch.cat([L.bases] * nver), L.codes_k, L.codes_v, L.anchor_k, L.anchor_v,
+                   L.scales_k, L.scales_v, n_versions=nver, version_start=vs)
+
+
 def replicate(L, B):
     sc = lambda t: None if t is None else t.clone()
     return B.Layer(L.dtype, L.batch, L.n_q_heads, L.n_kv_heads, L.window, L.cap, L.rank_k, L.rank_v,
                    L.bases.clone(), L.codes_k.clone(), sc(L.codes_v), L.anchor_k.clone(),
-                   L.anchor_v.clone(), sc(L.scales_k), sc(L.scales_v), head_group=L.head_group,
+                   L.anchor_v.clone(), sc(L.scales_k), sc(L.scales_v), n_versions=L.n_versions,
+                   version_start=sc(L.version_start), head_group=L.head_group,
                    value_mode=L.value_mode, resid_per_block=L.resid_per_block, predictor=sc(L.predictor),
                    resid=sc(L.resid), resid_slot=sc(L.resid_slot), resid_norm=sc(L.resid_norm),
                    rope_base=L.rope_base)
@@ -265,6 +281,10 @@ def main():
     ap.add_argument("--rope-base", type=float, default=0.0,
                     help="> 1: key codes of pre-RoPE keys, reconstructed and rotated in the decode "
                          "(rotate-half RoPE with this base; bf16 codes)")
+    ap.add_argument("--versions", type=int, default=1, metavar="V",
+                    help="codes made under V basis versions (OjaKV), the row's code slots cut into V "
+                         "equal runs of whole blocks; every version holds the same basis, so the output "
+                         "is that of one version (bf16 codes)")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated (0: >= 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -315,12 +335,17 @@ def main():
     rope_base = args.rope_base
     assert not rope_base or (bits == 16 and hg == 1 and not resid and w.dtype == "bf16"), \
         "pre-RoPE key codes: bf16 codes, no head groups, value codes"
+    nver = args.versions
+    assert nver == 1 or (bits == 16 and hg == 1 and not resid and not rope_base and w.dtype == "bf16"), \
+        "basis versions: bf16 codes, no head groups, value codes, keys after RoPE"
     L0, compress, oja = build_cache(w, B, dev, bits, hg, resid, rope_base)
+    if nver > 1:
+        L0 = with_versions(L0, B, nver, w.n_ctx)
     log(f"cache built and compressed on the GPU in {time.time() - t0:.1f} s "
         f"(compress {compress['ms']:.3f} ms, {compress['gbps']} GB/s)")
     if oja:
         log(f"Oja step over the prompt's keys: {oja['ms']:.3f} ms ({oja['gbps']} GB/s of rows)")
-    nb = algorithmic_bytes(w, w.n_ctx, bits, hg, resid)
+    nb = algorithmic_bytes(w, w.n_ctx, bits, hg, resid, nver)
     R = args.replicas or max(1, math.ceil((1 << 30) / nb["call"]))
     layers = [L0] + [replicate(L0, B) for _ in range(R - 1)]
     n = w.n_ctx
@@ -376,10 +401,12 @@ def main():
         kernel = f"k_partials_mfma, LowRAM values (key codes + {resid} residual rows per block)"
     if rope_base:
         kernel = "k_partials_mfma, pre-RoPE key codes (keys reconstructed and rotated per block)"
+    if nver > 1:
+        kernel += f", codes under {nver} basis versions"
     k_bytes = nb["partials"]
     achieved = k_bytes / (k_ms * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    traffic = None if (resid or rope_base) else traffic_from_profile(src_hash, args.codes, hg)
+    traffic = None if (resid or rope_base or nver > 1) else traffic_from_profile(src_hash, args.codes, hg)
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
@@ -402,7 +429,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": 128, "n_ctx": n, "rank_k": w.rank_k,
                    "rank_v": w.rank_v, "window": w.window, "n_splits": S, "cache_replicas": R,
-                   "codes": args.codes, "head_group": hg, "lowram_resid": resid, "rope_base": rope_base},
+                   "codes": args.codes, "head_group": hg, "lowram_resid": resid, "rope_base": rope_base,
+                   "basis_versions": nver},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": k_bytes,

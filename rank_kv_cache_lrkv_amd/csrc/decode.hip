@@ -248,17 +248,22 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, floa
 // version's rank-space sum is merged from that version's splits and
 // up-projected with that version's U_V; the rest is as in k_combine.  One
 // workgroup of 128 threads per (query head, batch row), thread t = output
-// feature t.
+// feature t.  The splits' maxima, sums and versions are read once into LDS
+// (a thread per split); every later loop runs over LDS or issues its record
+// loads eight at a time ahead of the arithmetic.  Sums run split by split in
+// index order, as the records are laid out.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(128) void k_combine_versions(LayerArgs L, DecodeArgs d, float *out) {
-  __shared__ float sot[128];
+  __shared__ float sm[LRKV_MAX_SPLITS], sl[LRKV_MAX_SPLITS];  // split maxima, sums
+  __shared__ int sv[LRKV_MAX_SPLITS];                         // split versions
+  __shared__ float sot[LRKV_MAX_VERSIONS][128];               // per-version rank-space sums
   const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int kvh = i / L.group;
   const int h = kvh / L.hg, j = kvh % L.hg;
   const HeadInfo hd = L.heads[h];
   const int rv = hd.rv;
-  const int S = d.n_splits;
+  const int S = d.n_splits, V = L.n_versions;
   const int64_t qi = int64_t(b) * L.n_q + i;
   const int n = row_ctx(d, b);
   const int c = max(0, n - 1 - L.window);
@@ -267,34 +272,53 @@ __global__ __launch_bounds__(128) void k_combine_versions(LayerArgs L, DecodeArg
   const int per = anchor_rows_per_split(a1 * L.hg, S);
   const int s_a0 = (j * a1) / per, s_a1 = min(S, ((j + 1) * a1 + per - 1) / per);  // as in k_combine
 
-  float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, split_record(d, qi, s)[0]);  // finite: token 0 is an anchor
-  float Ltot = 0.f;
-  for (int s = 0; s < S; ++s) {
+  for (int s = t; s < S; s += blockDim.x) {
     const float *r = split_record(d, qi, s);
-    if (r[0] != kNegInf) Ltot = fmaf(fast_exp2(r[0] - M), r[1], Ltot);
+    sm[s] = r[0];
+    sl[s] = r[1];
+    sv[s] = split_segment(L, b, s, S, nblk).v;
   }
-  float y = 0.f;
-  for (int v = 0; v < L.n_versions; ++v) {
-    // this version's merged rank-space sum (the splits of a version are consecutive)
-    if (t < rv) {
-      float o = 0.f;
-      for (int s = 0; s < S; ++s) {
-        if (split_segment(L, b, s, S, nblk).v != v) continue;
-        const float *r = split_record(d, qi, s);
-        if (r[0] != kNegInf) o = fmaf(fast_exp2(r[0] - M), r[4 + t], o);
+  for (int e = t; e < V * kD; e += blockDim.x) sot[e / kD][e % kD] = 0.f;
+  __syncthreads();
+
+  float M = kNegInf;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, sm[s]);  // finite: token 0 is an anchor
+  float Ltot = 0.f;
+  for (int s = 0; s < S; ++s)
+    if (sm[s] != kNegInf) Ltot = fmaf(fast_exp2(sm[s] - M), sl[s], Ltot);
+  // each version's merged rank-space sum (the splits of a version are consecutive)
+  if (t < rv) {
+    float o = 0.f;
+    int cur = sv[0];
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = split_record(d, qi, min(s0 + u, S - 1))[4 + t];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int s = s0 + u;
+        if (s >= S) break;
+        if (sv[s] != cur) {
+          sot[cur][t] = o;
+          o = 0.f;
+          cur = sv[s];
+        }
+        if (sm[s] != kNegInf) o = fmaf(fast_exp2(sm[s] - M), x[u], o);
       }
-      sot[t] = o;
     }
-    __syncthreads();
+    sot[cur][t] = o;
+  }
+  __syncthreads();
+  float y = 0.f;
+  for (int v = 0; v < V; ++v) {
     const T *uvt = static_cast<const T *>(L.bases) + v * L.version_elems + hd.u_v;  // U_V^T rows
-    for (int cc = 0; cc < rv; ++cc) y = fmaf(to_f32(uvt[cc * L.hg * kD + j * kD + t]), sot[cc], y);
-    __syncthreads();
+#pragma unroll 8
+    for (int cc = 0; cc < rv; ++cc) y = fmaf(to_f32(uvt[cc * L.hg * kD + j * kD + t]), sot[v][cc], y);
   }
   float oa = 0.f;
   for (int s = s_a0; s < s_a1; ++s) {
     const float *r = split_record(d, qi, s);
-    if (r[0] != kNegInf) oa = fmaf(fast_exp2(r[0] - M), r[d.oa + t], oa);
+    if (sm[s] != kNegInf) oa = fmaf(fast_exp2(sm[s] - M), r[d.oa + t], oa);
   }
   out[qi * kD + t] = (y + oa) / Ltot;
 }

@@ -45,6 +45,8 @@ Q = B_ * HQ * 128 * 2
     # LowRAM, 4 residual rows (bf16, 128 wide, 4-byte slot) per 32-slot block, key codes only
     ("lowram4", {"resid": 4},
      B_ * HKV * (C * RK * 2 + ((C + 31) // 32) * 4 * (128 * 2 + 4)) + ANCHORS + U_K + Q),
+    # codes under 3 basis versions: every version's U_K rows
+    ("versions3", {"versions": 3}, B_ * HKV * C * (RK + RV) * 2 + ANCHORS + 3 * U_K + Q),
 ])
 def test_partials_algorithmic_bytes(label, kw, expected):
     w = synth.WORKLOADS["llama31_8b_32k"]
