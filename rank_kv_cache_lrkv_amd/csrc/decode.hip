@@ -248,8 +248,8 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, floa
 // version's rank-space sum is merged from that version's splits and
 // up-projected with that version's U_V; the rest is as in k_combine.  One
 // workgroup of 128 threads per (query head, batch row), thread t = output
-// feature t.  The splits' maxima, sums and versions are read once into LDS
-// (a thread per split); every later loop runs over LDS or issues its record
+// feature t.  The splits' maxima, sums and versions (each record carries its
+// split's version) are read once into LDS (a thread per split); every later loop runs over LDS or issues its record
 // loads eight at a time ahead of the arithmetic.  Sums run split by split in
 // index order, as the records are laid out.
 // ---------------------------------------------------------------------------
@@ -266,17 +266,15 @@ __global__ __launch_bounds__(128) void k_combine_versions(LayerArgs L, DecodeArg
   const int S = d.n_splits, V = L.n_versions;
   const int64_t qi = int64_t(b) * L.n_q + i;
   const int n = row_ctx(d, b);
-  const int c = max(0, n - 1 - L.window);
-  const int nblk = (c + kBlock - 1) / kBlock;
   const int a1 = min(n, 1 + L.window);  // anchor rows per KV head
   const int per = anchor_rows_per_split(a1 * L.hg, S);
   const int s_a0 = (j * a1) / per, s_a1 = min(S, ((j + 1) * a1 + per - 1) / per);  // as in k_combine
 
-  for (int s = t; s < S; s += blockDim.x) {
-    const float *r = split_record(d, qi, s);
-    sm[s] = r[0];
-    sl[s] = r[1];
-    sv[s] = split_segment(L, b, s, S, nblk).v;
+  for (int s = t; s < S; s += blockDim.x) {  // m, l and the version the partials kernel wrote
+    const float4 r = *reinterpret_cast<const float4 *>(split_record(d, qi, s));
+    sm[s] = r.x;
+    sl[s] = r.y;
+    sv[s] = min(max(int(r.z), 0), V - 1);
   }
   for (int e = t; e < V * kD; e += blockDim.x) sot[e / kD][e % kD] = 0.f;
   __syncthreads();

@@ -255,7 +255,8 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
     for (int i = tid; i < G; i += blockDim.x) {
       float *rec = split_record(d, q0 + i, split);
       rec[0] = kNegInf;
-      rec[1] = rec[2] = rec[3] = 0.f;
+      rec[1] = rec[3] = 0.f;
+      rec[2] = float(sg.v);
     }
     for (int i = tid; i < G * rv; i += blockDim.x) split_record(d, q0 + i / rv, split)[4 + i % rv] = 0.f;
     return;
@@ -983,7 +984,8 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
     float *rec = split_record(d, q0 + hh, split);
     rec[0] = M;
     rec[1] = l;
-    rec[2] = rec[3] = 0.f;
+    rec[2] = float(sg.v);
+    rec[3] = 0.f;
   }
 }
 

@@ -63,8 +63,9 @@ __host__ __device__ __forceinline__ int64_t resid_entry(const LayerArgs &L, int 
 // Split s of a (batch row, KV head) covers a share of its code blocks and a
 // share of its a anchors (runs of at least 16 rows on the first splits); per
 // query head it leaves one record in the workspace:
-//   [m, l, 0, 0, o~[rvp], o_A[128]]
+//   [m, l, v, 0, o~[rvp], o_A[128]]
 // m: running max of the scores (log2 units, -inf if the split saw nothing),
+// v: the split's basis version (a float32 integer; 0 with one version),
 // l: sum of 2^(s - m), o~: rank-space value sum of the codes (rvp = rv_max
 // rounded up to 4), o_A: 128-dim value sum of the anchors (written only by
 // splits that hold anchors).
