@@ -270,6 +270,11 @@ __global__ __launch_bounds__(128) void k_combine_versions(LayerArgs L, DecodeArg
   const int per = anchor_rows_per_split(a1 * L.hg, S);
   const int s_a0 = (j * a1) / per, s_a1 = min(S, ((j + 1) * a1 + per - 1) / per);  // as in k_combine
 
+  // the anchor sums of output feature t from the first 8 splits holding this KV
+  // head's anchor rows, requested before anything else (as k_combine does)
+  float ax0[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) ax0[u] = split_record(d, qi, min(s_a0 + u, s_a1 - 1))[d.oa + t];
   for (int s = t; s < S; s += blockDim.x) {  // m, l and the version the partials kernel wrote
     const float4 r = *reinterpret_cast<const float4 *>(split_record(d, qi, s));
     sm[s] = r.x;
@@ -314,9 +319,20 @@ __global__ __launch_bounds__(128) void k_combine_versions(LayerArgs L, DecodeArg
     for (int cc = 0; cc < rv; ++cc) y = fmaf(to_f32(uvt[cc * L.hg * kD + j * kD + t]), sot[v][cc], y);
   }
   float oa = 0.f;
-  for (int s = s_a0; s < s_a1; ++s) {
-    const float *r = split_record(d, qi, s);
-    if (sm[s] != kNegInf) oa = fmaf(fast_exp2(sm[s] - M), r[d.oa + t], oa);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int s = s_a0 + u;
+    if (s < s_a1 && sm[s] != kNegInf) oa = fmaf(fast_exp2(sm[s] - M), ax0[u], oa);
+  }
+  for (int s0 = s_a0 + 8; s0 < s_a1; s0 += 8) {  // more anchor splits: 8 at a time, loads first
+    float ax[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) ax[u] = split_record(d, qi, min(s0 + u, s_a1 - 1))[d.oa + t];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u;
+      if (s < s_a1 && sm[s] != kNegInf) oa = fmaf(fast_exp2(sm[s] - M), ax[u], oa);
+    }
   }
   out[qi * kD + t] = (y + oa) / Ltot;
 }
