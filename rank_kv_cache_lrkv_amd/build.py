@@ -1,10 +1,12 @@
-"""Builds liblrkv.so in-tree with hipcc for gfx950.
+"""Builds the two libraries in-tree with hipcc for gfx950.
 
     python -m rank_kv_cache_lrkv_amd.build [-v]
 
-Every HIP source is compiled to an object under _build/ (in parallel), then
-linked into rank_kv_cache_lrkv_amd/liblrkv.so.  Packed float32 VALU instructions
-are switched off for the device code.
+Every HIP source under csrc/ is compiled to an object under _build/ (in
+parallel) and linked into rank_kv_cache_lrkv_amd/liblrkv.so (include/lrkv.h);
+the measurement kernels under probe/ go into liblrkv_probe.so
+(include/lrkv_probe.h), which only the benchmark loads.  Packed float32 VALU
+instructions are switched off for the device code.
 """
 
 from __future__ import annotations
@@ -18,9 +20,11 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
+PROBE = os.path.join(PKG, "probe")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblrkv.so")
+PROBE_LIB = os.path.join(PKG, "liblrkv_probe.so")
 ARCH = "gfx950"
 
 
@@ -31,8 +35,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(d=CSRC):
+    return sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(".hip"))
 
 
 COMMON_FLAGS = [
@@ -43,8 +47,8 @@ COMMON_FLAGS = [
 
 
 def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src, "-o", obj]
+    obj = os.path.join(BUILD_DIR, os.path.basename(os.path.dirname(src)) + "_" + os.path.basename(src) + ".o")
+    cmd = [hipcc(), *COMMON_FLAGS, f"-I{INCLUDE}", f"-I{os.path.dirname(src)}", "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,21 +60,27 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link liblrkv.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> str:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source, link liblrkv.so and liblrkv_probe.so; returns
+    the path of liblrkv.so."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs, psrcs = sources(CSRC), sources(PROBE)
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(psrcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + psrcs))
+    _link(objs[len(srcs):], PROBE_LIB, verbose)
+    return _link(objs[:len(srcs)], LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -264,12 +264,14 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
 
   // this (row, head)'s key and value code regions (and int8 scales) as buffer
   // resources; byte offsets are element offsets * CB / 8 (regions start on even
-  // elements)
+  // elements).  The extents are cap times the bytes of one code row (r * CB / 8,
+  // an integer for ranks that are multiples of 16), which the host bounds below
+  // 2^31; forming cap * r * CB first could overflow 32 bits.
   const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
-      static_cast<char *>(L.codes_k) + (hd.ck + int64_t(b) * L.cap * rk) * CB / 8, 0, L.cap * rk * CB / 8,
+      static_cast<char *>(L.codes_k) + (hd.ck + int64_t(b) * L.cap * rk) * CB / 8, 0, L.cap * (rk * CB / 8),
       kBufferWord3);
   const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
-      static_cast<char *>(L.codes_v) + (hd.cv + int64_t(b) * L.cap * rv) * CB / 8, 0, L.cap * rv * CB / 8,
+      static_cast<char *>(L.codes_v) + (hd.cv + int64_t(b) * L.cap * rv) * CB / 8, 0, L.cap * (rv * CB / 8),
       kBufferWord3);
   __amdgpu_buffer_rsrc_t skres = kres, svres = vres;
   if constexpr (QC) {

@@ -15,6 +15,7 @@ from .workloads import (  # noqa: F401
     calibration_rows,
     group_basis,
     haar_orthogonal,
+    layer_kv_device,
     queries,
     ranks,
     round_to_storage,

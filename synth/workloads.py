@@ -213,3 +213,29 @@ def queries(w: Workload, layer: int, step: int, b: int, scale: float = 1.0) -> n
     ``scale`` > 1 sharpens the attention (a peaky-softmax stress case)."""
     q = _rng(w, "query", layer, step, b).standard_normal((w.n_q_heads, HEAD_DIM)) * scale
     return round_to_storage(q, w.dtype)
+
+
+def layer_kv_device(w: Workload, layer: int, which: str, device="cuda"):
+    """Keys or values of every (batch row, KV head) of one layer drawn on the GPU:
+    a torch bfloat16 tensor [batch][n_kv_heads][n_total][128] of rows
+    (z * sigma) R^T with the same spectrum and the same Haar rotation per
+    (layer, KV head) as ``unit_kv``, but latents z from torch's device generator
+    (seeded per (layer, KV head, role)), multiplied in float32.  Same
+    distribution as ``unit_kv``, other random draws: for inputs too large to make
+    on the host in reasonable time (the 32-layer cache), where no oracle reads
+    them."""
+    import torch
+
+    assert w.v_from_k == 0.0, "device generation has no key-to-value map"
+    out = torch.empty((w.batch, w.n_kv_heads, w.n_total, HEAD_DIM), dtype=torch.bfloat16, device=device)
+    sig = torch.from_numpy(spectrum(_tau(w, which)).astype(np.float32)).to(device)
+    gen = torch.Generator(device=device)
+    for h in range(w.n_kv_heads):
+        seed = int(np.random.SeedSequence([w.wid, _ROLE["tok_" + which], layer, h, 1 << 20])
+                   .generate_state(1, np.uint64)[0] >> np.uint64(1))
+        gen.manual_seed(seed)
+        rt = torch.from_numpy(rotation(w, layer, h, which).T.astype(np.float32)).to(device)
+        z = torch.randn((w.batch, w.n_total, HEAD_DIM), generator=gen, device=device, dtype=torch.float32)
+        out[:, h] = ((z * sig) @ rt).to(torch.bfloat16)
+        del z
+    return out

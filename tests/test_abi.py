@@ -309,3 +309,42 @@ def test_rope_validation():
     L.value_mode, L.resid_per_block = 1, 4
     L.predictor, L.resid, L.resid_slot, L.resid_norm = FAKE, FAKE, FAKE, FAKE
     assert decode(L) == 4
+
+
+PROBE_HEADER = os.path.join(os.path.dirname(HEADER), "lrkv_probe.h")
+
+
+def test_probe_library_exports_its_header():
+    """The measurement library (read stream, spin) exports what lrkv_probe.h
+    declares, and the binding names the same functions."""
+    from rank_kv_cache_lrkv_amd import measure
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(lrkv_probe_[a-z_]+)\s*\(", text)))
+    assert declared == sorted(measure.exported_names())
+    lib = measure.lib()
+    out = os.popen(f"nm -D --defined-only {measure.LIB_PATH}").read()
+    for name in declared:
+        assert hasattr(lib, name), name
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 1 << 20, FAKE, 1024, 4, 0), 1),     # null source
+    ((FAKE, 1 << 20, None, 1024, 4, 0), 1),     # null sink
+    ((FAKE, 0, FAKE, 1024, 4, 0), 2),           # no bytes
+    ((FAKE, 1000, FAKE, 1024, 4, 0), 2),        # not a multiple of 16
+    ((FAKE, 1 << 20, FAKE, 0, 4, 0), 2),        # empty grid
+    ((FAKE, 1 << 20, FAKE, 70000, 4, 0), 2),    # grid past 65535
+    ((FAKE, 1 << 20, FAKE, 1024, 3, 0), 2),     # unroll not 1, 2, 4 or 8
+    ((FAKE + 8, 1 << 20, FAKE, 1024, 4, 0), 5), # misaligned source
+])
+def test_probe_read_rejects_bad_arguments(args, status):
+    from rank_kv_cache_lrkv_amd import measure
+    assert measure.lib().lrkv_probe_read(*args, None) == status
+
+
+def test_probe_spin_rejects_bad_arguments():
+    from rank_kv_cache_lrkv_amd import measure
+    assert measure.lib().lrkv_probe_spin(100, None, None) == 1
+    assert measure.lib().lrkv_probe_spin(-1, FAKE, None) == 2
+    assert measure.lib().lrkv_probe_spin((1 << 32) + 1, FAKE, None) == 2

@@ -161,15 +161,63 @@ def test_full_size_sampled(name, S):
     check_decode(got, oracle_units(w, 0, w.n_ctx, 0, sample_units(w), q), w.dtype, f"full_{name}")
 
 
-@pytest.mark.parametrize("layer", [0, 31])
+def prefill_rows(w, layer, n, kv):
+    """As ``prefill`` from already generated host rows kv = {"k": .., "v": ..}."""
+    rk, rv, bases = bases_flat(w, layer)
+    cmax = max(0, n - 1 - w.window)
+    L = B.Layer.allocate(dtype=B.LRKV_BF16, batch=w.batch, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+                         window=w.window, cap=layout.round_cap(cmax + w.n_steps), rank_k=rk, rank_v=rv,
+                         bases=dev(bases, w.dtype))
+    K, V = dev(kv["k"], w.dtype), dev(kv["v"], w.dtype)
+    B.lrkv_compress(L, 0, K[:, :, 1:], cmax, 0)
+    B.lrkv_compress(L, 1, V[:, :, 1:], cmax, 0)
+    B.lrkv_store_anchors(L, K[:, :, 0:1], V[:, :, 0:1], 0, 1)
+    lo = max(1, n - w.window)
+    B.lrkv_store_anchors(L, K[:, :, lo:n], V[:, :, lo:n], lo, n - lo)
+    return L, K, V
+
+
+def step_units(w, t):
+    """Units compared at decode step t (1-based): two per step, rotating so that
+    over the steps every (batch row, KV head) unit of the layer is compared at
+    least once, and every unit at the last step."""
+    units = [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
+    if t == w.n_steps:
+        return units
+    k = len(units)
+    return [units[(2 * (t - 1)) % k], units[(2 * (t - 1) + 1) % k]]
+
+
+@pytest.mark.parametrize("layer", range(32))
 def test_full_size_32layer_decode_steps(layer):
-    """32-layer workload at full context: prefill 32768 tokens with the layer's
-    mixed ranks, then 16 decode steps with cache maintenance (sampled units)."""
+    """32-layer workload at full context, every layer: prefill 32768 tokens with the
+    layer's mixed ranks, then 16 decode steps with cache maintenance; at each step
+    the decode output of two (batch row, KV head) units (rotating over the layer's
+    32 units) is compared with the oracle, and all 32 units at the last step."""
     w = W["llama31_8b_32layer"]
     rk, rv = synth.ranks(w, layer)
     announce(f"full 32-layer workload, layer {layer}, ranks {rk.tolist()} / {rv.tolist()}")
-    L, K, V = prefill(w, layer, w.n_ctx)
-    units = sample_units(w, 2)
+    kv = {x: full_rows(w, layer, x) for x in "kv"}
+    L, K, V = prefill_rows(w, layer, w.n_ctx, kv)
+    # oracle side: the exact projection of every code row up to the last step's
+    # context, once per unit (each code row is its own x U; a context's codes are
+    # the first rows), rounded to bf16 as stored
+    n_last = w.n_total
+    cpos_last = oracle.code_positions(n_last, w.window)
+    uk = [synth.basis(w, layer, h, "k", int(rk[h])).astype(np.float64) for h in range(w.n_kv_heads)]
+    uv = [synth.basis(w, layer, h, "v", int(rv[h])).astype(np.float64) for h in range(w.n_kv_heads)]
+    codes = {}
+
+    def unit_codes(b, h):
+        if (b, h) not in codes:
+            k = kv["k"][b, h].astype(np.float64)
+            v = kv["v"][b, h].astype(np.float64)
+            codes[(b, h)] = (to_storage(oracle.oracle_compress(k[cpos_last], uk[h]), w.dtype),
+                             to_storage(oracle.oracle_compress(v[cpos_last], uv[h]), w.dtype))
+        return codes[(b, h)]
+
+    g = w.group
+    compared = set()
     for t in range(1, w.n_steps + 1):
         pos = w.n_ctx + t - 1
         B.lrkv_append(L, K[:, :, pos].contiguous(), V[:, :, pos].contiguous(), pos)
@@ -177,5 +225,15 @@ def test_full_size_32layer_decode_steps(layer):
         q = queries(w, layer, t)
         got = decode(L, w, n, q, B.lrkv_decode_auto_splits(L, n))
         assert np.all(np.isfinite(got))
-        if t in (1, 8, 16):
-            check_decode(got, oracle_units(w, layer, n, t, units, q), "bf16", f"l{layer}_step{t}")
+        nc = len(oracle.code_positions(n, w.window))
+        apos = oracle.anchor_positions(n, w.window)
+        want = np.full_like(got, np.nan)
+        for b, h in step_units(w, t):
+            ck, cv = unit_codes(b, h)
+            rows = slice(h * g, (h + 1) * g)
+            want[b, rows] = oracle.oracle_decode_unit(
+                q[b, rows], uk[h], uv[h], ck[:nc], cv[:nc], kv["k"][b, h][apos].astype(np.float64),
+                kv["v"][b, h][apos].astype(np.float64), oracle.default_scale())
+            compared.add((b, h))
+        check_decode(got, want, "bf16", f"l{layer}_step{t}")
+    assert len(compared) == w.batch * w.n_kv_heads

@@ -72,3 +72,18 @@ def test_mixed_ranks_from_choices():
         seen_v |= set(rv.tolist())
     assert seen_k == {32, 48, 64, 96} and seen_v == {16, 32}
     assert np.array_equal(synth.ranks(w, 5)[0], synth.ranks(w, 5)[0])
+
+
+def test_32layer_ranks_cover_every_pair_in_mixed_layers():
+    """Every (r_k, r_v) pair of the 32-layer workload's choices occurs in a layer
+    whose KV heads have other pairs too (so each exact pair runs in a mixed-rank
+    decode), (32, 16) included."""
+    w = synth.WORKLOADS["llama31_8b_32layer"]
+    seen = set()
+    for layer in range(w.n_layers):
+        rk, rv = synth.ranks(w, layer)
+        pairs = set(zip(rk.tolist(), rv.tolist()))
+        if len(pairs) > 1:
+            seen |= pairs
+    assert (32, 16) in seen
+    assert seen == {(a, b) for a in w.rank_k_choices for b in w.rank_v_choices}
