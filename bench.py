@@ -243,7 +243,7 @@ def stream_ceiling(timer, nbytes, launches=12):
     bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
     sink = torch.zeros(65536, dtype=torch.int32, device="cuda")
     s = timer.stream.cuda_stream
-    best = None
+    best, sweep = None, []
     for grid in (1024, 2048, 4096, 8192):
         for unroll in (2, 4, 8):
             for nt in (False, True):
@@ -253,10 +253,12 @@ def stream_ceiling(timer, nbytes, launches=12):
                 fn(0)
                 ms = timer.total_ms(key, fn, launches) / launches
                 gbps = nbytes / (ms * 1e-3) / 1e9
+                sweep.append([grid, unroll, int(nt), round(gbps, 1)])
                 if best is None or gbps > best["gbps"]:
                     best = {"gbps": round(gbps, 1), "us_per_launch": round(ms * 1e3, 3), "bytes": nbytes,
                             "grid": grid, "block": 256, "unroll": unroll, "nontemporal": nt}
     del bufs
+    best["sweep"] = sweep
     return best
 
 
@@ -489,6 +491,7 @@ def run_layer(args, w):
     # splits per code stream: the workload's count per KV head, times the group size
     # with head groups (so the grid keeps its size); otherwise the library's choice
     S = w.n_splits * hg if (w.n_splits and not resid and not rope_base) else B.lrkv_decode_auto_splits(L0, n)
+    S = args.splits or S
     q = dev(np.stack([synth.queries(w, 0, 0, b) for b in range(w.batch)]))
     out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device="cuda")
     ws = B.workspace(L0, S)
@@ -771,6 +774,9 @@ def main():
                          "equal runs of whole blocks; every version holds the same basis, so the output "
                          "is that of one version (bf16 codes)")
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated (0: >= 1 GiB)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="context splits per code stream (single-layer workloads; 0: the workload's "
+                         "count, else the library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-ceiling", action="store_true")

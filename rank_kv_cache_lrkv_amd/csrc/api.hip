@@ -1,6 +1,7 @@
 // C entry points: argument checks on the host (before any HIP call), layout
 // offsets, then the launches.  No device memory is allocated here.
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -129,15 +130,49 @@ lrkv_status make_layer(const lrkv_layer *L, LayerArgs *A) {
 int32_t rvp_floats(const LayerArgs &A) { return ((A.rv_max + 3) / 4) * 4; }
 int32_t rec_floats(const LayerArgs &A) { return 4 + rvp_floats(A) + kD; }
 
+// code bytes per compressed token of latent group h (codes, scales, LowRAM
+// residual records): what one of its splits streams per token
+double token_bytes(const LayerArgs &A, int h) {
+  const HeadInfo &hd = A.heads[h];
+  if (A.lowram) return hd.rk * 2.0 + A.R * (kD * 2.0 + 4.0) / kBlock;
+  switch (A.dtype) {
+    case LRKV_F32: return (hd.rk + hd.rv) * 4.0;
+    case LRKV_BF16: return (hd.rk + hd.rv) * 2.0;
+    case LRKV_BF16_Q8: return (hd.rk + hd.rv) + 8.0;
+    default: return (hd.rk + hd.rv) * 0.5 + 8.0;
+  }
+}
+
+// S_h of every group for S splits of the widest group: in proportion to the
+// group's bytes per token, rounded, at least the basis versions (and 1)
+void group_splits(const LayerArgs &A, int32_t S, int32_t *nsplit) {
+  double wmax = 0.0;
+  for (int h = 0; h < A.n_lat; ++h) wmax = std::max(wmax, token_bytes(A, h));
+  for (int h = 0; h < A.n_lat; ++h) {
+    int64_t sh = std::llround(double(S) * token_bytes(A, h) / wmax);
+    sh = std::max<int64_t>(sh, A.n_versions);
+    sh = std::max<int64_t>(sh, 1);
+    nsplit[h] = int32_t(std::min<int64_t>(sh, S));
+  }
+}
+
 int32_t auto_splits(const LayerArgs &A, int32_t n_ctx) {
   const int64_t c = n_ctx - 1 - A.window;
   const int64_t nblk = c > 0 ? (c + LRKV_BLOCK - 1) / LRKV_BLOCK : 0;
-  const int64_t units = int64_t(A.batch) * A.n_lat;
-  // about as many workgroups as are resident at once on the 256 compute units
-  // (four per unit; three for the pre-RoPE and LowRAM kernels, whose LDS or
-  // registers allow three), at least four 32-slot blocks per split
-  const int64_t target = (A.rope || A.lowram) ? 768 : 1024;
-  int64_t s = (target + units - 1) / units;
+  // about as many workgroups as the launched kernel keeps resident at once on
+  // the device (its occupancy per compute unit times the compute units); without
+  // a device to ask, the figures of MI355X (256 compute units, four workgroups
+  // per unit, three for the pre-RoPE and LowRAM kernels).  The groups' splits
+  // follow their bytes per token, so the widest group's count is scaled by
+  // (widest bytes) / (mean bytes).  At least four 32-slot blocks per split.
+  const int per_cu = partials_blocks_per_cu(A), cus = device_cu_count();
+  const int64_t target = (per_cu > 0 && cus > 0) ? int64_t(per_cu) * cus : ((A.rope || A.lowram) ? 768 : 1024);
+  double wsum = 0.0, wmax = 0.0;
+  for (int h = 0; h < A.n_lat; ++h) {
+    wsum += token_bytes(A, h);
+    wmax = std::max(wmax, token_bytes(A, h));
+  }
+  int64_t s = int64_t(std::ceil(double(target) * wmax / (double(A.batch) * wsum) - 1e-9));
   const int64_t most = nblk / 4 > 1 ? nblk / 4 : 1;
   if (s > most) s = most;
   if (s < 1) s = 1;
@@ -178,6 +213,17 @@ lrkv_status make_decode(const lrkv_layer *L, const LayerArgs &A, int32_t n_ctx,
   std::memset(D, 0, sizeof(*D));
   D->n_ctx = n_ctx;
   D->n_splits = S;
+  group_splits(A, S, D->nsplit);
+  D->uniform = 1;
+  int32_t acc = 0;
+  for (int h = 0; h < A.n_lat; ++h) {
+    D->split0[h] = acc;
+    acc += D->nsplit[h];
+    D->uniform = D->uniform && D->nsplit[h] == S;
+  }
+  D->split0[A.n_lat] = acc;
+  D->row_items = acc;
+  D->items = acc * A.batch;
   D->rec = rec_floats(A);
   D->oa = 4 + rvp_floats(A);
   D->scale_log2 = sm_scale * kLog2e;

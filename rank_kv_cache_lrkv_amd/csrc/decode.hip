@@ -13,8 +13,10 @@
 // exponential is a hardware exp2.
 //
 // This file holds the float32-arithmetic stage 1 (used for float32 storage), the
-// combine, and the launchers; the bfloat16 stage 1 on the matrix cores is in
-// decode_mfma.hip.
+// combine (with or without basis versions), and the launchers; the bfloat16 stage
+// 1 on the matrix cores is in decode_mfma.hip.
+
+#include <algorithm>
 
 #include "decode_common.h"
 
@@ -28,10 +30,10 @@ namespace lrkv {
 template <typename T>
 __global__ __launch_bounds__(256) void k_partials_generic(LayerArgs L, DecodeArgs d) {
   __shared__ ChunkSmem sm;
-  const int S = d.n_splits;
-  const int split = blockIdx.x;
-  const int unit = blockIdx.y;
-  const int b = unit / L.n_kv, h = unit % L.n_kv;
+  const WorkItem wi = work_item(L, d);
+  const int S = wi.S, split = wi.split;
+  const int b = wi.b, h = wi.h;
+  const int unit = b * L.n_kv + h;
   const int g = L.group;
   const int W = L.window;
   const int tid = threadIdx.x;
@@ -95,41 +97,66 @@ __global__ __launch_bounds__(256) void k_partials_generic(LayerArgs L, DecodeArg
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2: one workgroup of 128 threads (t = the output features) per (query
-// head i, batch row b) merges that head's split records, with a single
-// round of loads: every term a thread needs (split maxima and denominators,
-// rank-space sums, anchor sums, its U_V column) is loaded at once from clamped
-// in-bounds indices and masked when used.  The threads form `groups` groups of
-// rv threads; group g merges splits g, g + groups, ... under its own max, then
-// the groups are merged under the common max M (finite: token 0 is an anchor
-// of every row, held by split 0).  The merged rank-space sum is up-projected
-// once with U_V, the anchor sums (on the first splits only) are added in the
-// 128-dim space, and the total is normalised.
-// Loads go through buffer resources (32-bit offsets).
+// Stage 2: one workgroup of 128 threads per (query head i, batch row b), thread t
+// = output feature t, merges the S_h split records of the head's group.
+//
+// Everything it reads is cut into 16-byte pieces of three kinds: the splits'
+// rank-space sums (rv / 4 pieces per split), the anchor sums of the splits that
+// hold this KV head's anchor rows (32 per split), and the U_V rows (128
+// elements each, one row per (version, column) pair).  Each thread takes P
+// pieces of every kind (P a compile-time instance, chosen on the host from the
+// call's sizes), all loaded in one round before any is used, every load
+// unconditional from a clamped in-range index (threads whose index was clamped
+// write the same data to the same LDS slot as the thread they duplicate);
+// pieces past a round's capacity are taken in further rounds.  Then:
+//  - every wave finds the common max M (finite: token 0 is an anchor of every
+//    row) from the split headers in LDS, and the denominator L;
+//  - thread e < V rv sums 2^(m_s - M) o~_s[c] over the splits of version
+//    v = e / rv, c = e % rv, in index order (the splits of a version are
+//    consecutive; each record carries its version);
+//  - thread t sums 2^(m_s - M) o_A,s[t] over the anchor splits in index order,
+//    up-projects the merged sums with column t of every U_V row, adds and
+//    divides by L.
+// U_V is U_V(version)^T of the head's KV head (rows of hg * 128 elements, the
+// slice at 128 j), or for LowRAM layers the row's predictor M (rank_k rows of
+// 128).  All orders are fixed, so a call is bitwise reproducible.
 // ---------------------------------------------------------------------------
-struct CombineSmem {
-  float m[128 / 16], l[128 / 16];  // per group of rv threads
-  float o[128];                    // per thread: its group's rank-space sum
-  float ot[128];                   // the merged rank-space sum
+constexpr int kCT = 128;  // threads of a combine workgroup
+
+// per-launch geometry of the combine (host-computed): slots per thread, round
+// capacities and the LDS layout (byte offsets)
+struct CombineArgs {
+  int P;                  // pieces of each kind per thread and round
+  int so, sa;             // splits of rank-space sums / anchor sums per round
+  int urows;              // U_V rows per round
+  int m, l, v, o, a, ov, u, bytes;
 };
 
-template <typename T>
-__global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, float *out) {
-  constexpr int UPRE = 32;  // U_V columns loaded up front (the rest, if any, later)
-  constexpr int PRE = 16;   // terms per thread loaded up front (the rest, if any, later)
-  __shared__ CombineSmem cs;
-  const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+template <typename T, int P>
+__global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, CombineArgs g, float *out) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  constexpr int kEP = 16 / sizeof(T);          // U_V elements per 16-byte piece
+  constexpr int kPPR = kD / kEP;               // pieces per U_V row
+  extern __shared__ __align__(16) char lds[];
+  const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x, lane = t & 63;
   const int kvh = i / L.group;                 // KV head; its latent group and slice
   const int h = kvh / L.hg, j = kvh % L.hg;
   const HeadInfo hd = L.heads[h];
   const int rv = hd.rv;
-  const int S = d.n_splits;
+  const int S = d.nsplit[h], V = L.n_versions;
+  float *sm = reinterpret_cast<float *>(lds + g.m);
+  float *sl = reinterpret_cast<float *>(lds + g.l);
+  int *sv = reinterpret_cast<int *>(lds + g.v);
+  float *so = reinterpret_cast<float *>(lds + g.o);   // [split of the round][rv]
+  float *sa = reinterpret_cast<float *>(lds + g.a);   // [anchor split of the round][128]
+  float *sov = reinterpret_cast<float *>(lds + g.ov); // [version][rv]
+  T *su = reinterpret_cast<T *>(lds + g.u);           // [row of the round][128]
   const int64_t qi = int64_t(b) * L.n_q + i;
-  const float *rc = split_record(d, qi, 0);
   const __amdgpu_buffer_rsrc_t rr =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(rc), 0, S * d.rec * 4, kBufferWord3);
-  auto rec = [&](int s, int f) {  // float f of split s's record
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, (s * d.rec + f) * 4, 0, 0));
+      __builtin_amdgcn_make_buffer_rsrc(split_record(d, qi, 0), 0, S * d.rec * 4, kBufferWord3);
+  auto rec4 = [&](int s, int f) {  // floats f .. f + 3 of split s's record
+    return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rr, (s * d.rec + f) * 4, 0, 0));
   };
   const int a1 = min(row_ctx(d, b), 1 + L.window);  // anchor rows per KV head
   const int per = anchor_rows_per_split(a1 * L.hg, S);
@@ -138,223 +165,208 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, floa
   // every split holds residual sums there
   const int s_a0 = L.lowram ? 0 : (j * a1) / per;
   const int s_a1 = L.lowram ? S : min(S, ((j + 1) * a1 + per - 1) / per);
-  // U_V^T rows (hg * 128 elements, this KV head's slice at j * 128), or for LowRAM
-  // the row's predictor M (rank_k rows of 128): element (c, t) of the slice is
-  // column c of output feature t
+  const int na = s_a1 - s_a0;              // >= 1
   const int urow = L.hg * kD;
+  const int rows = V * rv;                 // U_V rows: (version, column) pairs
+  // U^T row e = (version e / rv, column e % rv) of this KV head's slice, through a
+  // buffer resource over every version's rows
   const T *ubase = L.lowram ? static_cast<const T *>(L.pred) + hd.pred + int64_t(b) * rv * kD
                             : static_cast<const T *>(L.bases) + hd.u_v;
-  const __amdgpu_buffer_rsrc_t ur =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(ubase), 0, rv * urow * int(sizeof(T)), kBufferWord3);
-  auto uv = [&](int c) { return buffer_elem<T>(ur, (c * urow + j * kD + t) * int(sizeof(T))); };
-  const int groups = 128 / rv;
-  const int col = t % rv, grp = t / rv;
-  const int grp_c = min(grp, groups - 1);
-
-  float upre[UPRE];
-  float2 ml[PRE];
-  float ov[PRE], ma[PRE], av[PRE];
-  float mg = kNegInf, lg = 0.f, og = 0.f;
+  const int vstride = L.lowram ? 0 : int(L.version_elems);
+  const __amdgpu_buffer_rsrc_t ur = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T *>(ubase), 0, ((V - 1) * vstride + rv * urow) * int(sizeof(T)), kBufferWord3);
+  // piece k of this thread: sums piece pc of split s_t + s_step k (npc divides
+  // 128); anchor piece ac of anchor split a_t + 4 k; U_V piece uc of row
+  // u_t + (128 / kPPR) k
+  const int npc = rv >> 2, pc = t % npc, s_t = t / npc, s_step = kCT / npc;
+  const int ac = t & 31, a_t = t >> 5;
+  const int uc = t % kPPR, u_t = t / kPPR;
+  const int sr = min(S, g.so), ar = min(na, g.sa), ur_rows = min(rows, g.urows);
+  f4 op[P], ap[P];
+  u4 up[P];
+  auto load_o = [&](int r0, int nr) {
 #pragma unroll
-  for (int c = 0; c < UPRE; ++c) upre[c] = uv(min(c, rv - 1));
+    for (int k = 0; k < P; ++k) op[k] = rec4(r0 + min(s_t + s_step * k, nr - 1), 4 + 4 * pc);
+  };
+  auto store_o = [&](int nr) {
 #pragma unroll
-  for (int k = 0; k < PRE; ++k) {
-    const int s = min(grp_c + k * groups, S - 1);
-    ml[k] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rr, s * d.rec * 4, 0, 0));
-    ov[k] = rec(s, 4 + col);
-    const int sk = min(s_a0 + k, s_a1 - 1);
-    ma[k] = rec(sk, 0);
-    av[k] = rec(sk, d.oa + t);
-  }
-  // this group's splits under the group's own max
+    for (int k = 0; k < P; ++k) *reinterpret_cast<f4 *>(&so[min(s_t + s_step * k, nr - 1) * rv + 4 * pc]) = op[k];
+  };
+  auto load_a = [&](int r0, int nr) {
 #pragma unroll
-  for (int k = 0; k < PRE; ++k)
-    if (grp_c + k * groups < S) mg = fmaxf(mg, ml[k].x);
+    for (int k = 0; k < P; ++k) ap[k] = rec4(s_a0 + r0 + min(a_t + 4 * k, nr - 1), d.oa + 4 * ac);
+  };
+  auto store_a = [&](int nr) {
 #pragma unroll
-  for (int k = 0; k < PRE; ++k) {
-    if (grp_c + k * groups < S && ml[k].x != kNegInf) {  // empty splits hold nothing
-      const float w = fast_exp2(ml[k].x - mg);
-      lg = fmaf(w, ml[k].y, lg);
-      og = fmaf(w, ov[k], og);
+    for (int k = 0; k < P; ++k) *reinterpret_cast<f4 *>(&sa[min(a_t + 4 * k, nr - 1) * kD + 4 * ac]) = ap[k];
+  };
+  auto load_u = [&](int e0, int nr) {
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      const int e = e0 + min(u_t + (kCT / kPPR) * k, nr - 1);
+      const int v = e / rv, c = e - v * rv;
+      up[k] = __builtin_amdgcn_raw_buffer_load_b128(ur, (v * vstride + c * urow + j * kD + uc * kEP) * int(sizeof(T)),
+                                                    0, 0);
     }
-  }
-  // more splits than loaded up front: 8 at a time, all loads issued before the merge
-  for (int s0 = grp_c + PRE * groups; s0 < S; s0 += 8 * groups) {
-    float2 mlx[8];
-    float ovx[8];
+  };
+  auto store_u = [&](int nr) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int s = min(s0 + u * groups, S - 1);
-      mlx[u] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rr, s * d.rec * 4, 0, 0));
-      ovx[u] = rec(s, 4 + col);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float ms = mlx[u].x;
-      if (s0 + u * groups >= S || ms == kNegInf) continue;
-      const float mn = fmaxf(mg, ms);
-      const float a0 = fast_exp2(mg - mn), a1 = fast_exp2(ms - mn);  // mg = -inf gives a0 = 0
-      lg = fmaf(a1, mlx[u].y, lg * a0);
-      og = fmaf(a1, ovx[u], og * a0);
-      mg = mn;
-    }
-  }
-  if (grp < groups) {
-    cs.o[t] = og;
-    if (col == 0) {
-      cs.m[grp] = mg;
-      cs.l[grp] = lg;
-    }
-  }
-  __syncthreads();
+    for (int k = 0; k < P; ++k)
+      *reinterpret_cast<u4 *>(&su[(min(u_t + (kCT / kPPR) * k, nr - 1) * kPPR + uc) * kEP]) = up[k];
+  };
 
-  float M = kNegInf, Ltot = 0.f, oa = 0.f;
-  for (int g = 0; g < groups; ++g) M = fmaxf(M, cs.m[g]);
-  for (int g = 0; g < groups; ++g)
-    if (cs.m[g] != kNegInf) Ltot = fmaf(fast_exp2(cs.m[g] - M), cs.l[g], Ltot);
-  if (t < rv) {
-    float o = 0.f;
-    for (int g = 0; g < groups; ++g)
-      if (cs.m[g] != kNegInf) o = fmaf(fast_exp2(cs.m[g] - M), cs.o[g * rv + t], o);
-    cs.ot[t] = o;
+  // ---- one round of loads, then everything to LDS
+  const f4 hdr = rec4(min(t, S - 1), 0);
+  load_o(0, sr);
+  load_u(0, ur_rows);
+  load_a(0, ar);
+  __asm__ volatile("" ::: "memory");  // the loads stay ahead of every store below
+  sm[min(t, S - 1)] = hdr.x;
+  sl[min(t, S - 1)] = hdr.y;
+  sv[min(t, S - 1)] = min(max(int(hdr.z), 0), V - 1);
+  for (int s = t + kCT; s < S; s += kCT) {  // more than 128 splits
+    const f4 x = rec4(s, 0);
+    sm[s] = x.x;
+    sl[s] = x.y;
+    sv[s] = min(max(int(x.z), 0), V - 1);
   }
-  // anchor sums of output feature t (a split without rows of this head has m = -inf: weight 0)
-#pragma unroll
-  for (int k = 0; k < PRE; ++k)
-    if (s_a0 + k < s_a1 && ma[k] != kNegInf) oa = fmaf(fast_exp2(ma[k] - M), av[k], oa);
-  for (int s0 = s_a0 + PRE; s0 < s_a1; s0 += 8) {  // 8 at a time, loads first
-    float mx[8], ax[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int s = min(s0 + u, s_a1 - 1);
-      mx[u] = rec(s, 0);
-      ax[u] = rec(s, d.oa + t);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (s0 + u < s_a1 && mx[u] != kNegInf) oa = fmaf(fast_exp2(mx[u] - M), ax[u], oa);
-  }
-  __syncthreads();
-
-  float y = 0.f;
-#pragma unroll
-  for (int c = 0; c < UPRE; ++c) y = fmaf(upre[c], c < rv ? cs.ot[c] : 0.f, y);
-  for (int c = UPRE; c < rv; ++c) y = fmaf(uv(c), cs.ot[c], y);
-  out[qi * kD + t] = (y + oa) / Ltot;
-}
-
-// ---------------------------------------------------------------------------
-// Stage 2 with basis versions (codes made under several bases, OjaKV): each
-// version's rank-space sum is merged from that version's splits and
-// up-projected with that version's U_V; the rest is as in k_combine.  One
-// workgroup of 128 threads per (query head, batch row), thread t = output
-// feature t.  The splits' maxima, sums and versions (each record carries its
-// split's version) are read once into LDS (a thread per split); every later loop runs over LDS or issues its record
-// loads eight at a time ahead of the arithmetic.  Sums run split by split in
-// index order, as the records are laid out.
-// ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(128) void k_combine_versions(LayerArgs L, DecodeArgs d, float *out) {
-  __shared__ float sm[LRKV_MAX_SPLITS], sl[LRKV_MAX_SPLITS];  // split maxima, sums
-  __shared__ int sv[LRKV_MAX_SPLITS];                         // split versions
-  __shared__ float sot[LRKV_MAX_VERSIONS][128];               // per-version rank-space sums
-  const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  const int kvh = i / L.group;
-  const int h = kvh / L.hg, j = kvh % L.hg;
-  const HeadInfo hd = L.heads[h];
-  const int rv = hd.rv;
-  const int S = d.n_splits, V = L.n_versions;
-  const int64_t qi = int64_t(b) * L.n_q + i;
-  const int n = row_ctx(d, b);
-  const int a1 = min(n, 1 + L.window);  // anchor rows per KV head
-  const int per = anchor_rows_per_split(a1 * L.hg, S);
-  const int s_a0 = (j * a1) / per, s_a1 = min(S, ((j + 1) * a1 + per - 1) / per);  // as in k_combine
-
-  // the anchor sums of output feature t from the first 8 splits holding this KV
-  // head's anchor rows, requested before anything else (as k_combine does)
-  float ax0[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) ax0[u] = split_record(d, qi, min(s_a0 + u, s_a1 - 1))[d.oa + t];
-  for (int s = t; s < S; s += blockDim.x) {  // m, l and the version the partials kernel wrote
-    const float4 r = *reinterpret_cast<const float4 *>(split_record(d, qi, s));
-    sm[s] = r.x;
-    sl[s] = r.y;
-    sv[s] = min(max(int(r.z), 0), V - 1);
-  }
-  for (int e = t; e < V * kD; e += blockDim.x) sot[e / kD][e % kD] = 0.f;
+  store_o(sr);
+  store_u(ur_rows);
+  store_a(ar);
   __syncthreads();
 
   float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, sm[s]);  // finite: token 0 is an anchor
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, sm[s]);
+  M = wave_max(M);
+  auto wgt = [&](int s) {  // a split that saw nothing (m = -inf) weighs 0
+    const float m = sm[s];
+    return m == kNegInf ? 0.f : fast_exp2(m - M);
+  };
   float Ltot = 0.f;
-  for (int s = 0; s < S; ++s)
-    if (sm[s] != kNegInf) Ltot = fmaf(fast_exp2(sm[s] - M), sl[s], Ltot);
-  // each version's merged rank-space sum (the splits of a version are consecutive)
-  if (t < rv) {
-    float o = 0.f;
-    int cur = sv[0];
-    for (int s0 = 0; s0 < S; s0 += 8) {
-      float x[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = split_record(d, qi, min(s0 + u, S - 1))[4 + t];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int s = s0 + u;
-        if (s >= S) break;
-        if (sv[s] != cur) {
-          sot[cur][t] = o;
-          o = 0.f;
-          cur = sv[s];
-        }
-        if (sm[s] != kNegInf) o = fmaf(fast_exp2(sm[s] - M), x[u], o);
-      }
+  for (int s = lane; s < S; s += 64) Ltot = fmaf(wgt(s), sl[s], Ltot);
+  Ltot = wave_sum(Ltot);
+
+  // ---- merged rank-space sums, round by round of sr splits
+  for (int r0 = 0; r0 < S; r0 += sr) {
+    const int nr = min(sr, S - r0);
+    if (r0 > 0) {
+      __syncthreads();  // the previous round is summed
+      load_o(r0, nr);
+      __asm__ volatile("" ::: "memory");
+      store_o(nr);
+      __syncthreads();
     }
-    sot[cur][t] = o;
-  }
-  __syncthreads();
-  float y = 0.f;
-  for (int v = 0; v < V; ++v) {
-    const T *uvt = static_cast<const T *>(L.bases) + v * L.version_elems + hd.u_v;  // U_V^T rows
+    for (int e = t; e < rows; e += kCT) {
+      const int v = e / rv, c = e - v * rv;
+      float a = r0 > 0 ? sov[e] : 0.f;
+      if (V == 1) {
 #pragma unroll 8
-    for (int cc = 0; cc < rv; ++cc) y = fmaf(to_f32(uvt[cc * L.hg * kD + j * kD + t]), sot[v][cc], y);
-  }
-  float oa = 0.f;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int s = s_a0 + u;
-    if (s < s_a1 && sm[s] != kNegInf) oa = fmaf(fast_exp2(sm[s] - M), ax0[u], oa);
-  }
-  for (int s0 = s_a0 + 8; s0 < s_a1; s0 += 8) {  // more anchor splits: 8 at a time, loads first
-    float ax[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) ax[u] = split_record(d, qi, min(s0 + u, s_a1 - 1))[d.oa + t];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int s = s0 + u;
-      if (s < s_a1 && sm[s] != kNegInf) oa = fmaf(fast_exp2(sm[s] - M), ax[u], oa);
+        for (int s = 0; s < nr; ++s) a = fmaf(wgt(r0 + s), so[s * rv + c], a);
+      } else {
+        for (int s = 0; s < nr; ++s) a = fmaf(sv[r0 + s] == v ? wgt(r0 + s) : 0.f, so[s * rv + c], a);
+      }
+      sov[e] = a;
     }
+  }
+  // ---- anchor sums of feature t, round by round of ar anchor splits
+  float oa = 0.f;
+  for (int r0 = 0; r0 < na; r0 += ar) {
+    const int nr = min(ar, na - r0);
+    if (r0 > 0) {
+      __syncthreads();
+      load_a(r0, nr);
+      __asm__ volatile("" ::: "memory");
+      store_a(nr);
+      __syncthreads();
+    }
+    for (int s = 0; s < nr; ++s) {
+      const float w = wgt(s_a0 + r0 + s);
+      oa = w != 0.f ? fmaf(w, sa[s * kD + t], oa) : oa;
+    }
+  }
+  __syncthreads();  // sov complete
+
+  // ---- up-projection: column t of every U_V row against the merged sums
+  float y = 0.f;
+  for (int e0 = 0; e0 < rows; e0 += ur_rows) {
+    const int nr = min(ur_rows, rows - e0);
+    if (e0 > 0) {
+      __syncthreads();
+      load_u(e0, nr);
+      __asm__ volatile("" ::: "memory");
+      store_u(nr);
+      __syncthreads();
+    }
+#pragma unroll 8
+    for (int e = 0; e < nr; ++e) y = fmaf(to_f32(su[e * kD + t]), sov[e0 + e], y);
   }
   out[qi * kD + t] = (y + oa) / Ltot;
 }
 
-// ---------------------------------------------------------------------------
-// launchers
-// ---------------------------------------------------------------------------
+// the combine geometry of a call: P from the largest piece count of any kind
+// (rounded up to 2, 4, 8 or 16), round capacities, LDS layout
+static CombineArgs combine_args(const LayerArgs &L, const DecodeArgs &d) {
+  const int esize = L.dtype == LRKV_F32 ? 4 : 2;
+  const int S = d.n_splits, rv = L.rv_max, V = L.n_versions;
+  const int rows = V * rv;
+  int na = S;  // anchor splits of one KV head (all splits for LowRAM layers)
+  if (!L.lowram) {
+    const int a1 = d.n_ctx < 1 + L.window ? d.n_ctx : 1 + L.window;
+    na = 0;
+    for (int h = 0; h < L.n_lat; ++h) {
+      const int Sh = d.nsplit[h], per = anchor_rows_per_split(a1 * L.hg, Sh);
+      for (int jj = 0; jj < L.hg; ++jj) {
+        const int s0 = (jj * a1) / per, s1 = std::min(Sh, ((jj + 1) * a1 + per - 1) / per);
+        na = std::max(na, s1 - s0);
+      }
+    }
+    na = std::max(na, 1);
+  }
+  const int need = std::max({(S * (rv / 4) + kCT - 1) / kCT, (rows * (kD * esize / 16) + kCT - 1) / kCT,
+                             (na * 32 + kCT - 1) / kCT});
+  CombineArgs g{};
+  g.P = need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
+  g.so = g.P * kCT / (rv / 4);
+  g.sa = g.P * kCT / 32;
+  g.urows = g.P * kCT / (kD * esize / 16);
+  const int so_n = std::min(S, g.so), sa_n = std::min(na, g.sa), u_n = std::min(rows, g.urows);
+  g.m = 0;
+  g.l = g.m + 4 * S;
+  g.v = g.l + 4 * S;
+  g.o = (g.v + 4 * S + 15) / 16 * 16;
+  g.a = g.o + 4 * so_n * rv;
+  g.ov = g.a + 4 * sa_n * kD;
+  g.u = (g.ov + 4 * rows + 15) / 16 * 16;
+  g.bytes = g.u + u_n * kD * esize;
+  return g;
+}
+
+int generic_blocks_per_cu() { return kernel_blocks_per_cu(reinterpret_cast<const void *>(k_partials_generic<float>)); }
+
 hipError_t launch_decode_partials(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
   if (L.dtype != LRKV_F32) return launch_partials_mfma(L, d, s);
-  dim3 grid(d.n_splits, L.batch * L.n_kv);
-  hipLaunchKernelGGL(k_partials_generic<float>, grid, dim3(256), 0, s, L, d);
+  hipLaunchKernelGGL(k_partials_generic<float>, dim3(d.row_items, L.batch), dim3(256), 0, s, L, d);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_combine(const LayerArgs &L, const DecodeArgs &d, float *out, hipStream_t s) {
+template <typename T>
+static void launch_combine_t(const LayerArgs &L, const DecodeArgs &d, const CombineArgs &g, float *out,
+                             hipStream_t s) {
   dim3 grid(L.n_q, L.batch);
-  if (L.n_versions > 1)  // float32 layers have one version
-    hipLaunchKernelGGL(k_combine_versions<bf16_t>, grid, dim3(kD), 0, s, L, d, out);
-  else if (L.dtype == LRKV_F32)
-    hipLaunchKernelGGL(k_combine<float>, grid, dim3(kD), 0, s, L, d, out);
+  switch (g.P) {
+    case 2: hipLaunchKernelGGL((k_combine<T, 2>), grid, dim3(kCT), g.bytes, s, L, d, g, out); break;
+    case 4: hipLaunchKernelGGL((k_combine<T, 4>), grid, dim3(kCT), g.bytes, s, L, d, g, out); break;
+    case 8: hipLaunchKernelGGL((k_combine<T, 8>), grid, dim3(kCT), g.bytes, s, L, d, g, out); break;
+    default: hipLaunchKernelGGL((k_combine<T, 16>), grid, dim3(kCT), g.bytes, s, L, d, g, out); break;
+  }
+}
+
+hipError_t launch_decode_combine(const LayerArgs &L, const DecodeArgs &d, float *out, hipStream_t s) {
+  const CombineArgs g = combine_args(L, d);
+  if (L.dtype == LRKV_F32)  // float32 layers have one version
+    launch_combine_t<float>(L, d, g, out, s);
   else
-    hipLaunchKernelGGL(k_combine<bf16_t>, grid, dim3(kD), 0, s, L, d, out);
+    launch_combine_t<bf16_t>(L, d, g, out, s);
   return hipGetLastError();
 }
 

@@ -35,6 +35,33 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// The work item of stage-1 workgroup (blockIdx.x, blockIdx.y) of a
+// (row_items, batch) grid: batch row b, latent group h, split s of its S_h.
+// Workgroup i of a launch runs on XCD i % 8, each XCD with its own L2: when the
+// items divide by 8, XCD x takes the x-th eighth of the item list, so the splits
+// of a (row, group) unit -- which share its query, U_K and anchor rows -- land on
+// one XCD (a unit may straddle two eighths).
+struct WorkItem {
+  int b, h, split, S;
+};
+__device__ __forceinline__ WorkItem work_item(const LayerArgs &L, const DecodeArgs &d) {
+  const int i = blockIdx.x + d.row_items * blockIdx.y;
+  const int j = (d.items & 7) == 0 ? (i & 7) * (d.items >> 3) + (i >> 3) : i;
+  WorkItem w;
+  w.b = j / d.row_items;
+  const int r = j - w.b * d.row_items;
+  int h = 0;
+  if (d.uniform) {
+    h = r / d.n_splits;
+  } else {
+    while (h + 1 < L.n_lat && d.split0[h + 1] <= r) ++h;
+  }
+  w.h = h;
+  w.split = r - d.split0[h];
+  w.S = d.nsplit[h];
+  return w;
+}
+
 // record of query head qi = b * n_q + i for split s
 __device__ __forceinline__ float *split_record(const DecodeArgs &d, int64_t qi, int split) {
   return d.ws + (qi * d.n_splits + split) * d.rec;
@@ -43,7 +70,7 @@ __device__ __forceinline__ float *split_record(const DecodeArgs &d, int64_t qi, 
 // anchor rows [lo, hi) of split s out of a anchors: consecutive runs of at
 // least 16 rows on the first splits, so most splits carry no anchors at all
 constexpr int kMinAnchorRows = 16;
-__device__ __forceinline__ int anchor_rows_per_split(int a, int S) {
+__host__ __device__ __forceinline__ int anchor_rows_per_split(int a, int S) {
   const int even = (a + S - 1) / S;
   return even > kMinAnchorRows ? even : kMinAnchorRows;
 }

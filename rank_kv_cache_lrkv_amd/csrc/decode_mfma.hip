@@ -30,6 +30,9 @@
 // q~ = U_K^T q, and wave 0 folds them in before its code blocks while the other
 // waves already stream.
 
+#include <map>
+#include <mutex>
+
 #include "decode_common.h"
 #include "mfma_util.h"
 
@@ -197,20 +200,12 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
   bf16_t *const su = sm.w.r.su;
   auto &rq = sm.w.r.rq;
 
-  const int S = d.n_splits;
-  // Workgroup i of the launch runs on XCD i % 8, and each XCD has its own L2:
-  // when the units divide evenly, each XCD takes whole (row, head) units, so the
-  // query, U_K and anchor rows a unit's splits read are fetched into one L2.
-  int split = blockIdx.x, unit = blockIdx.y;
-  if (gridDim.y % 8 == 0) {
-    const int i = blockIdx.x + S * blockIdx.y;
-    const int k = i >> 3;
-    unit = (i & 7) * (gridDim.y >> 3) + k / S;
-    split = k % S;
-  }
-  // unit = (batch row b, latent group h); its G query heads are those of the hg
-  // KV heads h hg .. h hg + hg - 1 (GK each), which share the group's codes
-  const int b = unit / L.n_lat, h = unit % L.n_lat;
+  // (batch row b, latent group h) and split `split` of the group's S; the G
+  // query heads are those of the hg KV heads h hg .. h hg + hg - 1 (GK each),
+  // which share the group's codes
+  const WorkItem wi = work_item(L, d);
+  const int S = wi.S, split = wi.split;
+  const int b = wi.b, h = wi.h;
   const int GK = L.group, G = GK * L.hg;
   const int W = L.window;
   const HeadInfo hd = L.heads[h];
@@ -288,6 +283,11 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
     esres = __builtin_amdgcn_make_buffer_rsrc(L.rslot + e0, 0, (L.cap / kBlock) * L.R * 4, kBufferWord3);
   }
   const int kblk_bytes = kBlock * rk * CB / 8, vblk_bytes = kBlock * rv * CB / 8;
+  // Code blocks (and their scales and residual rows) are read exactly once per
+  // call: their loads carry the streaming (non-temporal) cache policy, which
+  // keeps them from displacing the query, U_K and anchor lines the splits of a
+  // unit share in L2, and measurably raises the read rate on this part.
+  constexpr int kStream = 2;
   int koff[2][NKC];
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
@@ -310,35 +310,35 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
-          if constexpr (CB == 8) r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b64(kres, koff[h2][kc], ks, 0);
-          else r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b32(kres, koff[h2][kc], ks, 0);
+          if constexpr (CB == 8) r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b64(kres, koff[h2][kc], ks, kStream);
+          else r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b32(kres, koff[h2][kc], ks, kStream);
         }
 #pragma unroll
       for (int ni = 0; ni < NVC; ++ni) {
-        if constexpr (CB == 8) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b64(vres, voff[ni], vs, 0);
-        else r.v[ni] = __builtin_amdgcn_raw_buffer_load_b32(vres, voff[ni], vs, 0);
+        if constexpr (CB == 8) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b64(vres, voff[ni], vs, kStream);
+        else r.v[ni] = __builtin_amdgcn_raw_buffer_load_b32(vres, voff[ni], vs, kStream);
       }
       const int ss = __builtin_amdgcn_readfirstlane(blk * kBlock * 4);
-      r.sk = __builtin_amdgcn_raw_buffer_load_b32(skres, soff, ss, 0);
-      r.sv = __builtin_amdgcn_raw_buffer_load_b32(svres, soff, ss, 0);
+      r.sk = __builtin_amdgcn_raw_buffer_load_b32(skres, soff, ss, kStream);
+      r.sv = __builtin_amdgcn_raw_buffer_load_b32(svres, soff, ss, kStream);
     } else {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc)
-          r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b128(kres, koff[h2][kc], ks, 0);
+          r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b128(kres, koff[h2][kc], ks, kStream);
       if constexpr (LR == 0) {
 #pragma unroll
-        for (int ni = 0; ni < NVC; ++ni) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b128(vres, voff[ni], vs, 0);
+        for (int ni = 0; ni < NVC; ++ni) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b128(vres, voff[ni], vs, kStream);
       }
     }
     if constexpr (LR > 0) {
       const int es = __builtin_amdgcn_readfirstlane(blk * L.R * kD * 2);
 #pragma unroll
       for (int i = 0; i < LRR; ++i)
-        if (i < L.R) r.e[i] = __builtin_amdgcn_raw_buffer_load_b32(eres, lane * 4 + i * kD * 2, es, 0);
+        if (i < L.R) r.e[i] = __builtin_amdgcn_raw_buffer_load_b32(eres, lane * 4 + i * kD * 2, es, kStream);
       r.es = __builtin_amdgcn_raw_buffer_load_b32(esres, min(lane, L.R - 1) * 4,
-                                                  __builtin_amdgcn_readfirstlane(blk * L.R * 4), 0);
+                                                  __builtin_amdgcn_readfirstlane(blk * L.R * 4), kStream);
     }
   };
 
@@ -1002,36 +1002,77 @@ __global__ __launch_bounds__(256, 3) void k_partials_rope(LayerArgs L, DecodeArg
   partials_body<RKMAX, RVMAX, false, 16, 0, 0, true>(L, d);
 }
 
+// ---------------------------------------------------------------------------
+// instance selection (the same choice for the launch and for the occupancy the
+// host sizes grids by)
+// ---------------------------------------------------------------------------
+typedef void (*PartialsFn)(LayerArgs, DecodeArgs);
+
 template <int RKMAX, int RVMAX, bool EXACT>
-static void launch_cb(const LayerArgs &L, const DecodeArgs &d, dim3 grid, hipStream_t s) {
-  if (L.dtype == LRKV_BF16_Q8)
-    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, EXACT, 8>), grid, dim3(256), 0, s, L, d);
-  else if (L.dtype == LRKV_BF16_Q4)
-    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, EXACT, 4>), grid, dim3(256), 0, s, L, d);
-  else
-    hipLaunchKernelGGL((k_partials_mfma<RKMAX, RVMAX, EXACT, 16>), grid, dim3(256), 0, s, L, d);
+static PartialsFn pick_cb(const LayerArgs &L) {
+  if (L.dtype == LRKV_BF16_Q8) return k_partials_mfma<RKMAX, RVMAX, EXACT, 8>;
+  if (L.dtype == LRKV_BF16_Q4) return k_partials_mfma<RKMAX, RVMAX, EXACT, 4>;
+  return k_partials_mfma<RKMAX, RVMAX, EXACT, 16>;
 }
 
 template <int RKMAX, int RVMAX>
-static hipError_t launch_rv(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
+static PartialsFn pick_rv(const LayerArgs &L) {
   bool exact = true;
   for (int h = 0; h < L.n_lat; ++h) exact = exact && L.heads[h].rk == RKMAX && L.heads[h].rv == RVMAX;
-  dim3 grid(d.n_splits, L.batch * L.n_lat);
-  if (exact) launch_cb<RKMAX, RVMAX, true>(L, d, grid, s);
-  else launch_cb<RKMAX, RVMAX, false>(L, d, grid, s);
-  return hipGetLastError();
+  return exact ? pick_cb<RKMAX, RVMAX, true>(L) : pick_cb<RKMAX, RVMAX, false>(L);
 }
 
 template <int RKMAX>
-static hipError_t launch_rk(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
-  if (L.rv_max <= 16) return launch_rv<RKMAX, 16>(L, d, s);
-  if (L.rv_max <= 32) return launch_rv<RKMAX, 32>(L, d, s);
-  if (L.rv_max <= 64) return launch_rv<RKMAX, 64>(L, d, s);
-  return launch_rv<RKMAX, 128>(L, d, s);
+static PartialsFn pick_rk(const LayerArgs &L) {
+  if (L.rv_max <= 16) return pick_rv<RKMAX, 16>(L);
+  if (L.rv_max <= 32) return pick_rv<RKMAX, 32>(L);
+  if (L.rv_max <= 64) return pick_rv<RKMAX, 64>(L);
+  return pick_rv<RKMAX, 128>(L);
 }
 
-// compute units of the current device (cached per device)
-static int cu_count() {
+// LowRAM layers: value sums over the key codes (RVMAX = RKMAX), bf16 codes; ranks
+// are read per head (no exact-rank instances); register arrays sized for at most
+// 4 query heads per KV head and 4 residual entries where that suffices
+template <int RKMAX>
+static PartialsFn pick_lr(const LayerArgs &L) {
+  const bool g4 = L.group <= 4, r4 = L.R <= 4;
+  if (g4 && r4) return k_partials_mfma<RKMAX, RKMAX, false, 16, 4, 4>;
+  if (g4) return k_partials_mfma<RKMAX, RKMAX, false, 16, 4, 8>;
+  if (r4) return k_partials_mfma<RKMAX, RKMAX, false, 16, 16, 4>;
+  return k_partials_mfma<RKMAX, RKMAX, false, 16, 16, 8>;
+}
+
+// keys compressed before RoPE (bf16 codes, per-head ranks read at run time)
+template <int RKMAX>
+static PartialsFn pick_rp(const LayerArgs &L) {
+  if (L.rv_max <= 16) return k_partials_rope<RKMAX, 16>;
+  if (L.rv_max <= 32) return k_partials_rope<RKMAX, 32>;
+  if (L.rv_max <= 64) return k_partials_rope<RKMAX, 64>;
+  return k_partials_rope<RKMAX, 128>;
+}
+
+static PartialsFn pick_partials(const LayerArgs &L) {
+  int rk_max = 0;
+  for (int h = 0; h < L.n_lat; ++h) rk_max = L.heads[h].rk > rk_max ? L.heads[h].rk : rk_max;
+  if (L.rope) {
+    if (rk_max <= 32) return pick_rp<32>(L);
+    if (rk_max <= 64) return pick_rp<64>(L);
+    if (rk_max <= 96) return pick_rp<96>(L);
+    return pick_rp<128>(L);
+  }
+  if (L.lowram) {
+    if (rk_max <= 32) return pick_lr<32>(L);
+    if (rk_max <= 64) return pick_lr<64>(L);
+    if (rk_max <= 96) return pick_lr<96>(L);
+    return pick_lr<128>(L);
+  }
+  if (rk_max <= 32) return pick_rk<32>(L);
+  if (rk_max <= 64) return pick_rk<64>(L);
+  if (rk_max <= 96) return pick_rk<96>(L);
+  return pick_rk<128>(L);
+}
+
+int device_cu_count() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -1043,53 +1084,40 @@ static int cu_count() {
   return cached[dev];
 }
 
-// LowRAM layers: value sums over the key codes (RVMAX = RKMAX), bf16 codes
-template <int RKMAX>
-static hipError_t launch_lr(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
-  dim3 grid(d.n_splits, L.batch * L.n_lat);
-  // ranks are read per head (no exact-rank instances); register arrays sized for
-  // at most 4 query heads per KV head and 4 residual entries where that suffices
-  const bool g4 = L.group <= 4, r4 = L.R <= 4;
-  if (g4 && r4) hipLaunchKernelGGL((k_partials_mfma<RKMAX, RKMAX, false, 16, 4, 4>), grid, dim3(256), 0, s, L, d);
-  else if (g4) hipLaunchKernelGGL((k_partials_mfma<RKMAX, RKMAX, false, 16, 4, 8>), grid, dim3(256), 0, s, L, d);
-  else if (r4) hipLaunchKernelGGL((k_partials_mfma<RKMAX, RKMAX, false, 16, 16, 4>), grid, dim3(256), 0, s, L, d);
-  else hipLaunchKernelGGL((k_partials_mfma<RKMAX, RKMAX, false, 16, 16, 8>), grid, dim3(256), 0, s, L, d);
-  return hipGetLastError();
+// resident workgroups of 256 threads per compute unit for a kernel, asked of the
+// runtime once per (kernel, device) and remembered
+int kernel_blocks_per_cu(const void *fn) {
+  static std::mutex mu;
+  static std::map<std::pair<const void *, int>, int> known;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const auto key = std::make_pair(fn, dev);
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = known.find(key);
+    if (it != known.end()) return it->second;
+  }
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 256, 0) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> g(mu);
+  known[key] = n;
+  return n;
 }
 
-// keys compressed before RoPE (bf16 codes, per-head ranks read at run time)
-template <int RKMAX>
-static hipError_t launch_rp(const LayerArgs &L, const DecodeArgs &d, hipStream_t s) {
-  dim3 grid(d.n_splits, L.batch * L.n_lat);
-  if (L.rv_max <= 16) hipLaunchKernelGGL((k_partials_rope<RKMAX, 16>), grid, dim3(256), 0, s, L, d);
-  else if (L.rv_max <= 32) hipLaunchKernelGGL((k_partials_rope<RKMAX, 32>), grid, dim3(256), 0, s, L, d);
-  else if (L.rv_max <= 64) hipLaunchKernelGGL((k_partials_rope<RKMAX, 64>), grid, dim3(256), 0, s, L, d);
-  else hipLaunchKernelGGL((k_partials_rope<RKMAX, 128>), grid, dim3(256), 0, s, L, d);
-  return hipGetLastError();
+int partials_blocks_per_cu(const LayerArgs &L) {
+  if (L.dtype == LRKV_F32) return generic_blocks_per_cu();
+  return kernel_blocks_per_cu(reinterpret_cast<const void *>(pick_partials(L)));
 }
 
 hipError_t launch_partials_mfma(const LayerArgs &L, const DecodeArgs &d0, hipStream_t s) {
   DecodeArgs d = d0;
-  // balancing pays when the whole grid is resident at once (four workgroups per CU)
-  d.balance = int64_t(d.n_splits) * L.batch * L.n_lat <= 4 * int64_t(cu_count());
-  int rk_max = 0;
-  for (int h = 0; h < L.n_lat; ++h) rk_max = L.heads[h].rk > rk_max ? L.heads[h].rk : rk_max;
-  if (L.rope) {
-    if (rk_max <= 32) return launch_rp<32>(L, d, s);
-    if (rk_max <= 64) return launch_rp<64>(L, d, s);
-    if (rk_max <= 96) return launch_rp<96>(L, d, s);
-    return launch_rp<128>(L, d, s);
-  }
-  if (L.lowram) {
-    if (rk_max <= 32) return launch_lr<32>(L, d, s);
-    if (rk_max <= 64) return launch_lr<64>(L, d, s);
-    if (rk_max <= 96) return launch_lr<96>(L, d, s);
-    return launch_lr<128>(L, d, s);
-  }
-  if (rk_max <= 32) return launch_rk<32>(L, d, s);
-  if (rk_max <= 64) return launch_rk<64>(L, d, s);
-  if (rk_max <= 96) return launch_rk<96>(L, d, s);
-  return launch_rk<128>(L, d, s);
+  // balancing pays when the whole grid is resident at once
+  const int per_cu = partials_blocks_per_cu(L), cus = device_cu_count();
+  d.balance = per_cu > 0 && cus > 0 && int64_t(d.items) <= int64_t(per_cu) * cus;
+  PartialsFn fn = pick_partials(L);
+  LayerArgs la = L;
+  void *args[] = {&la, &d};
+  return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(d.row_items, L.batch), dim3(256), args, 0, s);
 }
 
 }  // namespace lrkv

@@ -69,9 +69,17 @@ __host__ __device__ __forceinline__ int64_t resid_entry(const LayerArgs &L, int 
 // l: sum of 2^(s - m), o~: rank-space value sum of the codes (rvp = rv_max
 // rounded up to 4), o_A: 128-dim value sum of the anchors (written only by
 // splits that hold anchors).
+//
+// Splits per latent group.  n_splits = S is the split count of the group with
+// the most code bytes per token; group h gets S_h = nsplit[h] <= S splits, in
+// proportion to its own code bytes per token (all S with uniform ranks), so the
+// workgroups of a layer with mixed ranks stream about the same bytes each.
+// Stage 1 runs one workgroup per work item (batch row b, group h, split s < S_h),
+// items ordered by b, then h, then s: row_items = sum_h S_h per row, group h's
+// first item of a row at split0[h].  The launch grid is (row_items, batch).
 struct DecodeArgs {
   int32_t n_ctx;
-  int32_t n_splits;
+  int32_t n_splits;      // S: record stride, and S_h of the widest groups
   int32_t rec;           // floats per record: 4 + rvp + 128
   int32_t oa;            // offset of o_A in a record: 4 + rvp
   float scale_log2;      // sm_scale * log2(e): scores are kept in log2 units
@@ -79,7 +87,22 @@ struct DecodeArgs {
   const void *q;
   float *ws;             // [batch][n_q][n_splits][rec]
   int32_t balance;       // stage 1: raise the wave priority of the waves with more work left
+  int32_t uniform;       // every group has S_h = S
+  int32_t row_items;     // sum over groups of S_h
+  int32_t items;         // batch * row_items: the stage-1 workgroups
+  int32_t nsplit[LRKV_MAX_KV_HEADS];      // S_h
+  int32_t split0[LRKV_MAX_KV_HEADS + 1];  // first item of group h within a row
 };
+
+// host: the workgroups of one stage-1 launch that are resident on one compute
+// unit at once, for the kernel instance the layer would launch (0 if unknown)
+int partials_blocks_per_cu(const LayerArgs &L);
+// host: compute units of the current device (0 if unknown)
+int device_cu_count();
+// host: resident workgroups of 256 threads per compute unit of a kernel, and of
+// the float32 stage-1 kernel (0 if unknown)
+int kernel_blocks_per_cu(const void *fn);
+int generic_blocks_per_cu();
 
 // ---------------------------------------------------------------------------
 // storage types
