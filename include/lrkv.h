@@ -377,6 +377,23 @@ lrkv_status lrkv_decode_attn(const lrkv_layer *L, int32_t n_ctx, const int32_t *
                              const void *q, float *out, float sm_scale, int32_t n_splits,
                              void *workspace, size_t workspace_bytes, lrkv_stream_t stream);
 
+/*
+ * The decode step without a caller workspace, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): as lrkv_decode_attn, with the split records in an array the
+ * library holds in device memory, one per GPU, of 16 MiB (16777216 bytes), set
+ * up on the first call on each device and kept until the process ends.  The
+ * call allocates nothing.  Every call on one GPU shares the array: calls that
+ * overlap on a GPU (other streams, other threads) race, so serialise them.  The same kernels run as for lrkv_decode_attn with the same
+ * n_splits, so the output is bitwise the same.
+ * Errors: as lrkv_decode_attn; LRKV_ERR_WORKSPACE when
+ * lrkv_decode_workspace_size(L, n_splits) (n_splits after resolving 0) exceeds
+ * 16 MiB; LRKV_ERR_HIP if the array's address cannot be obtained.
+ */
+lrkv_status lrkv_decode_attn_noalloc(const lrkv_layer *L, int32_t n_ctx, const int32_t *ctx_lens,
+                                     const void *q, float *out, float sm_scale, int32_t n_splits,
+                                     lrkv_stream_t stream);
+
 const char *lrkv_status_string(lrkv_status s);
 
 /* Library version as 10000*major + 100*minor + patch. */

@@ -79,6 +79,8 @@ SIGNATURES = [
     ("lrkv_decode_combine", c_int32, [_P, c_int32, c_void_p, c_int32, c_void_p, c_size_t, c_void_p,
                                       c_void_p]),
     ("lrkv_decode_attn", c_int32, [_P, c_int32, c_void_p, c_void_p, c_void_p, c_float, c_int32, c_void_p, c_size_t, c_void_p]),
+    ("lrkv_decode_attn_noalloc", c_int32, [_P, c_int32, c_void_p, c_void_p, c_void_p, c_float, c_int32,
+                                           c_void_p]),
     ("lrkv_status_string", ctypes.c_char_p, [c_int32]),
     ("lrkv_version", c_int32, []),
 ]
@@ -355,6 +357,17 @@ def lrkv_decode_attn(layer: Layer, n_ctx: int, q, out, sm_scale: float, n_splits
                                   _ptr(out), sm_scale, n_splits, _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(stream)),
            "lrkv_decode_attn")
+
+
+def lrkv_decode_attn_noalloc(layer: Layer, n_ctx: int, q, out, sm_scale: float, n_splits: int, ctx_lens=None,
+                             stream=None):
+    """lrkv_decode_attn with the split records in the library's per-device array
+    (no workspace argument, nothing allocated)."""
+    _check(lib().lrkv_decode_attn_noalloc(ctypes.byref(layer.struct), n_ctx, _ptr(ctx_lens), _ptr(q), _ptr(out),
+                                          sm_scale, n_splits, _stream(stream)), "lrkv_decode_attn_noalloc")
+
+
+NOALLOC_CAPACITY = 16 << 20  # bytes of split records lrkv_decode_attn_noalloc holds per device
 
 
 def lrkv_version() -> int:

@@ -418,6 +418,23 @@ lrkv_status lrkv_decode_attn(const lrkv_layer *L, int32_t n_ctx, const int32_t *
   return hip_status(launch_decode_combine(A, D, out, s));
 }
 
+lrkv_status lrkv_decode_attn_noalloc(const lrkv_layer *L, int32_t n_ctx, const int32_t *ctx_lens,
+                                     const void *q, float *out, float sm_scale, int32_t n_splits,
+                                     lrkv_stream_t stream) {
+  LayerArgs A;
+  lrkv_status st = make_layer(L, &A);
+  if (st != LRKV_OK) return st;
+  if (!q || !out) return LRKV_ERR_NULL;
+  if (!aligned16(out)) return LRKV_ERR_ALIGN;
+  // every check first, with a stand-in for the array's address: the records of
+  // this call must fit in it (LRKV_ERR_WORKSPACE otherwise)
+  DecodeArgs D;
+  st = make_decode(L, A, n_ctx, ctx_lens, q, sm_scale, n_splits, reinterpret_cast<void *>(uintptr_t(256)),
+                   noalloc_scratch_bytes(), &D);
+  if (st != LRKV_OK) return st;
+  return decode_attn_noalloc(A, D, out, reinterpret_cast<hipStream_t>(stream));
+}
+
 const char *lrkv_status_string(lrkv_status s) {
   switch (s) {
     case LRKV_OK: return "ok";

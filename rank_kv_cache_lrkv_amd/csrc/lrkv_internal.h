@@ -197,6 +197,10 @@ hipError_t launch_append(const LayerArgs &L, const void *k, const void *v, int p
 hipError_t launch_decode_partials(const LayerArgs &L, const DecodeArgs &d, hipStream_t s);
 hipError_t launch_partials_mfma(const LayerArgs &L, const DecodeArgs &d, hipStream_t s);
 hipError_t launch_decode_combine(const LayerArgs &L, const DecodeArgs &d, float *out, hipStream_t s);
+// the decode step with its split records in the library's per-device array
+// (noalloc.hip); D.ws is set there
+size_t noalloc_scratch_bytes();
+lrkv_status decode_attn_noalloc(const LayerArgs &A, DecodeArgs &D, float *out, hipStream_t s);
 hipError_t launch_oja(const LayerArgs &L, int which, const void *x, int64_t sb, int64_t sh, int64_t st,
                       int n_tok, float eta, int vin, int vout, float *ws, hipStream_t s);
 size_t oja_workspace_bytes(const LayerArgs &L);

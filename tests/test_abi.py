@@ -348,3 +348,18 @@ def test_probe_spin_rejects_bad_arguments():
     assert measure.lib().lrkv_probe_spin(100, None, None) == 1
     assert measure.lib().lrkv_probe_spin(-1, FAKE, None) == 2
     assert measure.lib().lrkv_probe_spin((1 << 32) + 1, FAKE, None) == 2
+
+
+def test_noalloc_decode_validates_on_the_host():
+    """lrkv_decode_attn_noalloc checks every argument before any HIP call, and
+    rejects split records larger than its 16 MiB array."""
+    lib = B.lib()
+    L = layer(batch=64, n_q_heads=32, n_kv_heads=8, window=32, cap=96, rank_k=[32] * 8, rank_v=[32] * 8)
+    f = lambda **k: lib.lrkv_decode_attn_noalloc(ctypes.byref(L), k.get("n", 100), None, k.get("q", FAKE),
+                                                 k.get("out", FAKE), 0.088, k.get("S", 2), None)
+    assert f(q=None) == 1
+    assert f(out=FAKE + 4) == 5
+    assert f(n=0) == 2
+    assert f(n=10000) == 6
+    assert lib.lrkv_decode_workspace_size(ctypes.byref(L), 1024) > B.NOALLOC_CAPACITY
+    assert f(S=1024) == 7
