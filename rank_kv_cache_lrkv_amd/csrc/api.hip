@@ -172,11 +172,21 @@ int32_t auto_splits(const LayerArgs &A, int32_t n_ctx) {
     wsum += token_bytes(A, h);
     wmax = std::max(wmax, token_bytes(A, h));
   }
-  int64_t s = int64_t(std::ceil(double(target) * wmax / (double(A.batch) * wsum) - 1e-9));
+  int64_t s = int64_t(std::floor(double(target) * wmax / (double(A.batch) * wsum) + 1e-9));
   const int64_t most = nblk / 4 > 1 ? nblk / 4 : 1;
   if (s > most) s = most;
   if (s < 1) s = 1;
   if (s > LRKV_MAX_SPLITS) s = LRKV_MAX_SPLITS;
+  // the groups' rounded split counts must not add up to more workgroups than are
+  // resident at once: a second, nearly empty round would double the tail
+  int32_t ns[LRKV_MAX_KV_HEADS];
+  while (s > 1) {
+    group_splits(A, int32_t(s), ns);
+    int64_t items = 0;
+    for (int h = 0; h < A.n_lat; ++h) items += ns[h];
+    if (items * A.batch <= target) break;
+    --s;
+  }
   if (s < A.n_versions) s = A.n_versions;  // every basis version needs a split
   return int32_t(s);
 }

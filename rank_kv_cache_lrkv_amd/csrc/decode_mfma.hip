@@ -288,17 +288,21 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
   // keeps them from displacing the query, U_K and anchor lines the splits of a
   // unit share in L2, and measurably raises the read rate on this part.
   constexpr int kStream = 2;
+  // column groups past the head's rank (instances wider than the head) read from
+  // an offset past the region's extent: the buffer unit returns zeros for them
+  // without touching memory
+  constexpr int kAbsent = 0x40000000;
   int koff[2][NKC];
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
-      const int kg = min(4 * kc + q4, nkg - 1);  // absent groups re-read a present one, then zero
-      koff[h2][kc] = ((h2 * nkg + kg) * 16 + t16) * CB;
+      const int kg = 4 * kc + q4;
+      koff[h2][kc] = kg < nkg ? ((h2 * nkg + kg) * 16 + t16) * CB : kAbsent;
     }
   int voff[NVC];
 #pragma unroll
-  for (int ni = 0; ni < NVC; ++ni) voff[ni] = (q4 * rv + 16 * min(ni, nvt - 1) + t16) * CB;
+  for (int ni = 0; ni < NVC; ++ni) voff[ni] = ni < nvt ? (q4 * rv + 16 * ni + t16) * CB : kAbsent;
 
   auto load = [&](int blk, BlockRegs<NKC, NVC, CB> &r) {
     set_priority(blk);
@@ -655,9 +659,9 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) kr[tt][h2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          // U_K columns past rk are zero in LDS, so chunks past a head's rank add
-          // nothing (their code lanes re-read a present group): for narrow ranks
-          // they run unconditionally, sparing the branches
+          // U_K columns past rk are zero in LDS (and the code lanes of absent
+          // groups read zeros), so chunks past a head's rank add nothing: for
+          // narrow ranks they run unconditionally, sparing the branches
           for (int kc = 0; kc < NKC; ++kc) {
             if (kLean || 4 * kc < nkg) {
               const u32x4 a = *reinterpret_cast<const u32x4 *>(&su[(16 * ft + t16) * RS + 32 * kc + 8 * q4]);
