@@ -244,7 +244,7 @@ def stream_ceiling(timer, nbytes, launches=12):
     sink = torch.zeros(65536, dtype=torch.int32, device="cuda")
     s = timer.stream.cuda_stream
     best, sweep = None, []
-    for grid in (1024, 2048, 4096, 8192):
+    for grid in (512, 768, 1024, 2048, 4096, 8192):
         for unroll in (2, 4, 8):
             for nt in (False, True):
                 fn = lambda i: measure.read(bufs[i % nbuf], nbytes, sink, grid, unroll, nt, s)

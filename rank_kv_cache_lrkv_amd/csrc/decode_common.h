@@ -44,6 +44,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 struct WorkItem {
   int b, h, split, S;
 };
+// The group is found without a loop of dependent reads: with uniform splits by a
+// division, otherwise by counting, over every entry of split0 at once (scalar
+// reads that issue together), the groups h >= 1 whose first item is <= r.
 __device__ __forceinline__ WorkItem work_item(const LayerArgs &L, const DecodeArgs &d) {
   const int i = blockIdx.x + d.row_items * blockIdx.y;
   const int j = (d.items & 7) == 0 ? (i & 7) * (d.items >> 3) + (i >> 3) : i;
@@ -54,7 +57,12 @@ __device__ __forceinline__ WorkItem work_item(const LayerArgs &L, const DecodeAr
   if (d.uniform) {
     h = r / d.n_splits;
   } else {
-    while (h + 1 < L.n_lat && d.split0[h + 1] <= r) ++h;
+#pragma unroll
+    for (int k = 1; k < 16; ++k) h += (k < L.n_lat && d.split0[k] <= r) ? 1 : 0;
+    if (L.n_lat > 16) {
+#pragma unroll
+      for (int k = 16; k < LRKV_MAX_KV_HEADS; ++k) h += (k < L.n_lat && d.split0[k] <= r) ? 1 : 0;
+    }
   }
   w.h = h;
   w.split = r - d.split0[h];

@@ -200,6 +200,14 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
   bf16_t *const su = sm.w.r.su;
   auto &rq = sm.w.r.rq;
 
+  // Setup reads.  Every kernel-argument scalar the setup needs is taken at once
+  // (the empty asm takes them all as operands, so their scalar loads issue
+  // together and are waited for once); otherwise each branch on a loaded value
+  // would wait for its own round trip, a dozen of them before the first load.
+  __asm__ volatile("" ::"s"(d.row_items), "s"(d.items), "s"(d.uniform), "s"(d.n_splits), "s"(d.balance),
+                   "s"(d.ctx_lens), "s"(d.n_ctx), "s"(d.q), "s"(L.n_lat), "s"(L.window), "s"(L.hg), "s"(L.group),
+                   "s"(L.n_versions), "s"(L.cap), "s"(L.n_kv), "s"(L.n_q), "s"(L.codes_k), "s"(L.codes_v),
+                   "s"(L.anchor_k), "s"(L.anchor_v), "s"(L.bases));
   // (batch row b, latent group h) and split `split` of the group's S; the G
   // query heads are those of the hg KV heads h hg .. h hg + hg - 1 (GK each),
   // which share the group's codes
@@ -209,13 +217,16 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
   const int GK = L.group, G = GK * L.hg;
   const int W = L.window;
   const HeadInfo hd = L.heads[h];
+  // the group's row of the head table and the row's length: the second (and
+  // last) round of setup reads
+  const int n = row_ctx(d, b);
+  __asm__ volatile("" ::"s"(hd.rk), "s"(hd.rv), "s"(hd.u_k), "s"(hd.ck), "s"(hd.cv), "s"(wi.S), "s"(n));
   const int rk = EXACT ? RKMAX : hd.rk, rv = EXACT ? RVMAX : hd.rv;
   const int nkg = rk >> 3;   // 8-column groups of a key code
   const int nvt = rv >> 4;   // 16-column tiles of a value code
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, t16 = lane & 15;
-  const int n = row_ctx(d, b);
   const int c = max(0, n - 1 - W);
   const int nblk = (c + kBlock - 1) / kBlock;
   // the unit's anchor rows: a1 per KV head, KV head after KV head
