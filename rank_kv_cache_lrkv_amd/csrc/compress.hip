@@ -200,13 +200,54 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
     const T *Uk = static_cast<const T *>(L.bases) + ver * L.version_elems + hd.u_k;
     const T *Uv = static_cast<const T *>(L.bases) + ver * L.version_elems + hd.u_v;
     const int urow = hg * kD;  // elements of a basis row (U^T row)
-    float acck = 0.f, accv = 0.f;
-    if (tid < hd.rk)
-      for (int j = 0; j < hg; ++j)
-        for (int k = 0; k < kD; ++k) acck = fmaf(rk_row[j][k], to_f32(Uk[tid * urow + j * kD + k]), acck);
-    if (tid < hd.rv && !L.lowram)  // LowRAM layers have no value codes
-      for (int j = 0; j < hg; ++j)
-        for (int k = 0; k < kD; ++k) accv = fmaf(rv_row[j][k], to_f32(Uv[tid * urow + j * kD + k]), accv);
+    // Column e of the codes (key columns 0 .. rk - 1, then value columns) is the
+    // dot product of the leaving row(s) with basis row e: 16 lanes share a
+    // column, lane f8 taking features 8 f8 .. 8 f8 + 7 of every 128-slice with
+    // 16-byte loads, four columns per wave and step, the lanes' partial sums
+    // added by shuffles inside each 16-lane group
+    __shared__ float res[2 * kD];
+    {
+      constexpr int kE = 16 / sizeof(T);  // elements per 16-byte piece
+      const int lane = tid & 63, q = lane >> 4, f8 = lane & 15, wave = tid >> 6;
+      const int ncol = hd.rk + (L.lowram ? 0 : hd.rv);  // LowRAM layers have no value codes
+      for (int e0 = 0; e0 < ncol; e0 += 8) {
+        const int e = e0 + 4 * wave + q;
+        const int ec = min(e, ncol - 1);
+        const bool isk = ec < hd.rk;
+        const T *urow_p = isk ? Uk + ec * urow : Uv + (ec - hd.rk) * urow;
+        float acc = 0.f;
+        for (int j = 0; j < hg; ++j) {
+          float u[8];
+          if constexpr (sizeof(T) == 2) {
+            const uint4 w = *reinterpret_cast<const uint4 *>(urow_p + j * kD + 8 * f8);
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              u[2 * i] = __uint_as_float(ww[i] << 16);
+              u[2 * i + 1] = __uint_as_float(ww[i] & 0xffff0000u);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; i += kE) {
+              const float4 w = *reinterpret_cast<const float4 *>(urow_p + j * kD + 8 * f8 + i);
+              u[i] = w.x;
+              u[i + 1] = w.y;
+              u[i + 2] = w.z;
+              u[i + 3] = w.w;
+            }
+          }
+          const float *xr = isk ? rk_row[j] : rv_row[j];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc = fmaf(u[i], xr[8 * f8 + i], acc);
+        }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+        if (f8 == 0 && e < ncol) res[e] = acc;
+      }
+    }
+    __syncthreads();
+    const float acck = tid < hd.rk ? res[tid] : 0.f;
+    const float accv = tid < hd.rv && !L.lowram ? res[hd.rk + tid] : 0.f;
     if constexpr (QMAX > 0) {
       const float sk = qn_scale<QMAX>(block_absmax(tid < hd.rk ? acck : 0.f, red));
       const float sv = qn_scale<QMAX>(block_absmax(tid < hd.rv ? accv : 0.f, red));

@@ -133,3 +133,42 @@ def test_store_anchors_ring():
                 s = layout.anchor_slot(p, 8)
                 assert np.array_equal(ak[b, h, s], hc.k[b][h][p])
                 assert np.array_equal(av[b, h, s], hc.v[b][h][p])
+
+
+APPEND = [
+    ("bf16_W4_mixed", W["qwen3_1p7b_4k"].scaled(batch=2, n_q_heads=8, n_kv_heads=4, window=4, n_ctx=0,
+                                                 n_steps=70, mixed_ranks=True, rank_k_choices=(16, 48, 96, 128),
+                                                 rank_v_choices=(16, 32, 128))),
+    ("bf16_W0", W["llama31_8b_32layer"].scaled(batch=2, window=0, n_ctx=0, n_steps=40)),
+    ("f32_W4", W["tiny_f32"].scaled(window=4, n_ctx=0, n_steps=45)),
+]
+
+
+@pytest.mark.parametrize("label,w", APPEND, ids=[a[0] for a in APPEND])
+def test_append_codes_match_oracle(label, w):
+    """Cache maintenance token by token from position 0: every code slot an append
+    fills holds the projection of the token that left the window (of the new
+    token when W = 0), within the compress bar, and the anchor ring holds the
+    last W tokens exactly."""
+    announce(f"append codes {label}")
+    hc = host_case(w, n=w.n_steps)
+    n, Wn = w.n_steps, w.window
+    L = gpu_layer(hc, with_codes=False, cap=layout.round_cap(n))
+    k, v = upload_rows(hc, "k", n), upload_rows(hc, "v", n)
+    for pos in range(n):
+        B.lrkv_append(L, k[:, :, pos].contiguous(), v[:, :, pos].contiguous(), pos)
+    torch.cuda.synchronize()
+    c = max(0, n - 1 - Wn)  # code slots filled: tokens 1 .. n - W - 1
+    for which in "kv":
+        for b in range(w.batch):
+            for h in range(w.n_kv_heads):
+                got = read_codes(L, hc, which, b, h, c)
+                src = (hc.k if which == "k" else hc.v)[b][h][1:1 + c]
+                check_codes(got, src, (hc.u_k if which == "k" else hc.u_v)[h], w.dtype, f"{label}/{which}/b{b}h{h}")
+    ak = L.anchor_k.float().cpu().numpy()
+    av = L.anchor_v.float().cpu().numpy()
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            for p in oracle.anchor_positions(n, Wn):
+                s = layout.anchor_slot(int(p), Wn)
+                assert np.array_equal(ak[b, h, s], hc.k[b][h][p]) and np.array_equal(av[b, h, s], hc.v[b][h][p])
