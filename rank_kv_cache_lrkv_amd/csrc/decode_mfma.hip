@@ -1006,10 +1006,18 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
   }
 }
 
-// The kernels: the code-space instances at up to four workgroups per compute
-// unit; the pre-RoPE instances asked to fit three (their LDS is sized for it).
+// The kernels.  Code-space instances whose value width is at most 32 are asked
+// to fit four workgroups per compute unit (128 registers a lane): every such
+// instance does so without spilling, except the 128-wide key body with bf16 codes
+// and the LowRAM bodies with 16 residual rows, which keep the compiler's own
+// choice, as do the wider value bodies (they cannot fit four).  The pre-RoPE
+// instances are asked to fit three (their LDS is sized for it).
+template <int RKMAX, int RVMAX, int CB, int LR>
+constexpr int partials_min_blocks() {
+  return (RVMAX <= 32 && LR != 16 && !(RKMAX == 128 && CB == 16)) ? 4 : 1;
+}
 template <int RKMAX, int RVMAX, bool EXACT, int CB, int LR = 0, int LRR = 0>
-__global__ __launch_bounds__(256) void k_partials_mfma(LayerArgs L, DecodeArgs d) {
+__global__ __launch_bounds__(256, (partials_min_blocks<RKMAX, RVMAX, CB, LR>())) void k_partials_mfma(LayerArgs L, DecodeArgs d) {
   partials_body<RKMAX, RVMAX, EXACT, CB, LR, LRR, false>(L, d);
 }
 template <int RKMAX, int RVMAX>
