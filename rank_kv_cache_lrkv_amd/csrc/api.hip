@@ -162,7 +162,7 @@ int32_t auto_splits(const LayerArgs &A, int32_t n_ctx) {
   // about as many workgroups as the launched kernel keeps resident at once on
   // the device (its occupancy per compute unit times the compute units); without
   // a device to ask, the figures of MI355X (256 compute units, four workgroups
-  // per unit, three for the pre-RoPE and LowRAM kernels).  The groups' splits
+  // per unit, three for the LowRAM kernels and the narrower pre-RoPE ones).  The groups' splits
   // follow their bytes per token, so the widest group's count is scaled by
   // (widest bytes) / (mean bytes).  At least four 32-slot blocks per split.
   const int per_cu = partials_blocks_per_cu(A), cus = device_cu_count();

@@ -1011,7 +1011,9 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
 // instance does so without spilling, except the 128-wide key body with bf16 codes
 // and the LowRAM bodies with 16 residual rows, which keep the compiler's own
 // choice, as do the wider value bodies (they cannot fit four).  The pre-RoPE
-// instances are asked to fit three (their LDS is sized for it).
+// instances are asked for three where that needs no spill (their LDS is sized for
+// three), else for two (the 128/128 body keeps the compiler's choice: it spills
+// at two).
 template <int RKMAX, int RVMAX, int CB, int LR>
 constexpr int partials_min_blocks() {
   return (RVMAX <= 32 && LR != 16 && !(RKMAX == 128 && CB == 16)) ? 4 : 1;
@@ -1021,7 +1023,11 @@ __global__ __launch_bounds__(256, (partials_min_blocks<RKMAX, RVMAX, CB, LR>()))
   partials_body<RKMAX, RVMAX, EXACT, CB, LR, LRR, false>(L, d);
 }
 template <int RKMAX, int RVMAX>
-__global__ __launch_bounds__(256, 3) void k_partials_rope(LayerArgs L, DecodeArgs d) {
+constexpr int rope_min_blocks() {
+  return (RKMAX == 128 && RVMAX == 128) ? 1 : (RVMAX <= 32 && RKMAX <= 64 && !(RKMAX == 64 && RVMAX == 32)) ? 3 : 2;
+}
+template <int RKMAX, int RVMAX>
+__global__ __launch_bounds__(256, (rope_min_blocks<RKMAX, RVMAX>())) void k_partials_rope(LayerArgs L, DecodeArgs d) {
   partials_body<RKMAX, RVMAX, false, 16, 0, 0, true>(L, d);
 }
 

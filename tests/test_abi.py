@@ -210,7 +210,7 @@ def test_oja_validation():
     lib = B.lib()
     L = layer()
     need = lib.lrkv_oja_workspace_size(ctypes.byref(L))
-    assert need == 2 * (64 + 1) * 36 * 256 * 4     # 2 KV heads x (64 workgroup partials + the sum) of 36 tiles
+    assert need == 2 * (64 * 36 * 256 + 128 * 128) * 4  # 2 KV heads x (64 workgroup partials of 36 tiles + C in full)
     f = lambda L=L, **k: lib.lrkv_oja_update(ctypes.byref(L), k.get("which", 0), k.get("x", FAKE), 1024, 512,
                                              128, k.get("n", 10), k.get("eta", 0.5), k.get("vin", 0),
                                              k.get("vout", 0), k.get("ws", FAKE), k.get("wsb", need), None)
