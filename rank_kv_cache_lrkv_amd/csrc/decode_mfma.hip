@@ -188,13 +188,12 @@ __device__ __forceinline__ u32x4 i4x8_to_bf16_x16(uint32_t w) {
 // are scored against q whose features are permuted to the order the lanes hold
 // (k = 8 q4 + i <-> feature 32 kc + 16 (i / 4) + 4 q4 + i % 4).
 template <int RKMAX, int RVMAX, bool EXACT, int CB, int LR = 0, int LRR = 0, bool RP = false>
-__device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeArgs &d) {
+__device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeArgs &d, MfmaSmem<RKMAX, RVMAX, RP> &sm) {
   constexpr int NKC = (RKMAX + 31) / 32;  // score MFMAs per 16-token tile (K = 32 each)
   constexpr int NVC = RVMAX / 16;         // value MFMAs per block (16 columns each)
   constexpr bool QC = CB < 16;            // quantised codes with per-token scales
   constexpr float kX16 = CB == 4 ? 0.0625f : 1.f;  // undoes the x16 of 4-bit operands
   constexpr int RS = RKMAX + 8;           // RP: LDS row of U_K (one feature, RKMAX + 8 bf16)
-  __shared__ MfmaSmem<RKMAX, RVMAX, RP> sm;
   __shared__ float sra[RP ? kD / 2 : 1][2];      // RP: angle per position of each pair (revolutions)
   __shared__ float srd[RP ? kD / 2 : 1][3];      // RP: the angle over a wave's block stride; cos, sin over 16 positions
   bf16_t *const su = sm.w.r.su;
@@ -1018,9 +1017,24 @@ template <int RKMAX, int RVMAX, int CB, int LR>
 constexpr int partials_min_blocks() {
   return (RVMAX <= 32 && LR != 16 && !(RKMAX == 128 && CB == 16)) ? 4 : 1;
 }
+//
+// With mixed ranks (not EXACT, code-space values) a workgroup whose group's key
+// width fits a narrower body (64 columns; 32 in the 64-wide instances) runs that
+// body, so narrow groups do not carry the widest group's score MFMAs and operand
+// slots; the two bodies share one LDS allocation (the wider layout; the narrower
+// one is no larger).  (A third body made the compiler copy the kernel arguments
+// to scratch.)
 template <int RKMAX, int RVMAX, bool EXACT, int CB, int LR = 0, int LRR = 0>
 __global__ __launch_bounds__(256, (partials_min_blocks<RKMAX, RVMAX, CB, LR>())) void k_partials_mfma(LayerArgs L, DecodeArgs d) {
-  partials_body<RKMAX, RVMAX, EXACT, CB, LR, LRR, false>(L, d);
+  __shared__ MfmaSmem<RKMAX, RVMAX, false> sm;
+  if constexpr (!EXACT && LR == 0 && RKMAX > 32) {
+    constexpr int NARROW = RKMAX > 64 ? 64 : 32;
+    if (L.heads[work_item(L, d).h].rk <= NARROW) {
+      partials_body<NARROW, RVMAX, false, CB>(L, d, reinterpret_cast<MfmaSmem<NARROW, RVMAX, false> &>(sm));
+      return;
+    }
+  }
+  partials_body<RKMAX, RVMAX, EXACT, CB, LR, LRR, false>(L, d, sm);
 }
 template <int RKMAX, int RVMAX>
 constexpr int rope_min_blocks() {
@@ -1028,7 +1042,8 @@ constexpr int rope_min_blocks() {
 }
 template <int RKMAX, int RVMAX>
 __global__ __launch_bounds__(256, (rope_min_blocks<RKMAX, RVMAX>())) void k_partials_rope(LayerArgs L, DecodeArgs d) {
-  partials_body<RKMAX, RVMAX, false, 16, 0, 0, true>(L, d);
+  __shared__ MfmaSmem<RKMAX, RVMAX, true> sm;
+  partials_body<RKMAX, RVMAX, false, 16, 0, 0, true>(L, d, sm);
 }
 
 // ---------------------------------------------------------------------------
