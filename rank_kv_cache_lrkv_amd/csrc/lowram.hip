@@ -15,8 +15,9 @@
 //                   column (the MFMA contracts over tokens, so every operand
 //                   fragment is 8 consecutive tokens of one column)
 //   k_lowram_solve  one workgroup per (row, head): the partials summed in a
-//                   fixed order, Cholesky of C^T C + lam I and the two triangular
-//                   solves in LDS (float32), M stored as bf16
+//                   fixed order, C^T C + lam I eliminated (Cholesky with
+//                   unscaled columns) and the two triangular solves in LDS
+//                   (float32), M stored as bf16
 //   k_lowram_resid  per block: C M on the matrix cores against the staged M^T,
 //                   e = V - C M, squared norms, the block's top R by rank
 //                   counting, residual rows, slots and norms stored
@@ -27,11 +28,12 @@
 namespace lrkv {
 
 constexpr int kZStride = 40;  // LDS column of a staged tile: 32 tokens + 8 pad (80 bytes)
+constexpr int kMaxPartials = 16;  // Gram partials per unit (the solve keeps them all in flight)
 
 int lowram_partials(const LayerArgs &L) {
   const int units = L.batch * L.n_kv;
   const int p = (1024 + units - 1) / units;
-  return p < 1 ? 1 : (p > 16 ? 16 : p);
+  return p < 1 ? 1 : (p > kMaxPartials ? kMaxPartials : p);
 }
 
 static int lowram_rk_max(const LayerArgs &L) {
@@ -79,35 +81,59 @@ __global__ __launch_bounds__(256) void k_lowram_gram(LayerArgs L, const bf16_t *
 #pragma unroll
     for (int jj = 0; jj < NJT; ++jj) acc[it][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int blk = blo; blk < bhi; ++blk) {
-    __syncthreads();  // the previous tile's readers are done
-    // key codes: 32 tokens x rk / 8 pieces of 8 columns; slots past n_tok are zero
-    for (int pc = tid; pc < 4 * rk; pc += 256) {
-      const int t = pc / (rk / 8), cg = pc - t * (rk / 8);
-      const int slot = blk * kBlock + t;
-      u32x4 x = u32x4{0u, 0u, 0u, 0u};
-      if (slot < n_tok) x = *reinterpret_cast<const u32x4 *>(codes + kslot(slot, 8 * cg, rk));
+  // this thread's pieces of a tile: code pieces tid + 256 u (8 columns of one
+  // token each; 4 rk per tile) and value pieces tid + 256 u (8 features of one
+  // token; 512 per tile).  Loads are clamped to the last token (rows past n_tok
+  // are zeroed when staged, so no load waits where it is issued); every thread
+  // keeps the loads of two tiles in flight while the staged one is multiplied.
+  constexpr int NPK = (4 * RKMAX + 255) / 256;
+  struct Tile {
+    u32x4 k[NPK];
+    u32x4 v[2];
+  };
+  auto load = [&](int blk, Tile &t) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sz[(8 * cg + 2 * i) * kZStride + t] = bf16_t(x[i] & 0xffffu);
-        sz[(8 * cg + 2 * i + 1) * kZStride + t] = bf16_t(x[i] >> 16);
+    for (int u = 0; u < NPK; ++u) {
+      const int pc = min(tid + 256 * u, 4 * rk - 1);
+      const int tt = pc / (rk / 8), cg = pc - tt * (rk / 8);
+      const int slot = min(blk * kBlock + tt, n_tok - 1);
+      t.k[u] = *reinterpret_cast<const u32x4 *>(codes + kslot(slot, 8 * cg, rk));
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int pc = tid + 256 * u, tt = pc >> 4, fg = pc & 15;
+      const int slot = min(blk * kBlock + tt, n_tok - 1);
+      t.v[u] = *reinterpret_cast<const u32x4 *>(vb + int64_t(slot) * st + 8 * fg);
+    }
+  };
+  auto stage = [&](int blk, const Tile &t) {
+#pragma unroll
+    for (int u = 0; u < NPK; ++u) {
+      const int pc = tid + 256 * u;
+      if (pc < 4 * rk) {
+        const int tt = pc / (rk / 8), cg = pc - tt * (rk / 8);
+        const u32x4 x = blk * kBlock + tt < n_tok ? t.k[u] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sz[(8 * cg + 2 * i) * kZStride + tt] = bf16_t(x[i] & 0xffffu);
+          sz[(8 * cg + 2 * i + 1) * kZStride + tt] = bf16_t(x[i] >> 16);
+        }
       }
     }
-    // values: 32 tokens x 16 pieces of 8 features
-    for (int pc = tid; pc < 32 * 16; pc += 256) {
-      const int t = pc >> 4, fg = pc & 15;
-      const int slot = blk * kBlock + t;
-      u32x4 x = u32x4{0u, 0u, 0u, 0u};
-      if (slot < n_tok) x = *reinterpret_cast<const u32x4 *>(vb + int64_t(slot) * st + 8 * fg);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int pc = tid + 256 * u, tt = pc >> 4, fg = pc & 15;
+      const u32x4 x = blk * kBlock + tt < n_tok ? t.v[u] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sz[(rk + 8 * fg + 2 * i) * kZStride + t] = bf16_t(x[i] & 0xffffu);
-        sz[(rk + 8 * fg + 2 * i + 1) * kZStride + t] = bf16_t(x[i] >> 16);
+        sz[(rk + 8 * fg + 2 * i) * kZStride + tt] = bf16_t(x[i] & 0xffffu);
+        sz[(rk + 8 * fg + 2 * i + 1) * kZStride + tt] = bf16_t(x[i] >> 16);
       }
     }
-    __syncthreads();
-    // D[i][j] += sum over the tile's tokens of C[t][i] Z[t][j]: lane (q4, t16) feeds
-    // tokens 8 q4 .. 8 q4 + 7 of column 16 it + t16 (A) and of column 16 jt + t16 (B)
+  };
+  // D[i][j] += sum over the tile's tokens of C[t][i] Z[t][j]: lane (q4, t16) feeds
+  // tokens 8 q4 .. 8 q4 + 7 of column 16 it + t16 (A) and of column 16 jt + t16 (B)
+  auto multiply = [&]() {
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       if (it < rk / 16) {
@@ -122,6 +148,20 @@ __global__ __launch_bounds__(256) void k_lowram_gram(LayerArgs L, const bf16_t *
         }
       }
     }
+  };
+  auto step = [&](int blk, Tile &t) {
+    __syncthreads();  // the previous tile's readers are done
+    stage(blk, t);
+    __syncthreads();
+    if (blk + 2 < bhi) load(blk + 2, t);
+    multiply();
+  };
+  Tile ta, tb;
+  if (blo < bhi) load(blo, ta);
+  if (blo + 1 < bhi) load(blo + 1, tb);
+  for (int blk = blo; blk < bhi; blk += 2) {
+    step(blk, ta);
+    if (blk + 1 < bhi) step(blk + 1, tb);
   }
   // lane (q4, t16) holds D[16 it + 4 q4 + v][16 jt + t16]; rows of nz floats
   float *out = ws + (int64_t(unit) * P + p) * pfloats;
@@ -141,14 +181,22 @@ __global__ __launch_bounds__(256) void k_lowram_gram(LayerArgs L, const bf16_t *
 }
 
 // ---------------------------------------------------------------------------
-// The solve.  One workgroup of 256 threads per (row, head); everything in LDS,
-// float32.  A = C^T C + lam I is factored as L L^T in place (lower triangle,
-// right-looking, one column per step), then L Y = C^T V and L^T M = Y are solved
-// with one thread per output feature.
+// The solve.  One workgroup of 1024 threads per (row, head); everything in LDS,
+// float32.  The partials are summed in a fixed order (all of them in flight).
+// A = C^T C + lam I is eliminated right-looking with unscaled columns, one
+// column and one barrier per step: a_ij -= a_ik a_jk / a_kk for k < j <= i,
+// which leaves A = K diag(1 / d) K^T with K the lower triangle (column k as it
+// stood at step k, d_k = its diagonal) -- the Cholesky factor is K diag(d)^-1/2.
+// Then A M = B (B = C^T V) is solved by K diag(1/d) Z = B, swept forward in the
+// same steps (b_i -= a_ik b_k / d_k leaves b_k = d_k z_k), and K^T M = diag(d) Z
+// backward, a right-looking sweep of one barrier per row over the 128 columns.
 // ---------------------------------------------------------------------------
 constexpr int kSolveStride = 129;  // LDS row of the 128 x 128 matrices (odd: no bank conflicts down a column)
+constexpr int kSolveThreads = 1024;
 
-__global__ __launch_bounds__(256) void k_lowram_solve(LayerArgs L, int P, int64_t pfloats, const float *ws) {
+__global__ __launch_bounds__(kSolveThreads) void k_lowram_solve(LayerArgs L, int P, int64_t pfloats,
+                                                                 const float *ws) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
   __shared__ float sa[128 * kSolveStride];
   __shared__ float sbm[128 * kSolveStride];
   __shared__ float s_lam;
@@ -158,51 +206,64 @@ __global__ __launch_bounds__(256) void k_lowram_solve(LayerArgs L, int P, int64_
   const int rk = hd.rk, nz = rk + kD;
   const int tid = threadIdx.x;
   const float *part = ws + int64_t(unit) * P * pfloats;
-  for (int e = tid; e < rk * nz; e += 256) {
-    float x = 0.f;
-    for (int p = 0; p < P; ++p) x += part[int64_t(p) * pfloats + e];  // fixed order
-    const int i = e / nz, j = e - i * nz;
-    if (j < rk) sa[i * kSolveStride + j] = x;
-    else sbm[i * kSolveStride + (j - rk)] = x;
+  // 4 consecutive elements of a row per piece (nz is a multiple of 16)
+  for (int e4 = tid; e4 < rk * nz / 4; e4 += kSolveThreads) {
+    f4 v[kMaxPartials];
+#pragma unroll
+    for (int p = 0; p < kMaxPartials; ++p)
+      v[p] = *reinterpret_cast<const f4 *>(part + int64_t(min(p, P - 1)) * pfloats + 4 * e4);
+    f4 x = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < kMaxPartials; ++p)
+      if (p < P) x += v[p];  // fixed order
+    const int e = 4 * e4, i = e / nz, j = e - i * nz;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (j + c < rk) sa[i * kSolveStride + j + c] = x[c];
+      else sbm[i * kSolveStride + (j + c - rk)] = x[c];
+    }
   }
   __syncthreads();
-  if (tid == 0) {
+  if (tid < 64) {  // lam from the trace (one wave)
     float tr = 0.f;
-    for (int i = 0; i < rk; ++i) tr += sa[i * kSolveStride + i];
-    s_lam = 1e-6f * tr / float(rk) + 1e-30f;
+    for (int i = tid; i < rk; i += 64) tr += sa[i * kSolveStride + i];
+    tr = wave_sum(tr);
+    if (tid == 0) s_lam = 1e-6f * tr / float(rk) + 1e-30f;
   }
   __syncthreads();
   if (tid < rk) sa[tid * kSolveStride + tid] += s_lam;
   __syncthreads();
+  // elimination, with the forward sweep of B fused into it: step k updates the
+  // pairs k < j <= i < rk (threads as a 32 x 32 grid over them) and the rows
+  // i > k of B (b_i -= a_ik b_k / a_kk; thread (row group g, column f) takes rows
+  // g, g + 8, ...); both read only column k and row k of B, which step k leaves
+  // as they are
+  const int ti = tid >> 5, tj = tid & 31;
+  const int f = tid & (kD - 1), g = tid >> 7;
+  auto rcp_d = [&](int k) { return __builtin_amdgcn_rcpf(fmaxf(sa[k * kSolveStride + k], 1e-30f)); };
   for (int k = 0; k < rk; ++k) {
-    if (tid == 0) sa[k * kSolveStride + k] = sqrtf(fmaxf(sa[k * kSolveStride + k], 1e-30f));
-    __syncthreads();
-    const float dk = sa[k * kSolveStride + k];
-    for (int i = k + 1 + tid; i < rk; i += 256) sa[i * kSolveStride + k] /= dk;
-    __syncthreads();
-    const int m = rk - k - 1;
-    for (int e = tid; e < m * m; e += 256) {
-      const int i = k + 1 + e / m, j = k + 1 + e % m;
-      if (j <= i) sa[i * kSolveStride + j] -= sa[i * kSolveStride + k] * sa[j * kSolveStride + k];
+    const float inv = rcp_d(k);  // hardware reciprocal (about 1 ulp)
+    for (int i = k + 1 + ti; i < rk; i += 32) {
+      const float aik = sa[i * kSolveStride + k] * inv;
+      for (int j = k + 1 + tj; j <= i; j += 32)
+        sa[i * kSolveStride + j] = fmaf(-aik, sa[j * kSolveStride + k], sa[i * kSolveStride + j]);
     }
+    const float z = sbm[k * kSolveStride + f] * inv;
+    for (int i = k + 1 + ((g - k - 1) & 7); i < rk; i += 8)
+      sbm[i * kSolveStride + f] = fmaf(-sa[i * kSolveStride + k], z, sbm[i * kSolveStride + f]);
     __syncthreads();
   }
-  if (tid < kD) {
-    const int f = tid;
-    for (int i = 0; i < rk; ++i) {  // L Y = B
-      float y = sbm[i * kSolveStride + f];
-      for (int k = 0; k < i; ++k) y -= sa[i * kSolveStride + k] * sbm[k * kSolveStride + f];
-      sbm[i * kSolveStride + f] = y / sa[i * kSolveStride + i];
-    }
-    for (int i = rk - 1; i >= 0; --i) {  // L^T M = Y
-      float y = sbm[i * kSolveStride + f];
-      for (int k = i + 1; k < rk; ++k) y -= sa[k * kSolveStride + i] * sbm[k * kSolveStride + f];
-      sbm[i * kSolveStride + f] = y / sa[i * kSolveStride + i];
-    }
+  // backward: K^T M = B (as now updated); m_k = b_k / d_k, then b_i -= a_ki m_k for i < k
+  for (int k = rk - 1; k > 0; --k) {
+    const float mk = sbm[k * kSolveStride + f] * rcp_d(k);
+    for (int i = g; i < k; i += 8) sbm[i * kSolveStride + f] = fmaf(-sa[k * kSolveStride + i], mk, sbm[i * kSolveStride + f]);
+    __syncthreads();
   }
-  __syncthreads();
-  bf16_t *m = static_cast<bf16_t *>(L.pred) + hd.pred + int64_t(b) * rk * kD;
-  for (int e = tid; e < rk * kD; e += 256) m[e] = from_f32<bf16_t>(sbm[(e / kD) * kSolveStride + e % kD]);
+  bf16_t *mo = static_cast<bf16_t *>(L.pred) + hd.pred + int64_t(b) * rk * kD;
+  for (int e = tid; e < rk * kD; e += kSolveThreads) {
+    const int i = e / kD, c = e % kD;
+    mo[e] = from_f32<bf16_t>(sbm[i * kSolveStride + c] * rcp_d(i));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -337,7 +398,7 @@ static void launch_fit_rk(const LayerArgs &L, const bf16_t *v, int64_t sb, int64
   const int64_t pf = lowram_partial_floats(L);
   const int units = L.batch * L.n_kv;
   hipLaunchKernelGGL(k_lowram_gram<RKMAX>, dim3(P, units), dim3(256), 0, s, L, v, sb, sh, st, n_tok, pf, ws);
-  hipLaunchKernelGGL(k_lowram_solve, dim3(units), dim3(256), 0, s, L, P, pf, static_cast<const float *>(ws));
+  hipLaunchKernelGGL(k_lowram_solve, dim3(units), dim3(kSolveThreads), 0, s, L, P, pf, static_cast<const float *>(ws));
   const int nb = (n_tok + kBlock - 1) / kBlock;
   hipLaunchKernelGGL(k_lowram_resid<RKMAX>, dim3((nb + kResidBlocks - 1) / kResidBlocks, units), dim3(256), 0, s,
                      L, v, sb, sh, st, n_tok);
