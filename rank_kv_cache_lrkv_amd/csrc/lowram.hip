@@ -181,15 +181,18 @@ __global__ __launch_bounds__(256) void k_lowram_gram(LayerArgs L, const bf16_t *
 }
 
 // ---------------------------------------------------------------------------
-// The solve.  One workgroup of 1024 threads per (row, head); everything in LDS,
-// float32.  The partials are summed in a fixed order (all of them in flight).
-// A = C^T C + lam I is eliminated right-looking with unscaled columns, one
-// column and one barrier per step: a_ij -= a_ik a_jk / a_kk for k < j <= i,
-// which leaves A = K diag(1 / d) K^T with K the lower triangle (column k as it
-// stood at step k, d_k = its diagonal) -- the Cholesky factor is K diag(d)^-1/2.
-// Then A M = B (B = C^T V) is solved by K diag(1/d) Z = B, swept forward in the
-// same steps (b_i -= a_ik b_k / d_k leaves b_k = d_k z_k), and K^T M = diag(d) Z
-// backward, a right-looking sweep of one barrier per row over the 128 columns.
+// The solve.  One workgroup of 1024 threads per (row, head), float32.  The
+// partials are summed in a fixed order (all of them in flight).  A = C^T C +
+// lam I is eliminated in LDS right-looking with unscaled columns, one column and
+// one barrier per step: a_ij -= a_ik a_jk / a_kk for k < j <= i (threads as a
+// 32 x 32 grid over the pairs), which leaves A = K diag(1/d) K^T with K the
+// lower triangle (column k as it stood at step k, d_k = K_kk; the Cholesky
+// factor is K diag(d)^-1/2).  B = C^T V sits in registers, row i with the eight
+// threads 8 i .. 8 i + 7 (16 columns each); in the same steps row k is
+// published and every later row takes b_i -= a_ik b_k / a_kk, which leaves
+// B = diag(d) Z with K diag(1/d) Z = C^T V.  The backward sweep solves
+// K^T M = B the same way: row k of M = b_k / d_k published, b_i -= K_ki m_k for
+// i < k, one barrier per row.
 // ---------------------------------------------------------------------------
 constexpr int kSolveStride = 129;  // LDS row of the 128 x 128 matrices (odd: no bank conflicts down a column)
 constexpr int kSolveThreads = 1024;
@@ -197,8 +200,9 @@ constexpr int kSolveThreads = 1024;
 __global__ __launch_bounds__(kSolveThreads) void k_lowram_solve(LayerArgs L, int P, int64_t pfloats,
                                                                  const float *ws) {
   typedef float f4 __attribute__((ext_vector_type(4)));
-  __shared__ float sa[128 * kSolveStride];
-  __shared__ float sbm[128 * kSolveStride];
+  __shared__ float sa[128 * kSolveStride];   // A, then the factor K in its lower triangle
+  __shared__ float sbm[128 * kSolveStride];  // B as summed
+  __shared__ __align__(16) float srow[2][kD];  // the published row of B (or of M), by step parity
   __shared__ float s_lam;
   const int unit = blockIdx.x;
   const int b = unit / L.n_kv, h = unit % L.n_kv;
@@ -232,37 +236,62 @@ __global__ __launch_bounds__(kSolveThreads) void k_lowram_solve(LayerArgs L, int
   }
   __syncthreads();
   if (tid < rk) sa[tid * kSolveStride + tid] += s_lam;
+  const int ti = tid >> 5, tj = tid & 31;  // A: the 32 x 32 grid
+  const int bi = tid >> 3, bc = tid & 7;   // B: row bi, columns bc + 8 q
+  float br[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) br[q] = bi < rk ? sbm[bi * kSolveStride + bc + 8 * q] : 0.f;
   __syncthreads();
-  // elimination, with the forward sweep of B fused into it: step k updates the
-  // pairs k < j <= i < rk (threads as a 32 x 32 grid over them) and the rows
-  // i > k of B (b_i -= a_ik b_k / a_kk; thread (row group g, column f) takes rows
-  // g, g + 8, ...); both read only column k and row k of B, which step k leaves
-  // as they are
-  const int ti = tid >> 5, tj = tid & 31;
-  const int f = tid & (kD - 1), g = tid >> 7;
   auto rcp_d = [&](int k) { return __builtin_amdgcn_rcpf(fmaxf(sa[k * kSolveStride + k], 1e-30f)); };
+  auto publish = [&](float *row) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) row[bc + 8 * q] = br[q];
+  };
+  if (bi == 0) publish(srow[0]);
+  __syncthreads();
   for (int k = 0; k < rk; ++k) {
-    const float inv = rcp_d(k);  // hardware reciprocal (about 1 ulp)
+    const float inv = __builtin_amdgcn_rcpf(fmaxf(sa[k * kSolveStride + k], 1e-30f));  // hardware reciprocal
     for (int i = k + 1 + ti; i < rk; i += 32) {
       const float aik = sa[i * kSolveStride + k] * inv;
       for (int j = k + 1 + tj; j <= i; j += 32)
         sa[i * kSolveStride + j] = fmaf(-aik, sa[j * kSolveStride + k], sa[i * kSolveStride + j]);
     }
-    const float z = sbm[k * kSolveStride + f] * inv;
-    for (int i = k + 1 + ((g - k - 1) & 7); i < rk; i += 8)
-      sbm[i * kSolveStride + f] = fmaf(-sa[i * kSolveStride + k], z, sbm[i * kSolveStride + f]);
-    __syncthreads();
+    if (bi > k && bi < rk) {
+      const float* row = srow[k & 1];
+      const float aik = sa[bi * kSolveStride + k] * inv;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) br[q] = fmaf(-aik, row[bc + 8 * q], br[q]);
+      if (bi == k + 1) publish(srow[(k + 1) & 1]);  // row k + 1 is final now
+    }
+    __syncthreads();  // also: every read of the other parity's row is done
   }
-  // backward: K^T M = B (as now updated); m_k = b_k / d_k, then b_i -= a_ki m_k for i < k
+  // backward
+  if (bi == rk - 1) {
+    const float r = rcp_d(rk - 1);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) br[q] *= r;
+    publish(srow[(rk - 1) & 1]);
+  }
+  __syncthreads();
   for (int k = rk - 1; k > 0; --k) {
-    const float mk = sbm[k * kSolveStride + f] * rcp_d(k);
-    for (int i = g; i < k; i += 8) sbm[i * kSolveStride + f] = fmaf(-sa[k * kSolveStride + i], mk, sbm[i * kSolveStride + f]);
+    if (bi < k) {
+      const float* row = srow[k & 1];
+      const float kki = sa[k * kSolveStride + bi];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) br[q] = fmaf(-kki, row[bc + 8 * q], br[q]);
+      if (bi == k - 1) {  // row k - 1 is final now: m_{k-1} = b_{k-1} / d_{k-1}
+        const float r = rcp_d(k - 1);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) br[q] *= r;
+        publish(srow[(k - 1) & 1]);
+      }
+    }
     __syncthreads();
   }
-  bf16_t *mo = static_cast<bf16_t *>(L.pred) + hd.pred + int64_t(b) * rk * kD;
-  for (int e = tid; e < rk * kD; e += kSolveThreads) {
-    const int i = e / kD, c = e % kD;
-    mo[e] = from_f32<bf16_t>(sbm[i * kSolveStride + c] * rcp_d(i));
+  if (bi < rk) {
+    bf16_t *mo = static_cast<bf16_t *>(L.pred) + hd.pred + int64_t(b) * rk * kD + bi * kD;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) mo[bc + 8 * q] = from_f32<bf16_t>(br[q]);
   }
 }
 
