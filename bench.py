@@ -156,7 +156,11 @@ def cpu_info():
 
 def gpu_state():
     """Clocks and power of GPU 0 as rocm-smi reports them right after the timed
-    work (informational; None if the tool is unavailable)."""
+    work (informational; None if the tool is unavailable).  Skipped under the
+    profiler: its preloaded library would follow the tool's launcher into the
+    child process."""
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return {"skipped": "run under the profiler"}
     try:
         r = subprocess.run(["rocm-smi", "-d", "0", "--showclocks", "--showpower", "--json"],
                            capture_output=True, text=True, timeout=30)

@@ -53,11 +53,23 @@ __global__ __launch_bounds__(256) void k_partials_generic(LayerArgs L, DecodeArg
 
   // q~ = U_K^T q (U_K^T rows are the key basis directions), scaled into log2 units
   const T *Uk = static_cast<const T *>(L.bases) + hd.u_k;
-  for (int i = tid; i < g * dk; i += blockDim.x) {
+  // four consecutive threads per element, a quarter of the features each (all
+  // 64 of a thread's loads in flight), summed by two lane exchanges
+  for (int i0 = 0; i0 < g * dk; i0 += blockDim.x / 4) {
+    const int i = min(i0 + (tid >> 2), g * dk - 1), k0 = 32 * (tid & 3);
     const int hh = i / dk, cc = i % dk;
+    float x[32], y[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      x[u] = to_f32(qb[hh * kD + k0 + u]);
+      y[u] = to_f32(Uk[cc * kD + k0 + u]);
+    }
     float acc = 0.f;
-    for (int k = 0; k < kD; ++k) acc = fmaf(to_f32(qb[hh * kD + k]), to_f32(Uk[cc * kD + k]), acc);
-    sm.sq[hh][cc] = acc * d.scale_log2;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) acc = fmaf(x[u], y[u], acc);
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    if ((tid & 3) == 0 && i0 + (tid >> 2) < g * dk) sm.sq[hh][cc] = acc * d.scale_log2;
   }
   if (tid < g) {
     sm.m[tid] = kNegInf;

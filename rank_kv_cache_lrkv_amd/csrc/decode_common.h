@@ -158,7 +158,13 @@ __device__ __forceinline__ void chunked_softmax_pass(ChunkSmem &sm, int g, int l
       float s = kNegInf;
       if (j < nv) {
         float a = 0.f;
-        for (int c = 0; c < dk; ++c) a = fmaf(sm.sq[hh][c], kval(base + j, c), a);
+        for (int c0 = 0; c0 < dk; c0 += 16) {  // dk is a multiple of 16: 16 loads in flight
+          float x[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) x[u] = kval(base + j, c0 + u);
+#pragma unroll
+          for (int u = 0; u < 16; ++u) a = fmaf(sm.sq[hh][c0 + u], x[u], a);
+        }
         s = a;
       }
       sm.sp[hh][j] = s;
@@ -185,7 +191,14 @@ __device__ __forceinline__ void chunked_softmax_pass(ChunkSmem &sm, int g, int l
       if (o < g * dv) {
         const int hh = o / dv, c = o % dv;
         float a = acc[e] * sm.alpha[hh];
-        for (int j = 0; j < nv; ++j) a = fmaf(sm.sp[hh][j], vval(base + j, c), a);
+        for (int j0 = 0; j0 < nv; j0 += 16) {  // 16 loads in flight, rows clamped to the chunk
+          float x[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) x[u] = vval(base + min(j0 + u, nv - 1), c);
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            if (j0 + u < nv) a = fmaf(sm.sp[hh][j0 + u], x[u], a);
+        }
         acc[e] = a;
       }
     }
