@@ -164,7 +164,9 @@ int32_t auto_splits(const LayerArgs &A, int32_t n_ctx) {
   // a device to ask, the figures of MI355X (256 compute units, four workgroups
   // per unit, three for the LowRAM kernels and the narrower pre-RoPE ones).  The groups' splits
   // follow their bytes per token, so the widest group's count is scaled by
-  // (widest bytes) / (mean bytes).  At least four 32-slot blocks per split.
+  // (widest bytes) / (mean bytes).  At least sixteen 32-slot blocks per split
+  // on the matrix-core kernels (four per wave: with fewer, the per-workgroup setup
+  // outweighs the streaming it starts), four on the float32 one.
   const int per_cu = partials_blocks_per_cu(A), cus = device_cu_count();
   const int64_t target = (per_cu > 0 && cus > 0) ? int64_t(per_cu) * cus : ((A.rope || A.lowram) ? 768 : 1024);
   double wsum = 0.0, wmax = 0.0;
@@ -173,7 +175,8 @@ int32_t auto_splits(const LayerArgs &A, int32_t n_ctx) {
     wmax = std::max(wmax, token_bytes(A, h));
   }
   int64_t s = int64_t(std::floor(double(target) * wmax / (double(A.batch) * wsum) + 1e-9));
-  const int64_t most = nblk / 4 > 1 ? nblk / 4 : 1;
+  const int64_t min_blocks = A.dtype == LRKV_F32 ? 4 : 16;
+  const int64_t most = std::max<int64_t>(1, (nblk + min_blocks / 2) / min_blocks);
   if (s > most) s = most;
   if (s < 1) s = 1;
   if (s > LRKV_MAX_SPLITS) s = LRKV_MAX_SPLITS;
