@@ -11,7 +11,7 @@
 // largest ||e_t||^2.  Three kernels:
 //
 //   k_lowram_gram   C^T [C | V] on the matrix cores, one partial sum per
-//                   workgroup: each 32-token tile is staged in LDS column by
+//                   workgroup: each 64-token tile is staged in LDS column by
 //                   column (the MFMA contracts over tokens, so every operand
 //                   fragment is 8 consecutive tokens of one column)
 //   k_lowram_solve  one workgroup per (row, head): the partials summed in a
@@ -27,7 +27,6 @@
 
 namespace lrkv {
 
-constexpr int kZStride = 40;  // LDS column of a staged tile: 32 tokens + 8 pad (80 bytes)
 constexpr int kMaxPartials = 16;  // Gram partials per unit (the solve keeps them all in flight)
 
 int lowram_partials(const LayerArgs &L) {
@@ -54,15 +53,24 @@ size_t lowram_workspace_bytes(const LayerArgs &L) {
 
 // ---------------------------------------------------------------------------
 // C^T [C | V] partials.  Grid (P, batch * n_kv), 256 threads.  Partial p takes the
-// blocks [p nb / P, (p + 1) nb / P).  Wave w owns the column tiles jt = w, w + 4,
-// ... of the product and every row tile.
+// 64-token tiles [p nt / P, (p + 1) nt / P).  A tile is staged in LDS transposed
+// (row = one column of C or of V, its 64 tokens contiguous; rows 144 bytes apart,
+// so the 16 rows a fragment read spans fall on distinct banks): thread (tg, grp)
+// loads tokens 4 tg .. 4 tg + 3 of code column group grp (8 columns; one 64-byte
+// run of the blocked layout) and of value feature group grp, and stores each
+// column's four tokens as one 8-byte write.  Every thread keeps the loads of two
+// tiles in flight while the staged one is multiplied.  Wave w owns the column
+// tiles jt = w, w + 4, ... of the product and every row tile.
 // ---------------------------------------------------------------------------
+constexpr int kGTile = 64;               // tokens per staged tile
+constexpr int kGPitch = kGTile + 8;      // bf16 per LDS row (144 bytes)
+
 template <int RKMAX>
 __global__ __launch_bounds__(256) void k_lowram_gram(LayerArgs L, const bf16_t *v, int64_t sb, int64_t sh,
                                                      int64_t st, int n_tok, int64_t pfloats, float *ws) {
   constexpr int NZ = RKMAX + kD;
   constexpr int NIT = RKMAX / 16, NJT = (NZ / 16 + 3) / 4;
-  __shared__ bf16_t sz[NZ * kZStride];
+  __shared__ __align__(16) bf16_t sz[NZ * kGPitch];
   const int P = gridDim.x, p = blockIdx.x, unit = blockIdx.y;
   const int b = unit / L.n_kv, h = unit % L.n_kv;
   const HeadInfo hd = L.heads[h];
@@ -70,10 +78,12 @@ __global__ __launch_bounds__(256) void k_lowram_gram(LayerArgs L, const bf16_t *
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, t16 = lane & 15;
-  const int nb = (n_tok + kBlock - 1) / kBlock;
-  const int blo = int(int64_t(p) * nb / P), bhi = int(int64_t(p + 1) * nb / P);
+  const int nt = (n_tok + kGTile - 1) / kGTile;
+  const int tlo = int(int64_t(p) * nt / P), thi = int(int64_t(p + 1) * nt / P);
   const bf16_t *codes = static_cast<const bf16_t *>(L.codes_k) + hd.ck + int64_t(b) * L.cap * rk;
   const bf16_t *vb = v + b * sb + h * sh;
+  const int tg = tid & 15, grp = tid >> 4;  // tokens 4 tg .. 4 tg + 3; column / feature group grp
+  const bool has_code = grp < rk / 8;
 
   f32x4 acc[NIT][NJT];
 #pragma unroll
@@ -81,87 +91,74 @@ __global__ __launch_bounds__(256) void k_lowram_gram(LayerArgs L, const bf16_t *
 #pragma unroll
     for (int jj = 0; jj < NJT; ++jj) acc[it][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // this thread's pieces of a tile: code pieces tid + 256 u (8 columns of one
-  // token each; 4 rk per tile) and value pieces tid + 256 u (8 features of one
-  // token; 512 per tile).  Loads are clamped to the last token (rows past n_tok
-  // are zeroed when staged, so no load waits where it is issued); every thread
-  // keeps the loads of two tiles in flight while the staged one is multiplied.
-  constexpr int NPK = (4 * RKMAX + 255) / 256;
   struct Tile {
-    u32x4 k[NPK];
-    u32x4 v[2];
+    u32x4 k[4], v[4];
   };
-  auto load = [&](int blk, Tile &t) {
+  // tokens past n_tok are read clamped and zeroed when staged (no wait at the load)
+  auto load = [&](int tile, Tile &t) {
+    const int cg = has_code ? grp : 0;
 #pragma unroll
-    for (int u = 0; u < NPK; ++u) {
-      const int pc = min(tid + 256 * u, 4 * rk - 1);
-      const int tt = pc / (rk / 8), cg = pc - tt * (rk / 8);
-      const int slot = min(blk * kBlock + tt, n_tok - 1);
-      t.k[u] = *reinterpret_cast<const u32x4 *>(codes + kslot(slot, 8 * cg, rk));
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int pc = tid + 256 * u, tt = pc >> 4, fg = pc & 15;
-      const int slot = min(blk * kBlock + tt, n_tok - 1);
-      t.v[u] = *reinterpret_cast<const u32x4 *>(vb + int64_t(slot) * st + 8 * fg);
+    for (int u = 0; u < 4; ++u) {
+      const int tok = min(tile * kGTile + 4 * tg + u, n_tok - 1);
+      t.k[u] = *reinterpret_cast<const u32x4 *>(codes + kslot(tok, 8 * cg, rk));
+      t.v[u] = *reinterpret_cast<const u32x4 *>(vb + int64_t(tok) * st + 8 * grp);
     }
   };
-  auto stage = [&](int blk, const Tile &t) {
+  // word w of a piece holds columns 2 w (low half) and 2 w + 1 (high half)
+  auto put = [&](int row0, const u32x4 (&x)[4], bool valid0, bool valid1, bool valid2, bool valid3) {
+    u32x4 r[4];
+    r[0] = valid0 ? x[0] : u32x4{0u, 0u, 0u, 0u};
+    r[1] = valid1 ? x[1] : u32x4{0u, 0u, 0u, 0u};
+    r[2] = valid2 ? x[2] : u32x4{0u, 0u, 0u, 0u};
+    r[3] = valid3 ? x[3] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int u = 0; u < NPK; ++u) {
-      const int pc = tid + 256 * u;
-      if (pc < 4 * rk) {
-        const int tt = pc / (rk / 8), cg = pc - tt * (rk / 8);
-        const u32x4 x = blk * kBlock + tt < n_tok ? t.k[u] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sz[(8 * cg + 2 * i) * kZStride + tt] = bf16_t(x[i] & 0xffffu);
-          sz[(8 * cg + 2 * i + 1) * kZStride + tt] = bf16_t(x[i] >> 16);
-        }
-      }
+    for (int w = 0; w < 4; ++w) {
+      const u32x2 lo = {(r[0][w] & 0xffffu) | (r[1][w] << 16), (r[2][w] & 0xffffu) | (r[3][w] << 16)};
+      const u32x2 hi = {(r[0][w] >> 16) | (r[1][w] & 0xffff0000u), (r[2][w] >> 16) | (r[3][w] & 0xffff0000u)};
+      *reinterpret_cast<u32x2 *>(&sz[(row0 + 2 * w) * kGPitch + 4 * tg]) = lo;
+      *reinterpret_cast<u32x2 *>(&sz[(row0 + 2 * w + 1) * kGPitch + 4 * tg]) = hi;
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int pc = tid + 256 * u, tt = pc >> 4, fg = pc & 15;
-      const u32x4 x = blk * kBlock + tt < n_tok ? t.v[u] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sz[(rk + 8 * fg + 2 * i) * kZStride + tt] = bf16_t(x[i] & 0xffffu);
-        sz[(rk + 8 * fg + 2 * i + 1) * kZStride + tt] = bf16_t(x[i] >> 16);
-      }
-    }
+  };
+  auto stage = [&](int tile, const Tile &t) {
+    const int t0 = tile * kGTile + 4 * tg;
+    const bool v0 = t0 < n_tok, v1 = t0 + 1 < n_tok, v2 = t0 + 2 < n_tok, v3 = t0 + 3 < n_tok;
+    if (has_code) put(8 * grp, t.k, v0, v1, v2, v3);
+    put(rk + 8 * grp, t.v, v0, v1, v2, v3);
   };
   // D[i][j] += sum over the tile's tokens of C[t][i] Z[t][j]: lane (q4, t16) feeds
-  // tokens 8 q4 .. 8 q4 + 7 of column 16 it + t16 (A) and of column 16 jt + t16 (B)
+  // tokens 32 ks + 8 q4 .. +7 of column 16 it + t16 (A) and of column 16 jt + t16 (B)
   auto multiply = [&]() {
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      if (it < rk / 16) {
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(&sz[(16 * it + t16) * kZStride + 8 * q4]);
+    for (int ks = 0; ks < kGTile / 32; ++ks) {
 #pragma unroll
-        for (int jj = 0; jj < NJT; ++jj) {
-          const int jt = wave + 4 * jj;
-          if (jt < nz / 16) {
-            const u32x4 bb = *reinterpret_cast<const u32x4 *>(&sz[(16 * jt + t16) * kZStride + 8 * q4]);
-            acc[it][jj] = mfma16x16x32(a, bb, acc[it][jj]);
+      for (int it = 0; it < NIT; ++it) {
+        if (it < rk / 16) {
+          const u32x4 a = *reinterpret_cast<const u32x4 *>(&sz[(16 * it + t16) * kGPitch + 32 * ks + 8 * q4]);
+#pragma unroll
+          for (int jj = 0; jj < NJT; ++jj) {
+            const int jt = wave + 4 * jj;
+            if (jt < nz / 16) {
+              const u32x4 bb = *reinterpret_cast<const u32x4 *>(&sz[(16 * jt + t16) * kGPitch + 32 * ks + 8 * q4]);
+              acc[it][jj] = mfma16x16x32(a, bb, acc[it][jj]);
+            }
           }
         }
       }
     }
   };
-  auto step = [&](int blk, Tile &t) {
+  auto step = [&](int tile, Tile &t) {
     __syncthreads();  // the previous tile's readers are done
-    stage(blk, t);
+    stage(tile, t);
     __syncthreads();
-    if (blk + 2 < bhi) load(blk + 2, t);
+    if (tile + 2 < thi) load(tile + 2, t);
     multiply();
   };
   Tile ta, tb;
-  if (blo < bhi) load(blo, ta);
-  if (blo + 1 < bhi) load(blo + 1, tb);
-  for (int blk = blo; blk < bhi; blk += 2) {
-    step(blk, ta);
-    if (blk + 1 < bhi) step(blk + 1, tb);
+  if (tlo < thi) load(tlo, ta);
+  if (tlo + 1 < thi) load(tlo + 1, tb);
+  for (int tile = tlo; tile < thi; tile += 2) {
+    step(tile, ta);
+    if (tile + 1 < thi) step(tile + 1, tb);
   }
   // lane (q4, t16) holds D[16 it + 4 q4 + v][16 jt + t16]; rows of nz floats
   float *out = ws + (int64_t(unit) * P + p) * pfloats;
