@@ -123,6 +123,13 @@ def test_auto_splits():
     assert lib.lrkv_decode_auto_splits(ctypes.byref(L), 32768) == 32
     assert lib.lrkv_decode_auto_splits(ctypes.byref(L), 100) == 1
     assert lib.lrkv_decode_auto_splits(ctypes.byref(L), 0) == 0
+    # Qwen3-1.7B-shaped layer at 4K: 64 units could take 16 splits each, but a split
+    # keeps at least 16 of the row's 126 code blocks (4 per wave): 8 splits
+    Lq = layer(batch=8, n_q_heads=16, n_kv_heads=8, window=64, cap=4096, rank_k=[64] * 8, rank_v=[32] * 8)
+    assert lib.lrkv_decode_auto_splits(ctypes.byref(Lq), 4096) == 8
+    # float32 storage keeps at least 4 blocks a split
+    Lf = layer(dtype=0, batch=1, n_q_heads=1, n_kv_heads=1, window=16, cap=256, rank_k=[64], rank_v=[32])
+    assert lib.lrkv_decode_auto_splits(ctypes.byref(Lf), 256) == 2
     # the pre-RoPE and LowRAM kernels fit three workgroups per compute unit: 768 / 32 = 24
     L.rope_base = 500000.0
     assert lib.lrkv_decode_auto_splits(ctypes.byref(L), 32768) == 24
