@@ -53,9 +53,13 @@ Pins (tests/test_oracle.py): full attention at r = d with an orthogonal basis
 (the blog's section 04 plumbing check), brute-force reconstruction on tiny
 inputs, torch's float64 scaled_dot_product_attention, softmax weights summing to
 one, closed forms (n = 1, q = 0, constant values), invariances (basis sign, token
-order), compress closed forms and the OjaKV FAQ's ~16 GB KV-cache size.  Values
-on random inputs beyond those pins are "parity unpinned": the pages print no
-worked example.
+order), compress closed forms and the OjaKV FAQ's ~16 GB KV-cache size; the Oja
+step against eigendecomposition fixed points, the LowRAM fit against least
+squares, pre-RoPE decode against the complex-rotation form, group latents
+against block products (tests/oracle_pins.py, with planted mistakes in
+tests/test_oracle_mutants.py).  Every function here has such a pin; the pages
+print no worked example of the decode, so no pin is a printed value except the
+cache size.
 """
 
 from __future__ import annotations
