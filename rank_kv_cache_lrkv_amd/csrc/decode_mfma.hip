@@ -245,13 +245,21 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
   // get their loads served first and the youngest would stream alone at the end;
   // the waves with the larger share of their blocks still to read get the higher
   // issue priority instead, so all of them finish together.
+  // The priority of a request for block blk is floor(4 left / (total + 1)) with
+  // left = ceil((bhi - blk) / step) this wave's blocks from blk on: it is at least
+  // k exactly when left >= ceil(k (total + 1) / 4), i.e. when blk < bk[k] -- three
+  // thresholds taken once, so a request costs scalar compares, no division.
   const int total = first < bhi ? (bhi - first + step - 1) / step : 0;  // this wave's blocks
+  auto threshold = [&](int k) { return bhi - ((k * (total + 1) + 3) / 4 - 1) * step; };
+  const int bk1 = __builtin_amdgcn_readfirstlane(threshold(1));
+  const int bk2 = __builtin_amdgcn_readfirstlane(threshold(2));
+  const int bk3 = __builtin_amdgcn_readfirstlane(threshold(3));
   auto set_priority = [&](int blk) {
     if (!d.balance) return;
-    const int left = (4 * ((bhi - blk + step - 1) / step)) / (total + 1);  // 0..3
-    if (left >= 3) __builtin_amdgcn_s_setprio(3);
-    else if (left == 2) __builtin_amdgcn_s_setprio(2);
-    else if (left == 1) __builtin_amdgcn_s_setprio(1);
+    blk = __builtin_amdgcn_readfirstlane(blk);
+    if (blk < bk3) __builtin_amdgcn_s_setprio(3);
+    else if (blk < bk2) __builtin_amdgcn_s_setprio(2);
+    else if (blk < bk1) __builtin_amdgcn_s_setprio(1);
     else __builtin_amdgcn_s_setprio(0);
   };
   if (d.balance) __builtin_amdgcn_s_setprio(3);
