@@ -902,19 +902,24 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
   // double-buffered sweep.  The scheduling barriers keep the next block's loads
   // ahead of the current block's work: hoisting that work above them would make
   // the wave wait for the current block with nothing else in flight.
-  int j = first;
-  if (j < bhi) {
+  // The block indices are wave-uniform; taken as scalars, the clamped index of
+  // the next request is a scalar select, so nothing at the top of the loop writes
+  // a vector register (such a write made the compiler wait there for every load
+  // in flight, the next block's included, on every other block).
+  int j = __builtin_amdgcn_readfirstlane(first);
+  const int jstep = __builtin_amdgcn_readfirstlane(step), jend = __builtin_amdgcn_readfirstlane(bhi);
+  if (j < jend) {
     while (true) {
-      load(j + step < bhi ? j + step : j, r1);
+      load(j + jstep < jend ? j + jstep : j, r1);
       __builtin_amdgcn_sched_barrier(0);
       process(j, r0);
-      j += step;
-      if (j >= bhi) break;
-      load(j + step < bhi ? j + step : j, r0);
+      j += jstep;
+      if (j >= jend) break;
+      load(j + jstep < jend ? j + jstep : j, r0);
       __builtin_amdgcn_sched_barrier(0);
       process(j, r1);
-      j += step;
-      if (j >= bhi) break;
+      j += jstep;
+      if (j >= jend) break;
     }
   }
 
