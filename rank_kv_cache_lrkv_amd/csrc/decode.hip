@@ -151,10 +151,24 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, Comb
   constexpr int kEP = 16 / sizeof(T);          // U_V elements per 16-byte piece
   constexpr int kPPR = kD / kEP;               // pieces per U_V row
   extern __shared__ __align__(16) char lds[];
+  // Setup reads in two rounds: every kernel-argument scalar first (the empty asm
+  // takes them as operands, so their loads issue together and are waited for
+  // once), then the head's row of the head table, its split count and the row
+  // length; left to itself the compiler spreads them over six dependent rounds.
+  // (The group sizes pass through the first asm, so the divisions by them cannot
+  // start, and wait, before every load of the round is issued.)
+  int grp = L.group, hgs = L.hg;
+  __asm__ volatile("" : "+s"(grp), "+s"(hgs)
+                   : "s"(L.n_q), "s"(L.n_versions), "s"(L.window), "s"(L.lowram), "s"(L.pred), "s"(L.bases),
+                     "s"(L.version_elems), "s"(d.ws), "s"(d.n_splits), "s"(d.rec), "s"(d.oa), "s"(d.ctx_lens),
+                     "s"(d.n_ctx), "s"(g.so), "s"(g.sa), "s"(g.urows), "s"(out), "s"(g.m), "s"(g.l), "s"(g.v),
+                     "s"(g.o), "s"(g.a), "s"(g.ov), "s"(g.u));
   const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x, lane = t & 63;
-  const int kvh = i / L.group;                 // KV head; its latent group and slice
-  const int h = kvh / L.hg, j = kvh % L.hg;
+  const int kvh = i / grp;                     // KV head; its latent group and slice
+  const int h = kvh / hgs, j = kvh % hgs;
   const HeadInfo hd = L.heads[h];
+  const int n_row = row_ctx(d, b);
+  __asm__ volatile("" ::"s"(hd.rv), "s"(hd.u_v), "s"(hd.pred), "s"(d.nsplit[h]), "s"(n_row));
   const int rv = hd.rv;
   const int S = d.nsplit[h], V = L.n_versions;
   float *sm = reinterpret_cast<float *>(lds + g.m);
@@ -170,7 +184,7 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, Comb
   auto rec4 = [&](int s, int f) {  // floats f .. f + 3 of split s's record
     return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rr, (s * d.rec + f) * 4, 0, 0));
   };
-  const int a1 = min(row_ctx(d, b), 1 + L.window);  // anchor rows per KV head
+  const int a1 = min(n_row, 1 + L.window);  // anchor rows per KV head
   const int per = anchor_rows_per_split(a1 * L.hg, S);
   // splits s_a0 .. s_a1 - 1 hold this KV head's anchor rows j a1 .. (j + 1) a1 - 1
   // (the unit's rows, KV head after KV head, cut into runs of per rows); LowRAM:
@@ -192,6 +206,11 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, Comb
   // u_t + (128 / kPPR) k
   const int npc = rv >> 2, pc = t % npc, s_t = t / npc, s_step = kCT / npc;
   const int ac = t & 31, a_t = t >> 5;
+  // this thread's anchor-sum float in a record, held in a register from here: the
+  // compiler would otherwise read d.oa from the arguments again just before the
+  // anchor loads and wait for it there
+  int a_f = d.oa + 4 * ac;
+  __asm__ volatile("" : "+v"(a_f));
   const int uc = t % kPPR, u_t = t / kPPR;
   const int sr = min(S, g.so), ar = min(na, g.sa), ur_rows = min(rows, g.urows);
   f4 op[P], ap[P];
@@ -206,7 +225,7 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, Comb
   };
   auto load_a = [&](int r0, int nr) {
 #pragma unroll
-    for (int k = 0; k < P; ++k) ap[k] = rec4(s_a0 + r0 + min(a_t + 4 * k, nr - 1), d.oa + 4 * ac);
+    for (int k = 0; k < P; ++k) ap[k] = rec4(s_a0 + r0 + min(a_t + 4 * k, nr - 1), a_f);
   };
   auto store_a = [&](int nr) {
 #pragma unroll

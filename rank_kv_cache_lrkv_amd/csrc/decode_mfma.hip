@@ -300,6 +300,12 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
                                              (L.cap / kBlock) * L.R * kD * 2, kBufferWord3);
     esres = __builtin_amdgcn_make_buffer_rsrc(L.rslot + e0, 0, (L.cap / kBlock) * L.R * 4, kBufferWord3);
   }
+  // the same regions with no extent: a request with nothing left to fetch (the
+  // prefetch after a wave's last block, the first block of a wave without any)
+  // goes to these, so it stays an unconditional load yet the buffer unit returns
+  // zeros without touching memory
+  const __amdgpu_buffer_rsrc_t kres0 = __builtin_amdgcn_make_buffer_rsrc(L.codes_k, 0, 0, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vres0 = __builtin_amdgcn_make_buffer_rsrc(L.codes_v, 0, 0, kBufferWord3);
   const int kblk_bytes = kBlock * rk * CB / 8, vblk_bytes = kBlock * rv * CB / 8;
   // Code blocks (and their scales and residual rows) are read exactly once per
   // call: their loads carry the streaming (non-temporal) cache policy, which
@@ -322,8 +328,11 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
 #pragma unroll
   for (int ni = 0; ni < NVC; ++ni) voff[ni] = ni < nvt ? (q4 * rv + 16 * ni + t16) * CB : kAbsent;
 
-  auto load = [&](int blk, BlockRegs<NKC, NVC, CB> &r) {
+  auto load = [&](int blk, bool live, BlockRegs<NKC, NVC, CB> &r) {
     set_priority(blk);
+    const __amdgpu_buffer_rsrc_t kr = live ? kres : kres0, vr = live ? vres : vres0;
+    const __amdgpu_buffer_rsrc_t skr = live ? skres : kres0, svr = live ? svres : kres0;
+    const __amdgpu_buffer_rsrc_t er = live ? eres : kres0, esr = live ? esres : kres0;
     // the block offsets are wave-uniform: keep them in scalar registers
     const int ks = __builtin_amdgcn_readfirstlane(blk * kblk_bytes);
     const int vs = __builtin_amdgcn_readfirstlane(blk * vblk_bytes);
@@ -332,34 +341,34 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
-          if constexpr (CB == 8) r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b64(kres, koff[h2][kc], ks, kStream);
-          else r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b32(kres, koff[h2][kc], ks, kStream);
+          if constexpr (CB == 8) r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b64(kr, koff[h2][kc], ks, kStream);
+          else r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b32(kr, koff[h2][kc], ks, kStream);
         }
 #pragma unroll
       for (int ni = 0; ni < NVC; ++ni) {
-        if constexpr (CB == 8) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b64(vres, voff[ni], vs, kStream);
-        else r.v[ni] = __builtin_amdgcn_raw_buffer_load_b32(vres, voff[ni], vs, kStream);
+        if constexpr (CB == 8) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b64(vr, voff[ni], vs, kStream);
+        else r.v[ni] = __builtin_amdgcn_raw_buffer_load_b32(vr, voff[ni], vs, kStream);
       }
       const int ss = __builtin_amdgcn_readfirstlane(blk * kBlock * 4);
-      r.sk = __builtin_amdgcn_raw_buffer_load_b32(skres, soff, ss, kStream);
-      r.sv = __builtin_amdgcn_raw_buffer_load_b32(svres, soff, ss, kStream);
+      r.sk = __builtin_amdgcn_raw_buffer_load_b32(skr, soff, ss, kStream);
+      r.sv = __builtin_amdgcn_raw_buffer_load_b32(svr, soff, ss, kStream);
     } else {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc)
-          r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b128(kres, koff[h2][kc], ks, kStream);
+          r.k[h2][kc] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[h2][kc], ks, kStream);
       if constexpr (LR == 0) {
 #pragma unroll
-        for (int ni = 0; ni < NVC; ++ni) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b128(vres, voff[ni], vs, kStream);
+        for (int ni = 0; ni < NVC; ++ni) r.v[ni] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[ni], vs, kStream);
       }
     }
     if constexpr (LR > 0) {
       const int es = __builtin_amdgcn_readfirstlane(blk * L.R * kD * 2);
 #pragma unroll
       for (int i = 0; i < LRR; ++i)
-        if (i < L.R) r.e[i] = __builtin_amdgcn_raw_buffer_load_b32(eres, lane * 4 + i * kD * 2, es, kStream);
-      r.es = __builtin_amdgcn_raw_buffer_load_b32(esres, min(lane, L.R - 1) * 4,
+        if (i < L.R) r.e[i] = __builtin_amdgcn_raw_buffer_load_b32(er, lane * 4 + i * kD * 2, es, kStream);
+      r.es = __builtin_amdgcn_raw_buffer_load_b32(esr, min(lane, L.R - 1) * 4,
                                                   __builtin_amdgcn_readfirstlane(blk * L.R * 4), kStream);
     }
   };
@@ -405,12 +414,11 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
   u32x4 kk = *reinterpret_cast<const u32x4 *>(static_cast<const bf16_t *>(L.anchor_k) + arow * kD + piece * 8);
   u32x4 vv = *reinterpret_cast<const u32x4 *>(static_cast<const bf16_t *>(L.anchor_v) + arow * kD + piece * 8);
   __builtin_amdgcn_sched_barrier(0);
-  // the wave's first block (clamped to the last block; with no blocks at all
-  // block 0 is read and never used, which the region bound makes harmless)
+  // the wave's first block (a wave with no blocks at all requests nothing)
   BlockRegs<NKC, NVC, CB> r0, r1;
   {
     const int last = max(nblk - 1, 0);
-    load(min(first, last), r0);
+    load(min(first, last), first < bhi, r0);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -905,17 +913,18 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
   // The block indices are wave-uniform; taken as scalars, the clamped index of
   // the next request is a scalar select, so nothing at the top of the loop writes
   // a vector register (such a write made the compiler wait there for every load
-  // in flight, the next block's included, on every other block).
+  // in flight, the next block's included, on every other block).  After the
+  // wave's last block the request goes to the regions without extent.
   int j = __builtin_amdgcn_readfirstlane(first);
   const int jstep = __builtin_amdgcn_readfirstlane(step), jend = __builtin_amdgcn_readfirstlane(bhi);
   if (j < jend) {
     while (true) {
-      load(j + jstep < jend ? j + jstep : j, r1);
+      load(j + jstep < jend ? j + jstep : j, j + jstep < jend, r1);
       __builtin_amdgcn_sched_barrier(0);
       process(j, r0);
       j += jstep;
       if (j >= jend) break;
-      load(j + jstep < jend ? j + jstep : j, r0);
+      load(j + jstep < jend ? j + jstep : j, j + jstep < jend, r0);
       __builtin_amdgcn_sched_barrier(0);
       process(j, r1);
       j += jstep;
