@@ -145,17 +145,53 @@ __device__ void lowram_insert(const LayerArgs &L, int h, int b, int j, float cod
   if (s_take >= 0) static_cast<bf16_t *>(L.resid)[(e0 + s_take) * kD + tid] = from_f32<bf16_t>(e);
 }
 
+// Eight consecutive elements of a basis row: one 16-byte piece of a bf16 row,
+// two of a float32 row.
+template <typename T> struct Piece;
+template <> struct Piece<bf16_t> { uint4 a; };
+template <> struct Piece<float> { float4 a, b; };
+__device__ __forceinline__ Piece<bf16_t> load_piece(const bf16_t *p, int off) {
+  return Piece<bf16_t>{*reinterpret_cast<const uint4 *>(p + off)};
+}
+__device__ __forceinline__ Piece<float> load_piece(const float *p, int off) {
+  return Piece<float>{*reinterpret_cast<const float4 *>(p + off), *reinterpret_cast<const float4 *>(p + off + 4)};
+}
+__device__ __forceinline__ void unpack_piece(const Piece<bf16_t> &w, float (&u)[8]) {
+  const uint32_t ww[4] = {w.a.x, w.a.y, w.a.z, w.a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u[2 * i] = __uint_as_float(ww[i] << 16);
+    u[2 * i + 1] = __uint_as_float(ww[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack_piece(const Piece<float> &w, float (&u)[8]) {
+  u[0] = w.a.x, u[1] = w.a.y, u[2] = w.a.z, u[3] = w.a.w;
+  u[4] = w.b.x, u[5] = w.b.y, u[6] = w.b.z, u[7] = w.b.w;
+}
+// column steps (8 code columns each) of the append whose basis loads are in
+// flight together
+constexpr int kSteps = 16;
+
 // QMAX: 0 for bf16 / f32 codes, 127 for int8 codes, 7 for 4-bit codes
 template <typename T, int QMAX>
 __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, const T *vnew, int pos) {
   __shared__ float rk_row[LRKV_MAX_HEAD_GROUP][kD], rv_row[LRKV_MAX_HEAD_GROUP][kD];
   __shared__ float red[2];
+  // setup reads in two rounds: the kernel-argument scalars (taken together by
+  // the empty asm; the divisor passes through it, so the division cannot start,
+  // and wait, before every load is issued), then the group's row of the head table
+  int nlat = L.n_lat;
+  __asm__ volatile("" : "+s"(nlat)
+                   : "s"(L.hg), "s"(L.window), "s"(L.n_kv), "s"(L.n_versions), "s"(L.vstart), "s"(L.version_elems),
+                     "s"(L.bases), "s"(L.lowram), "s"(L.anchor_k), "s"(L.anchor_v), "s"(L.rope), "s"(L.cap),
+                     "s"(L.codes_k), "s"(L.codes_v));
   const int unit = blockIdx.x;
-  const int b = unit / L.n_lat, h = unit % L.n_lat;
+  const int b = unit / nlat, h = unit % nlat;
   const int hg = L.hg;
   const int W = L.window;
   const int tid = threadIdx.x;
   const HeadInfo hd = L.heads[h];
+  __asm__ volatile("" ::"s"(hd.rk), "s"(hd.rv), "s"(hd.u_k), "s"(hd.u_v));
   const int64_t kv0 = int64_t(b) * L.n_kv + int64_t(h) * hg;  // the group's first (row, KV head)
   auto ak = [&](int j) { return static_cast<T *>(L.anchor_k) + (kv0 + j) * (1 + W) * kD; };
   auto av = [&](int j) { return static_cast<T *>(L.anchor_v) + (kv0 + j) * (1 + W) * kD; };
@@ -166,18 +202,42 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
   if (W >= 1 && pos > W) {
     slot = 1 + (pos - 1) % W;  // holds token pos - W, which now leaves the window
     code_slot = pos - W - 1;
+  } else if (W == 0 && pos >= 1) {
+    code_slot = pos - 1;
+  } else {
+    slot = anchor_slot(pos, W);
+  }
+  // basis version of the code slot: the last one starting at or before it
+  int ver = 0;
+  if (code_slot >= 0)
+    for (int v = 1; v < L.n_versions; ++v)
+      if (L.vstart[int64_t(b) * L.n_versions + v] <= code_slot) ver = v;
+  const T *Uk = static_cast<const T *>(L.bases) + ver * L.version_elems + hd.u_k;
+  const T *Uv = static_cast<const T *>(L.bases) + ver * L.version_elems + hd.u_v;
+  const int urow = hg * kD;  // elements of a basis row (U^T row)
+  const int lane = tid & 63, q = lane >> 4, f8 = lane & 15, wave = tid >> 6;
+  const int ncol = hd.rk + (L.lowram ? 0 : hd.rv);  // LowRAM layers have no value codes
+  auto basis_piece = [&](int e00, int k, int j) {  // this lane's piece of step k of a chunk
+    const int ec = min(e00 + 8 * k + 4 * wave + q, ncol - 1);
+    return load_piece(ec < hd.rk ? Uk + ec * urow : Uv + (ec - hd.rk) * urow, j * kD + 8 * f8);
+  };
+  // the first chunk's basis pieces of the first KV head are requested before the
+  // leaving row, so the two round trips overlap
+  Piece<T> w0[kSteps];
+  if (code_slot >= 0) {
+#pragma unroll
+    for (int k = 0; k < kSteps; ++k) w0[k] = basis_piece(0, k, 0);
+  }
+  if (W >= 1 && pos > W) {
     for (int j = 0; j < hg; ++j) {
       rk_row[j][tid] = to_f32(ak(j)[slot * kD + tid]);
       rv_row[j][tid] = to_f32(av(j)[slot * kD + tid]);
     }
   } else if (W == 0 && pos >= 1) {
-    code_slot = pos - 1;
     for (int j = 0; j < hg; ++j) {
       rk_row[j][tid] = to_f32(kn(j)[tid]);
       rv_row[j][tid] = to_f32(vn(j)[tid]);
     }
-  } else {
-    slot = anchor_slot(pos, W);
   }
   __syncthreads();
   if (L.rope && code_slot >= 0) {  // keys compressed before RoPE: the leaving (post-RoPE)
@@ -192,57 +252,46 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
     }
     __syncthreads();
   }
+  __shared__ float res[2 * kD];
   if (code_slot >= 0) {  // uniform over the workgroup
-    // basis version of the slot: the last one starting at or before it
-    int ver = 0;
-    for (int v = 1; v < L.n_versions; ++v)
-      if (L.vstart[int64_t(b) * L.n_versions + v] <= code_slot) ver = v;
-    const T *Uk = static_cast<const T *>(L.bases) + ver * L.version_elems + hd.u_k;
-    const T *Uv = static_cast<const T *>(L.bases) + ver * L.version_elems + hd.u_v;
-    const int urow = hg * kD;  // elements of a basis row (U^T row)
     // Column e of the codes (key columns 0 .. rk - 1, then value columns) is the
     // dot product of the leaving row(s) with basis row e: 16 lanes share a
-    // column, lane f8 taking features 8 f8 .. 8 f8 + 7 of every 128-slice with
-    // 16-byte loads, four columns per wave and step, the lanes' partial sums
-    // added by shuffles inside each 16-lane group
-    __shared__ float res[2 * kD];
-    {
-      constexpr int kE = 16 / sizeof(T);  // elements per 16-byte piece
-      const int lane = tid & 63, q = lane >> 4, f8 = lane & 15, wave = tid >> 6;
-      const int ncol = hd.rk + (L.lowram ? 0 : hd.rv);  // LowRAM layers have no value codes
-      for (int e0 = 0; e0 < ncol; e0 += 8) {
-        const int e = e0 + 4 * wave + q;
-        const int ec = min(e, ncol - 1);
-        const bool isk = ec < hd.rk;
-        const T *urow_p = isk ? Uk + ec * urow : Uv + (ec - hd.rk) * urow;
-        float acc = 0.f;
-        for (int j = 0; j < hg; ++j) {
-          float u[8];
-          if constexpr (sizeof(T) == 2) {
-            const uint4 w = *reinterpret_cast<const uint4 *>(urow_p + j * kD + 8 * f8);
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    // column, lane f8 taking features 8 f8 .. 8 f8 + 7 of every 128-slice, four
+    // columns per wave and step, the lanes' partial sums added by shuffles inside
+    // each 16-lane group.  The basis pieces of kSteps steps (a chunk) are loaded
+    // together, every load from a clamped in-range row, before any is used: one
+    // round trip per chunk (one for ranks up to 128 columns in all) instead of
+    // one per step.
+    for (int e00 = 0; e00 < ncol; e00 += 8 * kSteps) {
+      float acc[kSteps];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              u[2 * i] = __uint_as_float(ww[i] << 16);
-              u[2 * i + 1] = __uint_as_float(ww[i] & 0xffff0000u);
-            }
-          } else {
+      for (int k = 0; k < kSteps; ++k) acc[k] = 0.f;
+      for (int j = 0; j < hg; ++j) {
+        Piece<T> w[kSteps];
+        if (e00 == 0 && j == 0) {
 #pragma unroll
-            for (int i = 0; i < 8; i += kE) {
-              const float4 w = *reinterpret_cast<const float4 *>(urow_p + j * kD + 8 * f8 + i);
-              u[i] = w.x;
-              u[i + 1] = w.y;
-              u[i + 2] = w.z;
-              u[i + 3] = w.w;
-            }
-          }
-          const float *xr = isk ? rk_row[j] : rv_row[j];
+          for (int k = 0; k < kSteps; ++k) w[k] = w0[k];
+        } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc = fmaf(u[i], xr[8 * f8 + i], acc);
+          for (int k = 0; k < kSteps; ++k) w[k] = basis_piece(e00, k, j);
         }
 #pragma unroll
-        for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-        if (f8 == 0 && e < ncol) res[e] = acc;
+        for (int k = 0; k < kSteps; ++k) {
+          const int ec = min(e00 + 8 * k + 4 * wave + q, ncol - 1);
+          const float *xr = (ec < hd.rk ? rk_row[j] : rv_row[j]) + 8 * f8;
+          float u[8];
+          unpack_piece(w[k], u);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[k] = fmaf(u[i], xr[i], acc[k]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kSteps; ++k) {
+        float a = acc[k];
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) a += __shfl_xor(a, o, 64);
+        const int e = e00 + 8 * k + 4 * wave + q;
+        if (f8 == 0 && e < ncol) res[e] = a;
       }
     }
     __syncthreads();
