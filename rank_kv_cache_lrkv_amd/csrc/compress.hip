@@ -228,6 +228,17 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
 #pragma unroll
     for (int k = 0; k < kSteps; ++k) w0[k] = basis_piece(0, k, 0);
   }
+  // the new token's key and value (stored into the ring at the end), requested now
+  T kx[LRKV_MAX_HEAD_GROUP], vx[LRKV_MAX_HEAD_GROUP];
+  if (slot >= 0) {
+#pragma unroll
+    for (int j = 0; j < LRKV_MAX_HEAD_GROUP; ++j) {
+      if (j < hg) {
+        kx[j] = kn(j)[tid];
+        vx[j] = vn(j)[tid];
+      }
+    }
+  }
   if (W >= 1 && pos > W) {
     for (int j = 0; j < hg; ++j) {
       rk_row[j][tid] = to_f32(ak(j)[slot * kD + tid]);
@@ -328,9 +339,12 @@ __global__ __launch_bounds__(128) void k_append(LayerArgs L, const T *knew, cons
     }
   }
   if (slot >= 0) {
-    for (int j = 0; j < hg; ++j) {
-      ak(j)[slot * kD + tid] = kn(j)[tid];
-      av(j)[slot * kD + tid] = vn(j)[tid];
+#pragma unroll
+    for (int j = 0; j < LRKV_MAX_HEAD_GROUP; ++j) {
+      if (j < hg) {
+        ak(j)[slot * kD + tid] = kx[j];
+        av(j)[slot * kD + tid] = vx[j];
+      }
     }
   }
 }
