@@ -139,6 +139,7 @@ constexpr int kCT = 128;  // threads of a combine workgroup
 // capacities and the LDS layout (byte offsets)
 struct CombineArgs {
   int P;                  // pieces of each kind per thread and round
+  int na;                 // most anchor splits of any KV head
   int so, sa;             // splits of rank-space sums / anchor sums per round
   int urows;              // U_V rows per round
   int m, l, v, o, a, ov, u, bytes;
@@ -334,6 +335,139 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, Comb
   out[qi * kD + t] = (y + oa) / Ltot;
 }
 
+// ---------------------------------------------------------------------------
+// Stage 2 in one round, for calls with one basis version whose pieces of every
+// kind fit one round of P per thread and whose heads have at most 128 splits:
+// the same loads as above, then
+//  - each wave finds M and L itself from the split headers it loaded (split s
+//    in lane s % 64, register s / 64), with DPP row rotations and four
+//    readlanes instead of LDS round trips, and each lane turns its split's max
+//    into that split's weight 2^(m_s - M) once;
+//  - every thread scales the rank-space pieces it loaded by their splits'
+//    weights (fetched from the owning lanes) and adds them in registers, and
+//    likewise the anchor pieces, so LDS receives partial sums, not records;
+//  - after one barrier thread c < rv adds the partial sums of column c, thread
+//    t the four anchor partials of feature t; after a second, thread t
+//    up-projects.
+// Every order is fixed, so a call is bitwise reproducible.
+// ---------------------------------------------------------------------------
+struct Combine1Lds {
+  int red, anc, ov, u, bytes;  // byte offsets: partial sums [s_step][rv], anchor partials [4][128], o~ [rv], U rows
+};
+
+template <typename T, int P>
+__global__ __launch_bounds__(128) void k_combine1(LayerArgs L, DecodeArgs d, Combine1Lds g, float *out) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  constexpr int kEP = 16 / sizeof(T);          // U elements per 16-byte piece
+  constexpr int kPPR = kD / kEP;               // pieces per U row
+  extern __shared__ __align__(16) char lds[];
+  int grp = L.group, hgs = L.hg;
+  __asm__ volatile("" : "+s"(grp), "+s"(hgs)
+                   : "s"(L.n_q), "s"(L.window), "s"(L.lowram), "s"(L.pred), "s"(L.bases), "s"(d.ws),
+                     "s"(d.n_splits), "s"(d.rec), "s"(d.oa), "s"(d.ctx_lens), "s"(d.n_ctx), "s"(out), "s"(g.red),
+                     "s"(g.anc), "s"(g.ov), "s"(g.u));
+  const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x, lane = t & 63;
+  const int kvh = i / grp;                     // KV head; its latent group and slice
+  const int h = kvh / hgs, j = kvh % hgs;
+  const HeadInfo hd = L.heads[h];
+  const int n_row = row_ctx(d, b);
+  __asm__ volatile("" ::"s"(hd.rv), "s"(hd.u_v), "s"(hd.pred), "s"(d.nsplit[h]), "s"(n_row));
+  const int rv = hd.rv;
+  const int S = d.nsplit[h];
+  float *sred = reinterpret_cast<float *>(lds + g.red);
+  float *sanc = reinterpret_cast<float *>(lds + g.anc);
+  float *sov = reinterpret_cast<float *>(lds + g.ov);
+  T *su = reinterpret_cast<T *>(lds + g.u);
+  const int64_t qi = int64_t(b) * L.n_q + i;
+  const __amdgpu_buffer_rsrc_t rr =
+      __builtin_amdgcn_make_buffer_rsrc(split_record(d, qi, 0), 0, S * d.rec * 4, kBufferWord3);
+  auto rec4 = [&](int s, int f) {  // floats f .. f + 3 of split s's record
+    return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rr, (s * d.rec + f) * 4, 0, 0));
+  };
+  const int a1 = min(n_row, 1 + L.window);     // anchor rows per KV head
+  const int per = anchor_rows_per_split(a1 * L.hg, S);
+  const int s_a0 = L.lowram ? 0 : (j * a1) / per;
+  const int s_a1 = L.lowram ? S : min(S, ((j + 1) * a1 + per - 1) / per);
+  const int na = s_a1 - s_a0;                  // >= 1
+  const int urow = L.hg * kD;
+  const T *ubase = L.lowram ? static_cast<const T *>(L.pred) + hd.pred + int64_t(b) * rv * kD
+                            : static_cast<const T *>(L.bases) + hd.u_v;
+  const __amdgpu_buffer_rsrc_t ur =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(ubase), 0, rv * urow * int(sizeof(T)), kBufferWord3);
+  // piece k of this thread: sums piece pc of split s_t + s_step k (threads past
+  // npc s_step, when npc does not divide 128, take none); anchor piece ac of
+  // anchor split a_t + 4 k; U piece uc of row u_t + (128 / kPPR) k
+  const int npc = rv >> 2, pc = t % npc, s_t = t / npc, s_step = kCT / npc;
+  const bool sact = s_t < s_step;
+  const int ac = t & 31, a_t = t >> 5;
+  const int uc = t % kPPR, u_t = t / kPPR;
+  int a_f = d.oa + 4 * ac;
+  __asm__ volatile("" : "+v"(a_f));
+
+  // ---- one round of loads
+  const f4 h0 = rec4(min(lane, S - 1), 0), h1 = rec4(min(lane + 64, S - 1), 0);
+  f4 op[P], ap[P];
+  u4 up[P];
+#pragma unroll
+  for (int k = 0; k < P; ++k) op[k] = rec4(min(s_t + s_step * k, S - 1), 4 + 4 * pc);
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    const int e = min(u_t + (kCT / kPPR) * k, rv - 1);
+    up[k] = __builtin_amdgcn_raw_buffer_load_b128(ur, (e * urow + j * kD + uc * kEP) * int(sizeof(T)), 0, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < P; ++k) ap[k] = rec4(s_a0 + min(a_t + 4 * k, na - 1), a_f);
+
+  // ---- the common max, the denominator and each split's weight (per wave)
+  const float m0 = lane < S ? h0.x : kNegInf, m1 = lane + 64 < S ? h1.x : kNegInf;
+  const float M = wave_max_dpp(fmaxf(m0, m1));  // finite: token 0 is an anchor of every row
+  const float w0 = m0 == kNegInf ? 0.f : fast_exp2(m0 - M);  // a split that saw nothing weighs 0
+  const float w1 = m1 == kNegInf ? 0.f : fast_exp2(m1 - M);
+  const float Ltot = wave_sum_dpp(fmaf(w0, h0.y, w1 * h1.y));
+  auto weight = [&](int s) {  // the weight of split s < 128, from the lane that holds it
+    const float x = __shfl(w0, s & 63, 64), y = __shfl(w1, s & 63, 64);
+    return s < 64 ? x : y;
+  };
+
+  // ---- partial sums into LDS
+  {
+    f4 part = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      const int s = s_t + s_step * k;
+      const float w = weight(s);
+      part += (sact && s < S ? w : 0.f) * op[k];
+    }
+    if (sact) *reinterpret_cast<f4 *>(&sred[s_t * rv + 4 * pc]) = part;
+    f4 pa = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      const int r = a_t + 4 * k;
+      const float w = weight(s_a0 + min(r, na - 1));
+      pa += (r < na ? w : 0.f) * ap[k];
+    }
+    *reinterpret_cast<f4 *>(&sanc[a_t * kD + 4 * ac]) = pa;
+#pragma unroll
+    for (int k = 0; k < P; ++k)
+      *reinterpret_cast<u4 *>(&su[(min(u_t + (kCT / kPPR) * k, rv - 1) * kPPR + uc) * kEP]) = up[k];
+  }
+  __syncthreads();
+  if (t < rv) {
+    float a = 0.f;
+    for (int r = 0; r < s_step; ++r) a += sred[r * rv + t];
+    sov[t] = a;
+  }
+  const float oa = (sanc[t] + sanc[kD + t]) + (sanc[2 * kD + t] + sanc[3 * kD + t]);
+  __syncthreads();
+
+  // ---- up-projection: column t of every U row against the merged sums
+  float y = 0.f;
+#pragma unroll 8
+  for (int e = 0; e < rv; ++e) y = fmaf(to_f32(su[e * kD + t]), sov[e], y);
+  out[qi * kD + t] = (y + oa) / Ltot;
+}
+
 // the combine geometry of a call: P from the largest piece count of any kind
 // (rounded up to 2, 4, 8 or 16), round capacities, LDS layout
 static CombineArgs combine_args(const LayerArgs &L, const DecodeArgs &d) {
@@ -353,11 +487,16 @@ static CombineArgs combine_args(const LayerArgs &L, const DecodeArgs &d) {
     }
     na = std::max(na, 1);
   }
-  const int need = std::max({(S * (rv / 4) + kCT - 1) / kCT, (rows * (kD * esize / 16) + kCT - 1) / kCT,
+  // a round covers P splits per thread row: kCT / (rv / 4) rows of threads take
+  // pieces of the sums (when rv / 4 does not divide kCT the remaining threads
+  // take none, so the capacity is P times the whole rows, not P kCT / (rv / 4))
+  const int srow = kCT / (rv / 4);
+  const int need = std::max({(S + srow - 1) / srow, (rows * (kD * esize / 16) + kCT - 1) / kCT,
                              (na * 32 + kCT - 1) / kCT});
   CombineArgs g{};
   g.P = need <= 2 ? 2 : need <= 4 ? 4 : need <= 8 ? 8 : 16;
-  g.so = g.P * kCT / (rv / 4);
+  g.na = na;
+  g.so = g.P * srow;
   g.sa = g.P * kCT / 32;
   g.urows = g.P * kCT / (kD * esize / 16);
   const int so_n = std::min(S, g.so), sa_n = std::min(na, g.sa), u_n = std::min(rows, g.urows);
@@ -392,8 +531,36 @@ static void launch_combine_t(const LayerArgs &L, const DecodeArgs &d, const Comb
   }
 }
 
+template <typename T>
+static void launch_combine1_t(const LayerArgs &L, const DecodeArgs &d, int P, float *out, hipStream_t s) {
+  const int esize = int(sizeof(T));
+  Combine1Lds g{};
+  g.red = 0;
+  g.anc = g.red + 4 * 512;
+  g.ov = g.anc + 4 * 4 * kD;
+  g.u = g.ov + 4 * kD;
+  g.bytes = g.u + L.rv_max * kD * esize;
+  dim3 grid(L.n_q, L.batch);
+  switch (P) {
+    case 2: hipLaunchKernelGGL((k_combine1<T, 2>), grid, dim3(kCT), g.bytes, s, L, d, g, out); break;
+    case 4: hipLaunchKernelGGL((k_combine1<T, 4>), grid, dim3(kCT), g.bytes, s, L, d, g, out); break;
+    case 8: hipLaunchKernelGGL((k_combine1<T, 8>), grid, dim3(kCT), g.bytes, s, L, d, g, out); break;
+    default: hipLaunchKernelGGL((k_combine1<T, 16>), grid, dim3(kCT), g.bytes, s, L, d, g, out); break;
+  }
+}
+
 hipError_t launch_decode_combine(const LayerArgs &L, const DecodeArgs &d, float *out, hipStream_t s) {
   const CombineArgs g = combine_args(L, d);
+  // one round of loads holds every piece when the round capacities cover the
+  // splits, the anchor splits and the U rows
+  const bool one_round = g.so >= d.n_splits && g.sa >= g.na && g.urows >= L.n_versions * L.rv_max;
+  if (L.n_versions == 1 && d.n_splits <= 128 && one_round) {
+    if (L.dtype == LRKV_F32)
+      launch_combine1_t<float>(L, d, g.P, out, s);
+    else
+      launch_combine1_t<bf16_t>(L, d, g.P, out, s);
+    return hipGetLastError();
+  }
   if (L.dtype == LRKV_F32)  // float32 layers have one version
     launch_combine_t<float>(L, d, g, out, s);
   else

@@ -35,6 +35,30 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Wave reductions without the LDS crossbar: rotations inside each 16-lane row
+// (DPP row_ror), then the four rows' results taken by readlane.  Every lane gets
+// the result; the order of the operations is fixed.
+template <int N> __device__ __forceinline__ float dpp_ror(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_of(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_ror<8>(v));
+  v = fmaxf(v, dpp_ror<4>(v));
+  v = fmaxf(v, dpp_ror<2>(v));
+  v = fmaxf(v, dpp_ror<1>(v));
+  return fmaxf(fmaxf(lane_of(v, 0), lane_of(v, 16)), fmaxf(lane_of(v, 32), lane_of(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_ror<8>(v);
+  v += dpp_ror<4>(v);
+  v += dpp_ror<2>(v);
+  v += dpp_ror<1>(v);
+  return (lane_of(v, 0) + lane_of(v, 16)) + (lane_of(v, 32) + lane_of(v, 48));
+}
+
 // The work item of stage-1 workgroup (blockIdx.x, blockIdx.y) of a
 // (row_items, batch) grid: batch row b, latent group h, split s of its S_h.
 // Workgroup i of a launch runs on XCD i % 8, each XCD with its own L2: when the

@@ -58,6 +58,12 @@ EDGE = [
     ("gqa_g8", BASE.scaled(n_q_heads=16, n_ctx=400), 0),
     ("gqa_g16", BASE.scaled(n_q_heads=32, n_ctx=400), 0),
     ("wide_window", BASE.scaled(window=300, n_ctx=1000), 0),
+    # value rank 48: rv / 4 = 12 threads a split row does not divide the combine's
+    # 128 threads, so a round holds P whole rows of 10 splits; every split here
+    # has code blocks (one round of the single-version merge, and more rounds
+    # than one of the general merge)
+    ("rv48_s42", BASE.scaled(rank_v=48, n_ctx=3000), 42),
+    ("rv48_s165", BASE.scaled(rank_v=48, n_ctx=6000), 165),
     ("ranks_16_48_96_128", BASE.scaled(n_kv_heads=4, n_q_heads=8, n_ctx=500, mixed_ranks=True,
                                        rank_k_choices=(16, 48, 96, 128), rank_v_choices=(16, 48, 96, 128)), 0),
     ("rank128_f32", BASE.scaled(dtype="f32", rank_k=128, rank_v=128, n_ctx=300), 0),
