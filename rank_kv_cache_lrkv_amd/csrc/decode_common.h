@@ -59,6 +59,25 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return (lane_of(v, 0) + lane_of(v, 16)) + (lane_of(v, 32) + lane_of(v, 48));
 }
 
+// Max and sum over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32,
+// l ^ 48) with this part's row-swapping permutes: permlane16_swap of a value
+// with itself leaves each lane holding its own row's value and its row
+// partner's (rows 0 <-> 1, 2 <-> 3) in the two results, permlane32_swap the
+// same for the wave's halves.  No LDS round trip; every lane gets the same
+// bits (the operations are commutative and the association is the same).
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // The work item of stage-1 workgroup (blockIdx.x, blockIdx.y) of a
 // (row_items, batch) grid: batch row b, latent group h, split s of its S_h.
 // Workgroup i of a launch runs on XCD i % 8, each XCD with its own L2: when the

@@ -566,8 +566,7 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
         s[v] = row < nr && (alo + r0 + row) / a1 == t16 / GK ? s[v] * d.scale_log2 : kNegInf;
       }
       float cm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+      cm = rows_max(cm);
       // a head may have no row in this chunk (rows of another KV head, or an absent head)
       const float mn = fmaxf(mA, cm);
       const bool none = mn == kNegInf;
@@ -576,8 +575,7 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
 #pragma unroll
       for (int v = 0; v < 4; ++v) p[v] = none ? 0.f : fast_exp2(s[v] - mn);
       float ps = (p[0] + p[1]) + (p[2] + p[3]);
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
+      ps = rows_sum(ps);
       lA = lA * al + ps;
       mA = mn;
       uint32_t vrow[kAnchorChunk];
@@ -809,8 +807,7 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
     // online softmax of head t16 over its 8 scores in this lane, 32 per block
     float bm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    bm = rows_max(bm);
     const float mn = fmaxf(m_run, bm);  // finite: a block holds at least one slot < c
     const float m_prev = m_run;
     const float alpha = fast_exp2(m_run - mn);
@@ -935,8 +932,7 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
   // ---- per-wave state to LDS (pre-RoPE codes: U_K and q's operands share the
   // space of the rank-space sums, so every wave must be done with its blocks)
   if constexpr (RP) __syncthreads();
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = rows_sum(l_run);
   if (q4 == 0 && t16 < G) {
     sm.m[wave][t16] = m_run;
     sm.l[wave][t16] = l_run;
