@@ -194,6 +194,7 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
   constexpr bool QC = CB < 16;            // quantised codes with per-token scales
   constexpr float kX16 = CB == 4 ? 0.0625f : 1.f;  // undoes the x16 of 4-bit operands
   constexpr int RS = RKMAX + 8;           // RP: LDS row of U_K (one feature, RKMAX + 8 bf16)
+  static_assert(LR == 0 || LRKV_MAX_GROUP * RVMAX >= kBlock * 16, "a wave's epilogue slice holds a block's weights");
   __shared__ float sra[RP ? kD / 2 : 1][2];      // RP: angle per position of each pair (revolutions)
   __shared__ float srd[RP ? kD / 2 : 1][3];      // RP: the angle over a wave's block stride; cos, sin over 16 positions
   bf16_t *const su = sm.w.r.su;
@@ -839,30 +840,39 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
       }
     }
     if constexpr (LR > 0) {
-      // kept residual rows: entry i holds slot t of this block (wave-uniform); head
-      // hh's weight of token t sits in lane 16 ((t % 16) / 4) + hh, register
-      // 4 (t / 16) + t % 4
+      // kept residual rows: entry i holds slot t of this block (wave-uniform).  The
+      // block's weights go to this wave's slice of the epilogue's LDS (free until
+      // the wave leaves its loop) as [token][head]: lane (q4, t16) holds head t16's
+      // weights of tokens 16 (j / 4) + 4 q4 + j % 4; an entry then reads its
+      // token's weights of four heads at a time with one broadcast 16-byte load,
+      // instead of selecting the register and reading each head's lane
+      float *pw = &sm.w.o[wave][0][0];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) pw[(16 * (jj >> 2) + 4 * q4 + (jj & 3)) * 16 + t16] = p[jj];
+      wave_lds_fence();
 #pragma unroll
       for (int i = 0; i < LRR; ++i) {
         if (i < L.R) {
           const int t = __builtin_amdgcn_readlane(int(r.es), i);
           if (t >= 0 && blk * kBlock + t < c) {
-            const int jsel = 4 * (t >> 4) + (t & 3), lsel = 16 * ((t & 15) >> 2);
-            float pv = p[0];
-#pragma unroll
-            for (int jj = 1; jj < 8; ++jj) pv = jsel == jj ? p[jj] : pv;
             const float e0 = __uint_as_float(r.e[i] << 16), e1 = __uint_as_float(r.e[i] & 0xffff0000u);
 #pragma unroll
-            for (int hh = 0; hh < LR; ++hh) {
-              if (hh < G) {
-                const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), lsel + hh));
-                res[hh][0] = fmaf(w, e0, res[hh][0]);
-                res[hh][1] = fmaf(w, e1, res[hh][1]);
+            for (int h4 = 0; h4 < LR; h4 += 4) {
+              if (h4 < G) {
+                const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&pw[t * 16 + h4]);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                  if (h4 + v < G) {
+                    res[h4 + v][0] = fmaf(w4[v], e0, res[h4 + v][0]);
+                    res[h4 + v][1] = fmaf(w4[v], e1, res[h4 + v][1]);
+                  }
+                }
               }
             }
           }
         }
       }
+      wave_lds_fence();  // this block's reads are done before the next block's writes
     }
     // weights as the A operand (k-slot j = 4 h + v), hi and lo parts
     if constexpr (QC) {
