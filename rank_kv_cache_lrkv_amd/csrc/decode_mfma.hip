@@ -67,6 +67,7 @@ struct MfmaSmem {
   uint32_t ak[kAnchorChunk][kD / 2];        // anchor rows (bf16 pairs)
   uint32_t av[kAnchorChunk][kD / 2];
   uint32_t sq[LRKV_MAX_GROUP][kD / 2];      // the group's queries (bf16 pairs), zero rows past G
+  float qs[LRKV_MAX_GROUP];                 // quantised codes: scale of a head's int8 q~ parts
   float m[5][LRKV_MAX_GROUP];               // per wave; [4] = the anchors
   float l[5][LRKV_MAX_GROUP];
   union {
@@ -512,8 +513,55 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
   }
   lds_barrier();
   // score B operands: lane (q4, t16) holds head t16's columns 8 (4 kc + q4) .. +7
-  // as bf16 hi and lo parts, zero for absent heads/columns
-  if (wave == 0) {
+  // as bf16 hi and lo parts, zero for absent heads/columns.
+  // Quantised codes are scored on the int8 matrix cores instead: q~ of head h is
+  // held as S (a + b / 254) with int8 a, b (|a|, |b| <= 127) and S = max |q~| / 127
+  // over the head's columns (an error below S / 508 per element); the B operand of
+  // MFMA pair pp has, in k-slot i of lane (q4, t16), the column that the A
+  // operand's slot i holds: chunk kc = 2 pp + i / 8, group 4 kc + q4, element j =
+  // i % 8 of it (4-bit codes: the even elements of the group in slots 0 .. 3, the
+  // odd ones in 4 .. 7, as the nibble split below lays them out).
+  if (wave == 0 && QC) {
+    constexpr int NP = (NKC + 1) / 2;
+    auto col_of = [&](int pp, int i) {  // column of k-slot i of pair pp, -1 if absent
+      const int kc = 2 * pp + (i >> 3), kg = 4 * kc + q4, j = i & 7;
+      const int e = CB == 4 ? (j < 4 ? 2 * j : 2 * (j - 4) + 1) : j;
+      return (kc < NKC && kg < nkg) ? kg * 8 + e : -1;
+    };
+    auto qval = [&](int pp, int i) {
+      const int cidx = col_of(pp, i);
+      return (t16 < G && cidx >= 0) ? sm.u.qt[t16][cidx] : 0.f;
+    };
+    float mx = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(qval(pp, i)));
+    mx = rows_max(mx);  // over the four rows: every column of the head
+    const float S = mx / 127.f;  // 0 for an absent head
+    const float inv = S > 0.f ? 1.f / S : 0.f, inv2 = S > 0.f ? 254.f / S : 0.f;
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+      u32x4 bh, bl;
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        uint32_t hw = 0u, lw = 0u;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const float x = qval(pp, 4 * w4 + bb);
+          const float hf = fminf(fmaxf(__builtin_rintf(x * inv), -127.f), 127.f);
+          const float lf = fminf(fmaxf(__builtin_rintf((x - S * hf) * inv2), -127.f), 127.f);
+          hw |= (uint32_t(int(hf)) & 0xffu) << (8 * bb);
+          lw |= (uint32_t(int(lf)) & 0xffu) << (8 * bb);
+        }
+        bh[w4] = hw;
+        bl[w4] = lw;
+      }
+      sm.bq[pp][0][lane] = bh;
+      sm.bq[pp][1][lane] = bl;
+    }
+    if (q4 == 0) sm.qs[t16] = S / 254.f;
+  } else if (wave == 0) {
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       const int kg = 4 * kc + q4;
@@ -532,6 +580,9 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
   }
   lds_barrier();
   }
+  // quantised codes: this lane's head's scale of its int8 q~ parts
+  float qsc = 0.f;
+  if constexpr (QC) qsc = sm.qs[t16];
 
   // ---- the split's anchor rows (wave 0, before its code blocks, while the other
   // waves already stream): scores on the matrix cores against q; the 128-dim
@@ -754,6 +805,37 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
           }
         }
       }
+    } else if constexpr (QC) {
+      // int8 matrix cores: 16 columns (two 8-column chunks) per product; the
+      // int8 codes are the A operand as loaded, 4-bit codes become 16 times their
+      // value by moving each nibble to the top of a byte (even and odd elements of
+      // a chunk in separate words); D = 254 D_a + D_b is exact in int32
+      constexpr int NP = (NKC + 1) / 2;
+      auto nib_even = [](uint32_t w) { return (w << 4) & 0xf0f0f0f0u; };
+      auto nib_odd = [](uint32_t w) { return w & 0xf0f0f0f0u; };
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        i32x4 dh = i32x4{0, 0, 0, 0}, dl = i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+          if (8 * pp < nkg) {
+            u32x4 a;
+            if constexpr (CB == 8) {
+              const u32x2 k0 = r.k[h2][2 * pp];
+              const u32x2 k1 = 2 * pp + 1 < NKC ? r.k[h2][2 * pp + 1] : u32x2{0u, 0u};
+              a = u32x4{k0[0], k0[1], k1[0], k1[1]};
+            } else {
+              const uint32_t k0 = r.k[h2][2 * pp];
+              const uint32_t k1 = 2 * pp + 1 < NKC ? r.k[h2][2 * pp + 1] : 0u;
+              a = u32x4{nib_even(k0), nib_odd(k0), nib_even(k1), nib_odd(k1)};
+            }
+            dh = mfma16x16x64_i8(a, sm.bq[pp][0][lane], dh);
+            dl = mfma16x16x64_i8(a, sm.bq[pp][1][lane], dl);
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s[h2][v] = float(dh[v] * 254 + dl[v]) * qsc;
+      }
     } else {
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
@@ -761,10 +843,7 @@ __device__ __forceinline__ void partials_body(const LayerArgs &L, const DecodeAr
         const u32x4 bh = sm.bq[kc][0][lane], bl = sm.bq[kc][1][lane];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          u32x4 a;
-          if constexpr (CB == 8) a = i8x8_to_bf16(r.k[h2][kc]);
-          else if constexpr (CB == 4) a = i4x8_to_bf16_x16(r.k[h2][kc]);
-          else a = r.k[h2][kc];
+          u32x4 a = r.k[h2][kc];
           if (4 * kc + q4 >= nkg) a = u32x4{0u, 0u, 0u, 0u};
           s[h2] = mfma16x16x32(a, bh, s[h2]);
           s[h2] = mfma16x16x32(a, bl, s[h2]);

@@ -15,6 +15,13 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+// 16x16x64 int8 products, int32 accumulation (exact)
+__device__ __forceinline__ i32x4 mfma16x16x64_i8(u32x4 a, u32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0,
+                                               0, 0);
+}
+
 // x = hi + lo: hi keeps the top 16 bits (truncation), lo is the remainder
 // rounded to nearest bf16; hi + lo matches x to about 2^-16 relative.
 __device__ __forceinline__ float bf16_trunc(float x) {
