@@ -336,9 +336,9 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, Comb
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2 in one round, for calls with one basis version whose pieces of every
-// kind fit one round of P per thread and whose heads have at most 128 splits:
-// the same loads as above, then
+// Stage 2 in one round, for calls whose pieces of every kind fit one round of P
+// per thread and whose heads have at most 128 splits: the same loads as above,
+// then
 //  - each wave finds M and L itself from the split headers it loaded (split s
 //    in lane s % 64, register s / 64), with DPP row rotations and four
 //    readlanes instead of LDS round trips, and each lane turns its split's max
@@ -348,14 +348,21 @@ __global__ __launch_bounds__(128) void k_combine(LayerArgs L, DecodeArgs d, Comb
 //    likewise the anchor pieces, so LDS receives partial sums, not records;
 //  - after one barrier thread c < rv adds the partial sums of column c, thread
 //    t the four anchor partials of feature t; after a second, thread t
-//    up-projects.
+//    up-projects;
+//  - with several basis versions the weighted pieces go to LDS split by split
+//    with each split's version, row e = (version v, column c) adds the splits of
+//    version v in index order, and the up-projection runs over every version's
+//    U_V rows.
 // Every order is fixed, so a call is bitwise reproducible.
 // ---------------------------------------------------------------------------
 struct Combine1Lds {
-  int red, anc, ov, u, bytes;  // byte offsets: partial sums [s_step][rv], anchor partials [4][128], o~ [rv], U rows
+  // byte offsets: partial sums ([s_step][rv]; with several versions every split's
+  // weighted sums [S][rv]), anchor partials [4][128], split versions [S], o~ [V rv],
+  // U rows [V rv][128]
+  int red, anc, ver, ov, u, bytes;
 };
 
-template <typename T, int P>
+template <typename T, int P, int PU>
 __global__ __launch_bounds__(128) void k_combine1(LayerArgs L, DecodeArgs d, Combine1Lds g, float *out) {
   typedef float f4 __attribute__((ext_vector_type(4)));
   typedef uint32_t u4 __attribute__((ext_vector_type(4)));
@@ -366,7 +373,7 @@ __global__ __launch_bounds__(128) void k_combine1(LayerArgs L, DecodeArgs d, Com
   __asm__ volatile("" : "+s"(grp), "+s"(hgs)
                    : "s"(L.n_q), "s"(L.window), "s"(L.lowram), "s"(L.pred), "s"(L.bases), "s"(d.ws),
                      "s"(d.n_splits), "s"(d.rec), "s"(d.oa), "s"(d.ctx_lens), "s"(d.n_ctx), "s"(out), "s"(g.red),
-                     "s"(g.anc), "s"(g.ov), "s"(g.u));
+                     "s"(g.anc), "s"(g.ver), "s"(g.ov), "s"(g.u), "s"(L.n_versions), "s"(L.version_elems));
   const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x, lane = t & 63;
   const int kvh = i / grp;                     // KV head; its latent group and slice
   const int h = kvh / hgs, j = kvh % hgs;
@@ -374,9 +381,11 @@ __global__ __launch_bounds__(128) void k_combine1(LayerArgs L, DecodeArgs d, Com
   const int n_row = row_ctx(d, b);
   __asm__ volatile("" ::"s"(hd.rv), "s"(hd.u_v), "s"(hd.pred), "s"(d.nsplit[h]), "s"(n_row));
   const int rv = hd.rv;
-  const int S = d.nsplit[h];
+  const int S = d.nsplit[h], V = L.n_versions;
+  const int rows = V * rv;                     // U rows: (version, column) pairs
   float *sred = reinterpret_cast<float *>(lds + g.red);
   float *sanc = reinterpret_cast<float *>(lds + g.anc);
+  int *sver = reinterpret_cast<int *>(lds + g.ver);
   float *sov = reinterpret_cast<float *>(lds + g.ov);
   T *su = reinterpret_cast<T *>(lds + g.u);
   const int64_t qi = int64_t(b) * L.n_q + i;
@@ -393,8 +402,9 @@ __global__ __launch_bounds__(128) void k_combine1(LayerArgs L, DecodeArgs d, Com
   const int urow = L.hg * kD;
   const T *ubase = L.lowram ? static_cast<const T *>(L.pred) + hd.pred + int64_t(b) * rv * kD
                             : static_cast<const T *>(L.bases) + hd.u_v;
-  const __amdgpu_buffer_rsrc_t ur =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(ubase), 0, rv * urow * int(sizeof(T)), kBufferWord3);
+  const int vstride = L.lowram ? 0 : int(L.version_elems);  // elements between versions' bases
+  const __amdgpu_buffer_rsrc_t ur = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T *>(ubase), 0, ((V - 1) * vstride + rv * urow) * int(sizeof(T)), kBufferWord3);
   // piece k of this thread: sums piece pc of split s_t + s_step k (threads past
   // npc s_step, when npc does not divide 128, take none); anchor piece ac of
   // anchor split a_t + 4 k; U piece uc of row u_t + (128 / kPPR) k
@@ -408,13 +418,15 @@ __global__ __launch_bounds__(128) void k_combine1(LayerArgs L, DecodeArgs d, Com
   // ---- one round of loads
   const f4 h0 = rec4(min(lane, S - 1), 0), h1 = rec4(min(lane + 64, S - 1), 0);
   f4 op[P], ap[P];
-  u4 up[P];
+  u4 up[PU];
 #pragma unroll
   for (int k = 0; k < P; ++k) op[k] = rec4(min(s_t + s_step * k, S - 1), 4 + 4 * pc);
 #pragma unroll
-  for (int k = 0; k < P; ++k) {
-    const int e = min(u_t + (kCT / kPPR) * k, rv - 1);
-    up[k] = __builtin_amdgcn_raw_buffer_load_b128(ur, (e * urow + j * kD + uc * kEP) * int(sizeof(T)), 0, 0);
+  for (int k = 0; k < PU; ++k) {
+    const int e = min(u_t + (kCT / kPPR) * k, rows - 1);  // U row (version e / rv, column e % rv)
+    const int v = e / rv, cc = e - v * rv;
+    up[k] = __builtin_amdgcn_raw_buffer_load_b128(ur, (v * vstride + cc * urow + j * kD + uc * kEP) * int(sizeof(T)),
+                                                  0, 0);
   }
 #pragma unroll
   for (int k = 0; k < P; ++k) ap[k] = rec4(s_a0 + min(a_t + 4 * k, na - 1), a_f);
@@ -430,16 +442,30 @@ __global__ __launch_bounds__(128) void k_combine1(LayerArgs L, DecodeArgs d, Com
     return s < 64 ? x : y;
   };
 
-  // ---- partial sums into LDS
+  // ---- partial sums into LDS: with one version each thread's splits added in
+  // registers; with several, every split's weighted sums by split, and its version
   {
-    f4 part = f4{0.f, 0.f, 0.f, 0.f};
+    if (V == 1) {
+      f4 part = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < P; ++k) {
-      const int s = s_t + s_step * k;
-      const float w = weight(s);
-      part += (sact && s < S ? w : 0.f) * op[k];
+      for (int k = 0; k < P; ++k) {
+        const int s = s_t + s_step * k;
+        const float w = weight(s);
+        part += (sact && s < S ? w : 0.f) * op[k];
+      }
+      if (sact) *reinterpret_cast<f4 *>(&sred[s_t * rv + 4 * pc]) = part;
+    } else {
+#pragma unroll
+      for (int k = 0; k < P; ++k) {
+        const int s = s_t + s_step * k;
+        const float w = weight(s);
+        if (sact && s < S) *reinterpret_cast<f4 *>(&sred[s * rv + 4 * pc]) = w * op[k];
+      }
+      if (t < 64) {  // wave 0: lane s holds split s's header (and s + 64's)
+        if (lane < S) sver[lane] = min(max(int(h0.z), 0), V - 1);
+        if (lane + 64 < S) sver[lane + 64] = min(max(int(h1.z), 0), V - 1);
+      }
     }
-    if (sact) *reinterpret_cast<f4 *>(&sred[s_t * rv + 4 * pc]) = part;
     f4 pa = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < P; ++k) {
@@ -449,14 +475,23 @@ __global__ __launch_bounds__(128) void k_combine1(LayerArgs L, DecodeArgs d, Com
     }
     *reinterpret_cast<f4 *>(&sanc[a_t * kD + 4 * ac]) = pa;
 #pragma unroll
-    for (int k = 0; k < P; ++k)
-      *reinterpret_cast<u4 *>(&su[(min(u_t + (kCT / kPPR) * k, rv - 1) * kPPR + uc) * kEP]) = up[k];
+    for (int k = 0; k < PU; ++k)
+      *reinterpret_cast<u4 *>(&su[(min(u_t + (kCT / kPPR) * k, rows - 1) * kPPR + uc) * kEP]) = up[k];
   }
   __syncthreads();
-  if (t < rv) {
-    float a = 0.f;
-    for (int r = 0; r < s_step; ++r) a += sred[r * rv + t];
-    sov[t] = a;
+  if (V == 1) {
+    if (t < rv) {
+      float a = 0.f;
+      for (int r = 0; r < s_step; ++r) a += sred[r * rv + t];
+      sov[t] = a;
+    }
+  } else {
+    for (int e = t; e < rows; e += kCT) {  // row e: version e / rv, column e % rv, its splits in order
+      const int v = e / rv, cc = e - v * rv;
+      float a = 0.f;
+      for (int s = 0; s < S; ++s) a += sver[s] == v ? sred[s * rv + cc] : 0.f;
+      sov[e] = a;
+    }
   }
   const float oa = (sanc[t] + sanc[kD + t]) + (sanc[2 * kD + t] + sanc[3 * kD + t]);
   __syncthreads();
@@ -464,7 +499,7 @@ __global__ __launch_bounds__(128) void k_combine1(LayerArgs L, DecodeArgs d, Com
   // ---- up-projection: column t of every U row against the merged sums
   float y = 0.f;
 #pragma unroll 8
-  for (int e = 0; e < rv; ++e) y = fmaf(to_f32(su[e * kD + t]), sov[e], y);
+  for (int e = 0; e < rows; ++e) y = fmaf(to_f32(su[e * kD + t]), sov[e], y);
   out[qi * kD + t] = (y + oa) / Ltot;
 }
 
@@ -531,21 +566,39 @@ static void launch_combine_t(const LayerArgs &L, const DecodeArgs &d, const Comb
   }
 }
 
-template <typename T>
-static void launch_combine1_t(const LayerArgs &L, const DecodeArgs &d, int P, float *out, hipStream_t s) {
-  const int esize = int(sizeof(T));
+static Combine1Lds combine1_lds(const LayerArgs &L, const DecodeArgs &d, int esize) {
+  const int V = L.n_versions, rows = V * L.rv_max;
   Combine1Lds g{};
   g.red = 0;
-  g.anc = g.red + 4 * 512;
-  g.ov = g.anc + 4 * 4 * kD;
-  g.u = g.ov + 4 * kD;
-  g.bytes = g.u + L.rv_max * kD * esize;
+  g.anc = g.red + 4 * (V == 1 ? 512 : d.n_splits * L.rv_max);
+  g.ver = g.anc + 4 * 4 * kD;
+  g.ov = g.ver + 4 * ((d.n_splits + 3) / 4 * 4);
+  g.u = g.ov + 4 * ((rows + 3) / 4 * 4);
+  g.bytes = g.u + rows * kD * esize;
+  return g;
+}
+
+template <typename T, int P>
+static void launch_combine1_pu(const LayerArgs &L, const DecodeArgs &d, const Combine1Lds &g, int PU, float *out,
+                               hipStream_t s) {
   dim3 grid(L.n_q, L.batch);
+  switch (PU) {
+    case 2: hipLaunchKernelGGL((k_combine1<T, P, 2>), grid, dim3(kCT), g.bytes, s, L, d, g, out); break;
+    case 4: hipLaunchKernelGGL((k_combine1<T, P, 4>), grid, dim3(kCT), g.bytes, s, L, d, g, out); break;
+    case 8: hipLaunchKernelGGL((k_combine1<T, P, 8>), grid, dim3(kCT), g.bytes, s, L, d, g, out); break;
+    default: hipLaunchKernelGGL((k_combine1<T, P, 16>), grid, dim3(kCT), g.bytes, s, L, d, g, out); break;
+  }
+}
+
+// P: pieces of the split sums and anchor sums per thread, PU: of the U rows
+template <typename T>
+static void launch_combine1_t(const LayerArgs &L, const DecodeArgs &d, int P, int PU, float *out, hipStream_t s) {
+  const Combine1Lds g = combine1_lds(L, d, int(sizeof(T)));
   switch (P) {
-    case 2: hipLaunchKernelGGL((k_combine1<T, 2>), grid, dim3(kCT), g.bytes, s, L, d, g, out); break;
-    case 4: hipLaunchKernelGGL((k_combine1<T, 4>), grid, dim3(kCT), g.bytes, s, L, d, g, out); break;
-    case 8: hipLaunchKernelGGL((k_combine1<T, 8>), grid, dim3(kCT), g.bytes, s, L, d, g, out); break;
-    default: hipLaunchKernelGGL((k_combine1<T, 16>), grid, dim3(kCT), g.bytes, s, L, d, g, out); break;
+    case 2: launch_combine1_pu<T, 2>(L, d, g, PU, out, s); break;
+    case 4: launch_combine1_pu<T, 4>(L, d, g, PU, out, s); break;
+    case 8: launch_combine1_pu<T, 8>(L, d, g, PU, out, s); break;
+    default: launch_combine1_pu<T, 16>(L, d, g, PU, out, s); break;
   }
 }
 
@@ -554,11 +607,20 @@ hipError_t launch_decode_combine(const LayerArgs &L, const DecodeArgs &d, float 
   // one round of loads holds every piece when the round capacities cover the
   // splits, the anchor splits and the U rows
   const bool one_round = g.so >= d.n_splits && g.sa >= g.na && g.urows >= L.n_versions * L.rv_max;
-  if (L.n_versions == 1 && d.n_splits <= 128 && one_round) {
+  // (and its LDS, with several versions a record slice per split, within 64 KB)
+  const bool fits = combine1_lds(L, d, L.dtype == LRKV_F32 ? 4 : 2).bytes <= 65536;
+  if (d.n_splits <= 128 && one_round && fits) {
+    // separate piece counts for the sums and anchors and for the U rows (with
+    // several versions the U rows alone may need many)
+    const int esize = L.dtype == LRKV_F32 ? 4 : 2;
+    const int srow = kCT / (L.rv_max / 4);
+    const int need = std::max((d.n_splits + srow - 1) / srow, (g.na * 32 + kCT - 1) / kCT);
+    const int need_u = (L.n_versions * L.rv_max * (kD * esize / 16) + kCT - 1) / kCT;
+    auto round_p = [](int n) { return n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : 16; };
     if (L.dtype == LRKV_F32)
-      launch_combine1_t<float>(L, d, g.P, out, s);
+      launch_combine1_t<float>(L, d, round_p(need), round_p(need_u), out, s);
     else
-      launch_combine1_t<bf16_t>(L, d, g.P, out, s);
+      launch_combine1_t<bf16_t>(L, d, round_p(need), round_p(need_u), out, s);
     return hipGetLastError();
   }
   if (L.dtype == LRKV_F32)  // float32 layers have one version
