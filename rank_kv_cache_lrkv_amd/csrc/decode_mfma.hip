@@ -156,11 +156,13 @@ __device__ __forceinline__ u32x4 i4x8_to_bf16_x16(uint32_t w) {
 // EXACT: every head of the layer has rank_k == RKMAX and rank_v == RVMAX, so all
 // rank tests fold at compile time; otherwise ranks are read per head (<= the max).
 // CB = 8 or 4: quantised codes with a float32 scale per token (keys and values):
-// the codes enter the MFMAs converted to bf16 (exact; 4-bit codes as 16 times
-// their value, the 16 taken out of q~ and of the value sums), a score is the
-// product times the key scale, and a token's weight is multiplied by its value
-// scale before it becomes the value MFMA's A operand (the denominator keeps the
-// plain weight).
+// key codes are scored on the int8 matrix cores as loaded (4-bit codes as 16
+// times their value, the 16 taken out of q~), against q~ held as two int8 parts
+// per head; value codes enter the bf16 MFMAs converted exactly (4-bit: 16 times
+// their value, the 16 taken out of the value sums).  A score is the product
+// times the key scale, and a token's weight is multiplied by its value scale
+// before it becomes the value MFMA's A operand (the denominator keeps the plain
+// weight).
 //
 // LR: LowRAM value amortisation (bf16 codes, RVMAX == RKMAX).  No value codes are
 // read: the value operand of a block is its key codes transposed (8 tokens of one
